@@ -1,0 +1,54 @@
+"""Seeded synthetic inputs: float32 weights and fp16 activations.
+
+This module only draws random numbers.  It holds none of the GEMM's
+arithmetic: no decoding, quantization, contraction or argmax.  Both the CPU
+oracle (through the tests) and the library consume what it draws.
+
+Recipe, per workload and per M, independently:
+  rng = numpy.random.default_rng(seed)          seed 0 unless stated
+  W   = float32(rng.standard_normal((K, N)) * 0.02)   drawn first, row-major K x N
+  x   = float16(rng.standard_normal((M, K)))          drawn second
+Large W are drawn in row chunks; numpy fills a Generator's normal draws from
+one sequential stream, so the chunked draw equals the one-shot draw (a CPU test
+checks this).
+
+The shapes are the decode shapes of a 27B-class hybrid model at one GPU's
+full size (the author's post serves such a model with 4-way tensor
+parallelism; its kernel table is measured at per-rank shapes that it does not
+list).
+"""
+
+import numpy as np
+
+# name: (format, M values, K, N)
+WORKLOADS = {
+    "tiny":    ("nvfp4", (1,), 256, 512),
+    "up":      ("nvfp4", (1,), 5120, 17408),
+    "gate_up": ("nvfp4", (8,), 5120, 34816),
+    "down":    ("nvfp4", (8,), 17408, 5120),
+    "qkv":     ("fp8", (1, 2, 4), 5120, 7168),
+    "o_proj":  ("fp8", (1, 2, 4), 6144, 5120),
+    "lm_head": ("nvfp4", (1, 8), 5120, 151936),
+}
+
+
+def draw_weights(rng, K, N, scale=0.02, chunk_rows=1024):
+    """float32 [K, N] = float32(standard_normal * scale), drawn in row chunks."""
+    w = np.empty((K, N), np.float32)
+    for r0 in range(0, K, chunk_rows):
+        r1 = min(K, r0 + chunk_rows)
+        w[r0:r1] = rng.standard_normal((r1 - r0, N)) * scale
+    return w
+
+
+def draw_activations(rng, M, K):
+    """float16 [M, K] = float16(standard_normal)."""
+    return rng.standard_normal((M, K)).astype(np.float16)
+
+
+def draw(M, K, N, seed=0):
+    """(W float32 [K, N], x float16 [M, K]) drawn in that order from one seeded stream."""
+    rng = np.random.default_rng(seed)
+    w = draw_weights(rng, K, N)
+    x = draw_activations(rng, M, K)
+    return w, x

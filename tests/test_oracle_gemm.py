@@ -1,0 +1,148 @@
+"""Pins of the oracle's GEMM, dequantization and argmax (CPU only).
+
+  * exactness of E2M1 x E4M3 products in fp16 and fp32 (all 16 x 254 pairs)
+  * brute force with exact rational arithmetic on tiny shapes
+  * closed-form special cases: one-hot x, scaling by powers of two, zero
+    weights, duplicated columns, constant blocks
+"""
+
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from fp8_quantized_skinny_amd import synth
+
+
+def test_e2m1_times_e4m3_exact_in_fp16_and_fp32():
+    q = oracle.e2m1_decode(np.arange(16))
+    s = oracle.e4m3_decode(np.array([c for c in range(256) if c not in (0x7F, 0xFF)]))
+    prod = np.outer(q, s)
+    assert np.array_equal(prod.astype(np.float16).astype(np.float64), prod)
+    assert np.array_equal(prod.astype(np.float32).astype(np.float64), prod)
+    nz = np.abs(prod[prod != 0])
+    assert nz.min() == 2.0 ** -10 and nz.max() == 2688.0
+
+
+def _frac_e2m1(c):
+    s = -1 if c & 8 else 1
+    e, m = (c >> 1) & 3, c & 1
+    return s * (Fraction(m, 2) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 2)))
+
+
+def _frac_e4m3(c):
+    s = -1 if c & 0x80 else 1
+    e, m = (c >> 3) & 15, c & 7
+    return s * (Fraction(m, 512) if e == 0 else Fraction(2) ** (e - 7) * (1 + Fraction(m, 8)))
+
+
+def test_nvfp4_gemm_brute_force_fractions():
+    for M, K, N, seed in [(1, 32, 5, 0), (3, 48, 4, 1), (8, 64, 3, 2)]:
+        w, x = synth.draw(M, K, N, seed=seed)
+        codes, scales, g = oracle.nvfp4_quantize(w)
+        y = oracle.nvfp4_gemm(x, codes, scales, g)
+        for m in range(M):
+            for n in range(N):
+                tot = Fraction(0)
+                for k in range(K):
+                    byte = int(codes[n, k // 2])
+                    c = byte & 15 if k % 2 == 0 else byte >> 4
+                    tot += Fraction(float(x[m, k])) * _frac_e2m1(c) * _frac_e4m3(int(scales[n, k // 16]))
+                exact = tot * Fraction(float(g))
+                assert abs(float(exact) - y[m, n]) <= 1e-13 * max(1.0, abs(float(exact)))
+
+
+def test_fp8_gemm_brute_force_fractions():
+    M, K, N = 2, 160, 130
+    w, x = synth.draw(M, K, N, seed=9)
+    codes, scales = oracle.fp8_quantize(w)
+    y = oracle.fp8_gemm(x, codes, scales)
+    for m in range(M):
+        for n in (0, 1, 127, 128, 129):
+            tot = Fraction(0)
+            for k in range(K):
+                tot += (Fraction(float(x[m, k])) * _frac_e4m3(int(codes[n, k]))
+                        * Fraction(float(scales[n // 128, k // 128])))
+            assert abs(float(tot) - y[m, n]) <= 1e-13 * max(1.0, abs(float(tot)))
+
+
+def test_one_hot_rows_recover_dequantized_weights():
+    K, N = 64, 16
+    w, _ = synth.draw(1, K, N, seed=11)
+    codes, scales, g = oracle.nvfp4_quantize(w)
+    x = np.eye(K, dtype=np.float16)[:8]
+    y = oracle.nvfp4_gemm(x, codes, scales, np.float32(1.0))
+    deq = oracle.nvfp4_dequant_unscaled(codes, scales, K)
+    assert np.array_equal(y, deq[:8])
+
+
+def test_power_of_two_scaling_is_exact():
+    w, x = synth.draw(2, 128, 24, seed=12)
+    codes, scales, g = oracle.nvfp4_quantize(w)
+    y1 = oracle.nvfp4_gemm(x, codes, scales, g)
+    y2 = oracle.nvfp4_gemm((x.astype(np.float32) * 4).astype(np.float16), codes, scales, g)
+    assert np.array_equal(y2, 4 * y1)
+
+
+def test_constant_block_gives_scaled_code_sum():
+    K, N = 32, 2
+    w, _ = synth.draw(1, K, N, seed=13)
+    codes, scales, g = oracle.nvfp4_quantize(w)
+    x = np.zeros((1, K), np.float16)
+    x[0, 16:32] = 1.0
+    y = oracle.nvfp4_gemm(x, codes, scales, g)
+    for n in range(N):
+        q = oracle.e2m1_decode(oracle.nvfp4_unpack_codes(codes, K)[n, 16:32]).sum()
+        assert y[0, n] == q * oracle.e4m3_decode(scales[n, 1]) * np.float64(g)
+
+
+def test_zero_weights_and_argmax_ties():
+    K, N = 64, 40
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.zeros((N, K // 16), np.uint8)
+    _, x = synth.draw(3, K, N, seed=14)
+    y = oracle.nvfp4_gemm(x, codes, scales, np.float32(0.5))
+    assert not y.any()
+    idx, _ = oracle.argmax_rows(y)
+    assert np.array_equal(idx, [0, 0, 0])
+    # duplicated best column: lower index wins
+    w, _ = synth.draw(1, K, N, seed=15)
+    c2, s2, g2 = oracle.nvfp4_quantize(w)
+    y = oracle.nvfp4_gemm(x, c2, s2, g2)
+    best = np.argmax(y[0])
+    c2[N - 1], s2[N - 1] = c2[best], s2[best]
+    c2[best - 1 if best > 0 else 0], s2[best - 1 if best > 0 else 0] = c2[best], s2[best]
+    y = oracle.nvfp4_gemm(x, c2, s2, g2)
+    idx, _ = oracle.argmax_rows(y)
+    assert idx[0] == max(best - 1, 0)
+
+
+def test_argmax_matches_scan():
+    rng = np.random.default_rng(16)
+    y = rng.integers(-5, 5, size=(6, 50)).astype(np.float64)
+    idx, margin = oracle.argmax_rows(y)
+    for m in range(6):
+        best = 0
+        for n in range(50):
+            if y[m, n] > y[m, best]:
+                best = n
+        assert idx[m] == best
+    assert np.all(margin >= 0)
+
+
+def test_column_subset_matches_full():
+    w, x = synth.draw(4, 256, 300, seed=17)
+    codes, scales, g = oracle.nvfp4_quantize(w)
+    full = oracle.nvfp4_gemm(x, codes, scales, g, chunk=64)
+    cols = np.array([0, 5, 299, 150])
+    assert np.array_equal(oracle.nvfp4_gemm(x, codes, scales, g, cols=cols), full[:, cols])
+    c8, s8 = oracle.fp8_quantize(w)
+    f8 = oracle.fp8_gemm(x, c8, s8, chunk=100)
+    assert np.array_equal(oracle.fp8_gemm(x, c8, s8, cols=cols), f8[:, cols])
+
+
+def test_compare_metrics():
+    ref = np.array([[3.0, 4.0], [0.0, 1.0]])
+    m = oracle.compare(ref + np.array([[0.0, 0.1], [0.0, 0.0]]), ref)
+    assert abs(m["rel_frob"] - 0.1 / np.sqrt(26)) < 1e-15
+    assert abs(m["row_max"] - 0.1 / np.sqrt(12.5)) < 1e-15
