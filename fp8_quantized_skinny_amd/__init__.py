@@ -1,0 +1,187 @@
+"""Weight-only quantized skinny GEMM for MI355X (gfx950): Python binding.
+
+The functions below have the names of the C ABI in include/skinny.h and only
+marshal arguments: host arrays are NumPy, device buffers are torch tensors
+(torch is used for device memory and streams only).  Every GEMM runs in the
+HIP kernels of libskinny.so; there is no other code path.  If the library
+cannot be loaded, the first call raises.
+
+    y = x . dequant(W),   x fp16 [M, K] (M = 1..8),  y fp16 [M, N]
+"""
+
+import ctypes
+
+import numpy as np
+
+from ._lib import lib
+
+OK, EINVAL, ESHAPE, EALIGN, ESIZE, EHIP, EFORMAT = range(7)
+OP_NVFP4, OP_FP8, OP_LM_HEAD = 0, 1, 2
+ENGINE_VALU, ENGINE_MFMA = 0, 1
+
+
+class SkinnyError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib().skinny_strerror(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+def _check(status, where):
+    if status != OK:
+        raise SkinnyError(status, where)
+
+
+def _host_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace_bytes(op, M, K, N):
+    return int(lib().skinny_workspace_bytes(op, M, K, N))
+
+
+def strerror(status):
+    return lib().skinny_strerror(status).decode()
+
+
+# ---------------------------------------------------------------- host-side
+def nvfp4_quantize(w):
+    """w float32 [K, N] (host) -> (codes u8 [N, K/2], scales u8 [N, K/16], g float)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    K, N = w.shape
+    codes = np.empty((N, K // 2), np.uint8)
+    scales = np.empty((N, max(K // 16, 1)), np.uint8)
+    g = ctypes.c_float()
+    _check(lib().nvfp4_quantize(_host_ptr(w), K, N, _host_ptr(codes), _host_ptr(scales), ctypes.byref(g)),
+           "nvfp4_quantize")
+    return codes, scales, np.float32(g.value)
+
+
+def fp8_quantize(w):
+    """w float32 [K, N] (host) -> (codes u8 [N, K] E4M3FN, scales f32 [ceil(N/128), ceil(K/128)])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    K, N = w.shape
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((-(-N // 128), -(-K // 128)), np.float32)
+    _check(lib().fp8_quantize(_host_ptr(w), K, N, _host_ptr(codes), _host_ptr(scales)), "fp8_quantize")
+    return codes, scales
+
+
+def nvfp4_pack(codes, scales, g, K, N):
+    """Canonical NVFP4 arrays (host) -> packed blob (host uint8 array) for the GEMM calls."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    if codes.size < N * (K // 2) or scales.size < N * (K // 16):
+        raise ValueError("codes/scales smaller than N x K/2 / N x K/16")
+    size = ctypes.c_size_t(0)
+    _check(lib().nvfp4_pack(_host_ptr(codes), _host_ptr(scales), float(g), K, N, None, ctypes.byref(size)),
+           "nvfp4_pack")
+    out = np.zeros(size.value, np.uint8)
+    _check(lib().nvfp4_pack(_host_ptr(codes), _host_ptr(scales), float(g), K, N, _host_ptr(out),
+                            ctypes.byref(size)), "nvfp4_pack")
+    return out
+
+
+def packed_bytes(K, N):
+    size = ctypes.c_size_t(0)
+    dummy = np.zeros(1, np.uint8)
+    _check(lib().nvfp4_pack(_host_ptr(dummy), _host_ptr(dummy), 0.0, K, N, None, ctypes.byref(size)),
+           "nvfp4_pack")
+    return size.value
+
+
+# -------------------------------------------------------------- device calls
+def _shape_checks(x, M, K, out, N, name):
+    if x.dim() != 2 or x.shape[0] != M or x.shape[1] != K:
+        raise ValueError(f"x must be [M, K] = [{M}, {K}]")
+    if out is not None and out.numel() < M * N:
+        raise ValueError(f"{name} must hold M x N = {M} x {N} elements")
+
+
+def nvfp4_gemm(w_packed, x, y, K=None, N=None, workspace=None, stream=None, config=None):
+    """y[M, N] fp16 = x[M, K] fp16 . dequant(W); w_packed: CUDA uint8 blob from nvfp4_pack.
+
+    config: optional (engine, ct, nw) kernel choice; default lets the library pick."""
+    import torch
+    M, Kx = x.shape
+    K = Kx if K is None else K
+    N = y.shape[-1] if N is None else N
+    _shape_checks(x, M, K, y, N, "y")
+    if w_packed.numel() < packed_bytes(K, N):
+        raise ValueError("w_packed is smaller than the blob for this K, N")
+    wp = _dev(w_packed, torch.uint8, "w_packed")
+    xp, yp = _dev(x, torch.float16, "x"), _dev(y, torch.float16, "y")
+    ws, wsb = (None, 0) if workspace is None else (_dev(workspace, torch.uint8, "workspace"), workspace.numel())
+    if config is None:
+        st = lib().nvfp4_gemm(wp, xp, yp, M, K, N, ws, wsb, _stream(stream))
+    else:
+        st = lib().nvfp4_gemm_config(wp, xp, yp, M, K, N, ws, wsb, _stream(stream), *config)
+    _check(st, "nvfp4_gemm")
+    return y
+
+
+def fp8_gemm(w, block_scales, x, y, workspace=None, stream=None, config=None):
+    """y[M, N] fp16 = x . (E4M3(w) * S); w CUDA uint8 [N, K], block_scales CUDA f32 [N/128, K/128]."""
+    import torch
+    M, K = x.shape
+    N = w.shape[0]
+    _shape_checks(x, M, K, y, N, "y")
+    if w.numel() < N * K or block_scales.numel() < (-(-N // 128)) * (-(-K // 128)):
+        raise ValueError("w or block_scales smaller than the shape requires")
+    wp = _dev(w, torch.uint8, "w")
+    sp = _dev(block_scales, torch.float32, "block_scales")
+    xp, yp = _dev(x, torch.float16, "x"), _dev(y, torch.float16, "y")
+    ws, wsb = (None, 0) if workspace is None else (_dev(workspace, torch.uint8, "workspace"), workspace.numel())
+    if config is None:
+        st = lib().fp8_gemm(wp, sp, xp, yp, M, K, N, ws, wsb, _stream(stream))
+    else:
+        st = lib().fp8_gemm_config(wp, sp, xp, yp, M, K, N, ws, wsb, _stream(stream), *config)
+    _check(st, "fp8_gemm")
+    return y
+
+
+def lm_head_gemm_argmax(w_packed, x, idx, N, logits=None, workspace=None, stream=None, config=None):
+    """idx[M] int32 = per-row argmax over the fp32 logits of x . dequant(W) (ties -> lowest n).
+
+    workspace: CUDA uint8 tensor of workspace_bytes(OP_LM_HEAD, ...) bytes, zero-filled once."""
+    import torch
+    M, K = x.shape
+    _shape_checks(x, M, K, logits, N, "logits")
+    if idx.numel() < M:
+        raise ValueError("idx must hold M elements")
+    if w_packed.numel() < packed_bytes(K, N):
+        raise ValueError("w_packed is smaller than the blob for this K, N")
+    need = workspace_bytes(OP_LM_HEAD, M, K, N)
+    if workspace is None or workspace.numel() < need:
+        raise ValueError(f"workspace of at least {need} bytes is required")
+    wp = _dev(w_packed, torch.uint8, "w_packed")
+    xp, ip = _dev(x, torch.float16, "x"), _dev(idx, torch.int32, "idx")
+    lp = None if logits is None else _dev(logits, torch.float16, "logits")
+    ws = _dev(workspace, torch.uint8, "workspace")
+    if config is None:
+        st = lib().lm_head_gemm_argmax(wp, xp, ip, lp, M, K, N, ws, workspace.numel(), _stream(stream))
+    else:
+        st = lib().lm_head_gemm_argmax_config(wp, xp, ip, lp, M, K, N, ws, workspace.numel(), _stream(stream),
+                                              *config)
+    _check(st, "lm_head_gemm_argmax")
+    return idx

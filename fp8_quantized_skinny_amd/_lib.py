@@ -1,0 +1,48 @@
+"""ctypes loader for libskinny.so (built in-tree by build.py)."""
+
+import ctypes
+import os
+
+from . import build as _build
+
+_LIB = None
+
+c_int, c_size_t, c_float, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+P = c_void_p
+
+
+def _declare(lib):
+    sig = {
+        "nvfp4_pack": (c_int, [P, P, c_float, c_int, c_int, P, ctypes.POINTER(c_size_t)]),
+        "nvfp4_gemm": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
+        "nvfp4_gemm_config": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int]),
+        "fp8_gemm": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
+        "fp8_gemm_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int]),
+        "lm_head_gemm_argmax": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
+        "lm_head_gemm_argmax_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P,
+                                               c_int, c_int, c_int]),
+        "nvfp4_quantize": (c_int, [P, c_int, c_int, P, P, ctypes.POINTER(c_float)]),
+        "fp8_quantize": (c_int, [P, c_int, c_int, P, P]),
+        "skinny_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+        "skinny_strerror": (ctypes.c_char_p, [c_int]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+def lib():
+    """The loaded library; it is built first only if no built copy exists."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _LIB = _declare(ctypes.CDLL(_build.LIB))
+    return _LIB
+
+
+EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp4_quantize",
+            "fp8_quantize", "skinny_workspace_bytes", "skinny_strerror", "nvfp4_gemm_config",
+            "fp8_gemm_config", "lm_head_gemm_argmax_config")

@@ -1,0 +1,353 @@
+// Host side of the C ABI: argument checks, the NVFP4 packer, the host
+// quantizers and kernel selection.  No HIP call happens before every check
+// has passed, so all error paths run on machines without a GPU.
+#include "skinny.h"
+#include "internal.h"
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+using namespace skinny;
+
+namespace {
+
+constexpr int kMaxK = 1 << 20;
+constexpr int kMaxN = 1 << 24;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(int M, int K, int N) {
+  if (M < 1 || M > SKINNY_MAX_M) return SKINNY_ESHAPE;
+  if (K < 16 || K % 16 != 0 || K > kMaxK) return SKINNY_ESHAPE;
+  if (N < 1 || N > kMaxN) return SKINNY_ESHAPE;
+  return SKINNY_OK;
+}
+
+// ---- E2M1 / E4M3FN encoders (round to nearest, ties to the even code) ------
+// Positive magnitudes of E2M1 codes 0..7.
+const double kE2m1Mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+int e2m1_code(double v) {
+  const int sign = std::signbit(v) ? 8 : 0;
+  const double a = std::fabs(v);
+  int i = 0;  // smallest i with a <= midpoint(i, i+1), else 7
+  while (i < 7 && a > 0.5 * (kE2m1Mag[i] + kE2m1Mag[i + 1])) ++i;
+  if (i < 7 && a == 0.5 * (kE2m1Mag[i] + kE2m1Mag[i + 1]) && (i & 1)) ++i;
+  return sign | i;
+}
+
+double e4m3_value(int code) {  // code 0..126 (positive, finite)
+  const int e = (code >> 3) & 15, m = code & 7;
+  return e == 0 ? std::ldexp(static_cast<double>(m), -9) : std::ldexp(1.0 + m / 8.0, e - 7);
+}
+
+struct E4m3Table {
+  double mid[126];  // midpoint between codes i and i+1
+  E4m3Table() {
+    for (int i = 0; i < 126; ++i) mid[i] = 0.5 * (e4m3_value(i) + e4m3_value(i + 1));
+  }
+};
+const E4m3Table& e4m3_table() {
+  static const E4m3Table t;
+  return t;
+}
+
+int e4m3_code(double v) {
+  const int sign = std::signbit(v) ? 0x80 : 0;
+  const double a = std::fabs(v);
+  const double* mid = e4m3_table().mid;
+  int lo = 0, hi = 126;  // find smallest i in [0,126] with a <= mid[i] (126 = saturate)
+  while (lo < hi) {
+    const int md = (lo + hi) / 2;
+    if (a <= mid[md]) hi = md; else lo = md + 1;
+  }
+  int i = lo;
+  if (i < 126 && a == mid[i] && (i & 1)) ++i;
+  return sign | i;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_EHIP; }
+
+LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax) {
+  const Geometry g = nvfp4_geometry(K, N);
+  LaunchCfg c{(M == 1 && !argmax) ? 0 : 1, 1, 4};
+  if (g.nt < 1024) c.nw = 8;
+  return c;
+}
+
+LaunchCfg default_fp8_cfg(int M, int K, int N) {
+  (void)M;
+  const int nt = (N + kTileCols - 1) / kTileCols;
+  (void)K;
+  LaunchCfg c{1, 1, 4};
+  if (nt < 1024) c.nw = 8;
+  return c;
+}
+
+int nvfp4_common_checks(const void* w_packed, const uint16_t* x, const void* out, int M, int K, int N) {
+  if (!w_packed || !x || !out) return SKINNY_EINVAL;
+  int s = check_shape(M, K, N);
+  if (s) return s;
+  if (!aligned(w_packed, 16) || !aligned(x, 16)) return SKINNY_EALIGN;
+  return SKINNY_OK;
+}
+
+}  // namespace
+
+namespace skinny {
+
+Geometry nvfp4_geometry(int K, int N) {
+  Geometry g;
+  g.kc = (K + kChunkK - 1) / kChunkK;
+  g.nt = (N + kTileCols - 1) / kTileCols;
+  g.sg = (g.kc + kChunksPerScaleGroup - 1) / kChunksPerScaleGroup;
+  g.codes_bytes = static_cast<size_t>(g.nt) * g.kc * kTileBytes;
+  g.scales_bytes = static_cast<size_t>(g.nt) * g.sg * kTileBytes;
+  g.total_bytes = kHeaderBytes + g.codes_bytes + g.scales_bytes;
+  return g;
+}
+
+}  // namespace skinny
+
+extern "C" {
+
+const char* skinny_strerror(int status) {
+  switch (status) {
+    case SKINNY_OK: return "ok";
+    case SKINNY_EINVAL: return "invalid argument (null pointer or bad value)";
+    case SKINNY_ESHAPE: return "unsupported shape (M in 1..8, K % 16 == 0, N >= 1)";
+    case SKINNY_EALIGN: return "device pointer not aligned";
+    case SKINNY_ESIZE: return "buffer or workspace too small";
+    case SKINNY_EHIP: return "HIP runtime or launch error";
+    case SKINNY_EFORMAT: return "bad format (NaN scale byte or bad blob)";
+    default: return "unknown status";
+  }
+}
+
+size_t skinny_workspace_bytes(int op, int M, int K, int N) {
+  if (check_shape(M, K, N)) return 0;
+  switch (op) {
+    case 0: return 0;
+    case 1: return 0;
+    case 2: return kArgmaxWorkspaceBytes;
+    default: return 0;
+  }
+}
+
+int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float gscale, int K, int N,
+               void* out, size_t* out_bytes) {
+  if (!codes || !scales || !out_bytes) return SKINNY_EINVAL;
+  if (K < 16 || K % 16 != 0 || K > kMaxK || N < 1 || N > kMaxN) return SKINNY_ESHAPE;
+  if (!std::isfinite(gscale) || gscale < 0.0f) return SKINNY_EINVAL;
+  const Geometry geo = nvfp4_geometry(K, N);
+  if (!out) {
+    *out_bytes = geo.total_bytes;
+    return SKINNY_OK;
+  }
+  if (*out_bytes < geo.total_bytes) return SKINNY_ESIZE;
+  const size_t nscale = static_cast<size_t>(N) * (K / 16);
+  for (size_t i = 0; i < nscale; ++i)
+    if ((scales[i] & 0x7F) == 0x7F) return SKINNY_EFORMAT;
+
+  uint8_t* blob = static_cast<uint8_t*>(out);
+  std::memset(blob, 0, geo.total_bytes);
+  Nvfp4Header h{};
+  h.magic = kBlobMagic;
+  h.version = kBlobVersion;
+  h.K = K;
+  h.N = N;
+  h.kc = geo.kc;
+  h.nt = geo.nt;
+  h.sg = geo.sg;
+  h.g = gscale;
+  h.codes_off = kHeaderBytes;
+  h.codes_bytes = geo.codes_bytes;
+  h.scales_off = kHeaderBytes + geo.codes_bytes;
+  h.scales_bytes = geo.scales_bytes;
+  std::memcpy(blob, &h, sizeof(h));
+
+  const size_t row_codes = K / 2, row_scales = K / 16;
+  uint8_t* ctile = blob + kHeaderBytes;
+  for (int t = 0; t < geo.nt; ++t) {
+    for (int kc = 0; kc < geo.kc; ++kc) {
+      uint8_t* dst = ctile + (static_cast<size_t>(t) * geo.kc + kc) * kTileBytes;
+      for (int lane = 0; lane < 64; ++lane) {
+        const int grp = lane >> 4, c = lane & 15;
+        const int n = t * kTileCols + c;
+        if (n >= N) continue;
+        const int k0 = kc * kChunkK + grp * 32;
+        for (int i = 0; i < 16; ++i) {
+          const int k = k0 + 2 * i;
+          if (k >= K) break;
+          dst[lane * 16 + i] = codes[static_cast<size_t>(n) * row_codes + k / 2];
+        }
+      }
+    }
+  }
+  uint8_t* sgrp = blob + h.scales_off;
+  for (int t = 0; t < geo.nt; ++t) {
+    for (int sg = 0; sg < geo.sg; ++sg) {
+      uint8_t* dst = sgrp + (static_cast<size_t>(t) * geo.sg + sg) * kTileBytes;
+      for (int lane = 0; lane < 64; ++lane) {
+        const int grp = lane >> 4, c = lane & 15;
+        const int n = t * kTileCols + c;
+        if (n >= N) continue;
+        for (int j = 0; j < kChunksPerScaleGroup; ++j) {
+          const int kc = sg * kChunksPerScaleGroup + j;
+          for (int half = 0; half < 2; ++half) {
+            const int k = kc * kChunkK + grp * 32 + 16 * half;
+            if (k >= K) continue;
+            dst[lane * 16 + 2 * j + half] = scales[static_cast<size_t>(n) * row_scales + k / 16];
+          }
+        }
+      }
+    }
+  }
+  *out_bytes = geo.total_bytes;
+  return SKINNY_OK;
+}
+
+int nvfp4_quantize(const float* w, int K, int N, uint8_t* codes, uint8_t* scales, float* g_out) {
+  if (!w || !codes || !scales || !g_out) return SKINNY_EINVAL;
+  if (K < 16 || K % 16 != 0 || K > kMaxK || N < 1 || N > kMaxN) return SKINNY_ESHAPE;
+  const size_t total = static_cast<size_t>(K) * N;
+  double amax = 0.0;
+  for (size_t i = 0; i < total; ++i) {
+    const float v = w[i];
+    if (!std::isfinite(v)) return SKINNY_EINVAL;
+    amax = std::fmax(amax, std::fabs(static_cast<double>(v)));
+  }
+  const float g = static_cast<float>(amax / (6.0 * 448.0));
+  *g_out = g;
+  const size_t row_codes = K / 2, row_scales = K / 16;
+  std::memset(codes, 0, row_codes * N);
+  std::memset(scales, 0, row_scales * N);
+  if (g == 0.0f) return SKINNY_OK;
+  const double gd = g;
+  std::vector<double> blk(16);
+  for (int n = 0; n < N; ++n) {
+    for (int b = 0; b < K / 16; ++b) {
+      double bmax = 0.0;
+      for (int i = 0; i < 16; ++i) {
+        blk[i] = static_cast<double>(w[static_cast<size_t>(b * 16 + i) * N + n]);
+        bmax = std::fmax(bmax, std::fabs(blk[i]));
+      }
+      const double t = (bmax / 6.0) / gd;
+      const int sc = e4m3_code(t);
+      scales[static_cast<size_t>(n) * row_scales + b] = static_cast<uint8_t>(sc);
+      const double denom = e4m3_value(sc & 0x7F) * gd;
+      if (denom == 0.0) continue;
+      uint8_t* dst = codes + static_cast<size_t>(n) * row_codes + b * 8;
+      for (int i = 0; i < 8; ++i) {
+        const int lo = e2m1_code(blk[2 * i] / denom);
+        const int hi = e2m1_code(blk[2 * i + 1] / denom);
+        dst[i] = static_cast<uint8_t>(lo | (hi << 4));
+      }
+    }
+  }
+  return SKINNY_OK;
+}
+
+int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales) {
+  if (!w || !codes || !scales) return SKINNY_EINVAL;
+  if (K < 1 || K > kMaxK || N < 1 || N > kMaxN) return SKINNY_ESHAPE;
+  const size_t total = static_cast<size_t>(K) * N;
+  for (size_t i = 0; i < total; ++i)
+    if (!std::isfinite(w[i])) return SKINNY_EINVAL;
+  const int KB = (K + 127) / 128, NB = (N + 127) / 128;
+  std::memset(codes, 0, total);
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n1 = std::min(N, nb * 128 + 128);
+    for (int kb = 0; kb < KB; ++kb) {
+      const int k1 = std::min(K, kb * 128 + 128);
+      double bmax = 0.0;
+      for (int k = kb * 128; k < k1; ++k)
+        for (int n = nb * 128; n < n1; ++n)
+          bmax = std::fmax(bmax, std::fabs(static_cast<double>(w[static_cast<size_t>(k) * N + n])));
+      const float S = static_cast<float>(bmax / 448.0);
+      scales[static_cast<size_t>(nb) * KB + kb] = S;
+      if (S == 0.0f) continue;
+      const double Sd = S;
+      for (int n = nb * 128; n < n1; ++n)
+        for (int k = kb * 128; k < k1; ++k)
+          codes[static_cast<size_t>(n) * K + k] =
+              static_cast<uint8_t>(e4m3_code(static_cast<double>(w[static_cast<size_t>(k) * N + n]) / Sd));
+    }
+  }
+  return SKINNY_OK;
+}
+
+int nvfp4_gemm_config(const void* w_packed, const uint16_t* x, uint16_t* y, int M, int K, int N,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      int engine, int ct, int nw) {
+  int s = nvfp4_common_checks(w_packed, x, y, M, K, N);
+  if (s) return s;
+  if (!aligned(y, 16)) return SKINNY_EALIGN;
+  (void)workspace;
+  (void)workspace_bytes;
+  const LaunchCfg cfg{engine, ct, nw};
+  if (!nvfp4_cfg_supported(cfg, M, false)) return SKINNY_EINVAL;
+  return launch_status(launch_nvfp4(static_cast<const uint8_t*>(w_packed), x, y, M, K, N, cfg,
+                                    nullptr, nullptr, stream));
+}
+
+int nvfp4_gemm(const void* w_packed, const uint16_t* x, uint16_t* y, int M, int K, int N,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int s = check_shape(M, K, N);
+  if (s) return s;
+  const LaunchCfg c = default_nvfp4_cfg(M, K, N, false);
+  return nvfp4_gemm_config(w_packed, x, y, M, K, N, workspace, workspace_bytes, stream, c.engine, c.ct, c.nw);
+}
+
+int fp8_gemm_config(const uint8_t* w, const float* block_scales, const uint16_t* x, uint16_t* y,
+                    int M, int K, int N, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream, int engine, int ct, int nw) {
+  if (!w || !block_scales || !x || !y) return SKINNY_EINVAL;
+  int s = check_shape(M, K, N);
+  if (s) return s;
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(block_scales, 4))
+    return SKINNY_EALIGN;
+  (void)workspace;
+  (void)workspace_bytes;
+  const LaunchCfg cfg{engine, ct, nw};
+  if (!fp8_cfg_supported(cfg, M)) return SKINNY_EINVAL;
+  return launch_status(launch_fp8(w, block_scales, x, y, M, K, N, cfg, stream));
+}
+
+int fp8_gemm(const uint8_t* w, const float* block_scales, const uint16_t* x, uint16_t* y,
+             int M, int K, int N, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int s = check_shape(M, K, N);
+  if (s) return s;
+  const LaunchCfg c = default_fp8_cfg(M, K, N);
+  return fp8_gemm_config(w, block_scales, x, y, M, K, N, workspace, workspace_bytes, stream,
+                         c.engine, c.ct, c.nw);
+}
+
+int lm_head_gemm_argmax_config(const void* w_packed, const uint16_t* x, int32_t* idx,
+                               uint16_t* logits, int M, int K, int N, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream, int engine, int ct,
+                               int nw) {
+  int s = nvfp4_common_checks(w_packed, x, idx, M, K, N);
+  if (s) return s;
+  if (!aligned(idx, 4) || (logits && !aligned(logits, 16))) return SKINNY_EALIGN;
+  if (!workspace) return SKINNY_EINVAL;
+  if (!aligned(workspace, 16)) return SKINNY_EALIGN;
+  if (workspace_bytes < skinny_workspace_bytes(2, M, K, N)) return SKINNY_ESIZE;
+  const LaunchCfg cfg{engine, ct, nw};
+  if (!nvfp4_cfg_supported(cfg, M, true)) return SKINNY_EINVAL;
+  return launch_status(launch_nvfp4(static_cast<const uint8_t*>(w_packed), x, logits, M, K, N, cfg,
+                                    idx, workspace, stream));
+}
+
+int lm_head_gemm_argmax(const void* w_packed, const uint16_t* x, int32_t* idx, uint16_t* logits,
+                        int M, int K, int N, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  int s = check_shape(M, K, N);
+  if (s) return s;
+  const LaunchCfg c = default_nvfp4_cfg(M, K, N, true);
+  return lm_head_gemm_argmax_config(w_packed, x, idx, logits, M, K, N, workspace, workspace_bytes,
+                                    stream, c.engine, c.ct, c.nw);
+}
+
+}  // extern "C"

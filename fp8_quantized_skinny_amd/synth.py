@@ -32,12 +32,16 @@ WORKLOADS = {
 }
 
 
-def draw_weights(rng, K, N, scale=0.02, chunk_rows=1024):
+def draw_weights(rng, K, N, scale=0.02, chunk_rows=256):
     """float32 [K, N] = float32(standard_normal * scale), drawn in row chunks."""
     w = np.empty((K, N), np.float32)
+    buf = np.empty((min(chunk_rows, K), N), np.float64)
     for r0 in range(0, K, chunk_rows):
         r1 = min(K, r0 + chunk_rows)
-        w[r0:r1] = rng.standard_normal((r1 - r0, N)) * scale
+        b = buf[:r1 - r0]
+        rng.standard_normal(out=b)
+        np.multiply(b, scale, out=b)
+        w[r0:r1] = b
     return w
 
 

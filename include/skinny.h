@@ -1,0 +1,186 @@
+/*
+ * skinny.h -- C ABI of the weight-only quantized skinny GEMM for MI355X (gfx950).
+ *
+ *   y[M, N] = x[M, K] . dequant(W)[K, N],   1 <= M <= 8
+ *
+ * The operation is the one the pages build their decode path on: the
+ * weights stay compressed in HBM and each fragment is widened to fp16 in
+ * registers right before the matrix unit uses it, with no separate
+ * dequantize-to-fp16 pass ("NVFP4 on Volta!" author's post, section "What I
+ * actually built").  M = 1 is ordinary decode; M = 8 is the target token
+ * plus k = 7 speculative drafts verified in one pass (same post, the
+ * paragraph on why the M = 8 row of its bandwidth table matters).  Published
+ * FP4 regions go to the NVFP4 path and published FP8 regions to the FP8
+ * path, with fp16 activations (same post, section "v1.0 -> v1.1").
+ *
+ * Formats (OCP MX v1.0 element encodings):
+ *   NVFP4 : E2M1 4-bit codes, one E4M3FN scale per 16 consecutive K of one
+ *           output column, one fp32 per-tensor scale g.
+ *           w~[k][n] = e2m1(q) * e4m3(s) * g
+ *   FP8   : E4M3FN codes, one fp32 scale per 128 x 128 block of W.
+ *           w~[k][n] = e4m3(c) * S[n/128][k/128]
+ *   x     : fp16 (IEEE binary16), row-major [M][K]
+ *   y     : fp16, row-major [M][N], round-to-nearest-even of the fp32 sum
+ *
+ * Conventions shared by every call:
+ *   - Every function returns an int status (SKINNY_OK == 0) and never aborts.
+ *   - All argument checks happen on the host before any HIP call; a call that
+ *     fails them returns an error and enqueues nothing.
+ *   - Device pointers must be 16-byte aligned.  The library allocates no
+ *     memory: the caller owns every buffer.
+ *   - GEMM calls are asynchronous on the caller's stream; faults of the kernel
+ *     itself surface at the next synchronisation (HIP semantics).
+ *   - K must be a multiple of 16 (one NVFP4 scale block); N >= 1; K >= 16.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef SKINNY_H
+#define SKINNY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SKINNY_OK = 0,
+  SKINNY_EINVAL = 1,   /* null pointer or bad value                          */
+  SKINNY_ESHAPE = 2,   /* M, K or N outside what the call supports           */
+  SKINNY_EALIGN = 3,   /* device pointer not 16-byte aligned                 */
+  SKINNY_ESIZE = 4,    /* output or workspace buffer too small               */
+  SKINNY_EHIP = 5,     /* HIP runtime / launch error                         */
+  SKINNY_EFORMAT = 6   /* NaN scale byte or bad packed-blob header           */
+};
+
+/* Largest supported row count: the target token plus seven drafts. */
+#define SKINNY_MAX_M 8
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_pack -- lay NVFP4 codes and scales out for 128-bit coalesced loads.
+ *
+ * Host only, run once per weight tensor.  The compressed weights are what the
+ * kernels stream from HBM (post, "What I actually built"); this call only
+ * reorders bytes, it changes no value.
+ *
+ *   codes  : host, uint8 [N][K/2]; byte j of row n holds k = 2j in its low
+ *            nibble and k = 2j+1 in its high nibble (E2M1 codes).
+ *   scales : host, uint8 [N][K/16]; E4M3FN scale of K-block b of column n.
+ *            0x7F and 0xFF (NaN) are rejected with SKINNY_EFORMAT.
+ *   g      : per-tensor fp32 scale (finite, >= 0).
+ *   out    : host buffer of *out_bytes bytes, or NULL to query the size.
+ *            On success *out_bytes is set to the blob size.
+ *
+ * The blob starts with a 256-byte header (magic "SKN4", version, K, N, g)
+ * followed by the code tiles and the scale groups.  The caller copies the
+ * blob as-is into a device buffer it owns and passes that to nvfp4_gemm or
+ * lm_head_gemm_argmax.  Returns SKINNY_ESIZE if out is non-NULL and
+ * *out_bytes is smaller than the blob.
+ * ------------------------------------------------------------------------- */
+int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float g,
+               int K, int N, void* out, size_t* out_bytes);
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_gemm -- y = x . (e2m1(q) * e4m3(s) * g), fp32 accumulate, fp16 out.
+ *
+ *   w_packed  : device, blob from nvfp4_pack for exactly this K and N.
+ *   x         : device, fp16 [M][K] row-major.
+ *   y         : device, fp16 [M][N] row-major (written, never read).
+ *   M         : 1..8.
+ *   workspace : device buffer of at least skinny_workspace_bytes(0, M, K, N)
+ *               bytes, zero-filled before its first use; each call leaves it
+ *               zero-filled again.  May be NULL when that size is 0.
+ *   stream    : HIP stream the kernel is enqueued on (0 = null stream).
+ * ------------------------------------------------------------------------- */
+int nvfp4_gemm(const void* w_packed, const uint16_t* x, uint16_t* y,
+               int M, int K, int N, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * fp8_gemm -- y = x . (e4m3(c) * S), fp32 accumulate, fp16 out.
+ *
+ * The FP8 regions of a published checkpoint are served in FP8 rather than
+ * converted to NVFP4 (post, section "v1.0 -> v1.1").
+ *
+ *   w            : device, uint8 [N][K] E4M3FN codes (canonical, no packing).
+ *   block_scales : device, fp32 [ceil(N/128)][ceil(K/128)].
+ *   x, y, M, workspace, stream : as for nvfp4_gemm (op 1 for the size).
+ * ------------------------------------------------------------------------- */
+int fp8_gemm(const uint8_t* w, const float* block_scales, const uint16_t* x,
+             uint16_t* y, int M, int K, int N, void* workspace,
+             size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * lm_head_gemm_argmax -- vocabulary-sized NVFP4 GEMM with a fused per-row
+ * argmax (post: the native 4-bit lm_head row of the bandwidth table; the
+ * drafter should propose greedy / local-argmax tokens, section "This is a
+ * server, not a GEMM screenshot").
+ *
+ *   w_packed, x, M, K, N : as for nvfp4_gemm.
+ *   idx       : device, int32 [M]; idx[m] = the smallest n whose fp32 logit
+ *               g * sum_k x[m][k] * e2m1 * e4m3 is the row maximum.  The
+ *               comparison uses the fp32 logits before any fp16 rounding.
+ *   logits    : device fp16 [M][N] or NULL (then no logits are written).
+ *   workspace : at least skinny_workspace_bytes(2, M, K, N) bytes,
+ *               zero-filled before first use, left zero-filled by each call.
+ *               Calls that share one workspace must not overlap in time.
+ * ------------------------------------------------------------------------- */
+int lm_head_gemm_argmax(const void* w_packed, const uint16_t* x, int32_t* idx,
+                        uint16_t* logits, int M, int K, int N, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Host quantizers (offline weight preparation, not part of the GEMM).  They
+ * stand in for the pages' offline FP16 -> NVFP4 conversion script (ai-manual
+ * article, section "NVFP4 model conversion") and produce the canonical
+ * arrays that nvfp4_pack and fp8_gemm take.
+ *
+ * nvfp4_quantize: w host fp32 [K][N] row-major (K % 16 == 0).
+ *   g = fp32(amax|w| / 2688); per 16-block of a column: s = E4M3(blk_amax/6/g)
+ *   (float64, round to nearest even, saturating); q = E2M1(w / (s*g))
+ *   (float64 ratio, RNE, saturating, sign of zero kept; all 0 when s == 0).
+ *   Outputs codes [N][K/2], scales [N][K/16] (layouts as nvfp4_pack), *g.
+ * fp8_quantize: w host fp32 [K][N]; per 128x128 block S = fp32(blk_amax/448),
+ *   c = E4M3(w / S) (float64 ratio; all 0 when S == 0).  Outputs codes [N][K]
+ *   and scales [ceil(N/128)][ceil(K/128)].
+ * Both reject non-finite weights with SKINNY_EINVAL.
+ * ------------------------------------------------------------------------- */
+int nvfp4_quantize(const float* w, int K, int N, uint8_t* codes,
+                   uint8_t* scales, float* g);
+int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales);
+
+/* ---------------------------------------------------------------------------
+ * The three GEMM calls with an explicit kernel choice instead of the
+ * library's pick (same arguments and results, used to compare kernels):
+ *   engine : 0 = VALU dot2 engine (nvfp4_gemm with M == 1 only),
+ *            1 = MFMA 16x16x32 f16 engine (all calls, M = 1..8)
+ *   ct     : 16-column tiles per workgroup: 1, 2 or 4
+ *   nw     : wavefronts per workgroup, which split K: 4 or 8
+ * A combination that is not built returns SKINNY_EINVAL.
+ * ------------------------------------------------------------------------- */
+int nvfp4_gemm_config(const void* w_packed, const uint16_t* x, uint16_t* y,
+                      int M, int K, int N, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, int engine,
+                      int ct, int nw);
+int fp8_gemm_config(const uint8_t* w, const float* block_scales,
+                    const uint16_t* x, uint16_t* y, int M, int K, int N,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                    int engine, int ct, int nw);
+int lm_head_gemm_argmax_config(const void* w_packed, const uint16_t* x,
+                               int32_t* idx, uint16_t* logits, int M, int K,
+                               int N, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, int engine, int ct, int nw);
+
+/* Workspace bytes a call needs. op: 0 = nvfp4_gemm, 1 = fp8_gemm,
+ * 2 = lm_head_gemm_argmax.  Returns 0 for an unsupported op or shape. */
+size_t skinny_workspace_bytes(int op, int M, int K, int N);
+
+/* Static description of a status code (never NULL). */
+const char* skinny_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_H */

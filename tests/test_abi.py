@@ -1,0 +1,211 @@
+"""C ABI checks that need no GPU: exports, argument validation, packer, quantizers.
+
+Every error path here returns before the library makes any HIP call, so these
+tests run on machines without a GPU.  Fake device pointers are plain integers
+and are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import fp8_quantized_skinny_amd as sk
+from fp8_quantized_skinny_amd import synth
+from fp8_quantized_skinny_amd._lib import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 0x10000          # fake, 16-byte aligned "device" address (never touched)
+MIS = 0x10008        # 8-byte aligned only
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "skinny.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:int|size_t|const char\*)\s+(\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _header_functions()
+    assert {"nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax"} <= set(names)
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror_covers_all_codes():
+    for s in range(7):
+        assert sk.strerror(s) and sk.strerror(s) != "unknown status"
+    assert sk.strerror(99) == "unknown status"
+
+
+def _gemm(M=1, K=256, N=512, w=A, x=A, y=A, ws=None, wsb=0):
+    return lib().nvfp4_gemm(w, x, y, M, K, N, ws, wsb, None)
+
+
+def test_nvfp4_gemm_argument_errors():
+    assert _gemm(w=None) == sk.EINVAL
+    assert _gemm(x=None) == sk.EINVAL
+    assert _gemm(y=None) == sk.EINVAL
+    for M in (0, 9, -1):
+        assert _gemm(M=M) == sk.ESHAPE
+    for K in (0, 8, 24, 100, (1 << 20) + 16):
+        assert _gemm(K=K) == sk.ESHAPE
+    assert _gemm(N=0) == sk.ESHAPE
+    assert _gemm(w=MIS) == sk.EALIGN
+    assert _gemm(x=MIS) == sk.EALIGN
+    assert _gemm(y=MIS) == sk.EALIGN
+
+
+def test_explicit_config_rejections():
+    L = lib()
+    # VALU engine is M = 1 only; unknown engine / tile counts / wave counts are rejected.
+    assert L.nvfp4_gemm_config(A, A, A, 2, 256, 512, None, 0, None, 0, 1, 4) == sk.EINVAL
+    assert L.nvfp4_gemm_config(A, A, A, 1, 256, 512, None, 0, None, 2, 1, 4) == sk.EINVAL
+    assert L.nvfp4_gemm_config(A, A, A, 1, 256, 512, None, 0, None, 1, 3, 4) == sk.EINVAL
+    assert L.nvfp4_gemm_config(A, A, A, 1, 256, 512, None, 0, None, 1, 1, 5) == sk.EINVAL
+    assert L.fp8_gemm_config(A, A, A, A, 1, 256, 512, None, 0, None, 0, 1, 4) == sk.EINVAL
+    assert L.lm_head_gemm_argmax_config(A, A, A, None, 1, 256, 512, A, 256, None, 0, 1, 4) == sk.EINVAL
+
+
+def test_fp8_gemm_argument_errors():
+    L = lib()
+    f = lambda **k: L.fp8_gemm(k.get("w", A), k.get("s", A), k.get("x", A), k.get("y", A), k.get("M", 1),
+                               k.get("K", 256), k.get("N", 256), None, 0, None)
+    assert f(w=None) == sk.EINVAL and f(s=None) == sk.EINVAL
+    assert f(M=9) == sk.ESHAPE and f(K=40) == sk.ESHAPE and f(N=0) == sk.ESHAPE
+    assert f(w=MIS) == sk.EALIGN and f(s=A + 2) == sk.EALIGN
+
+
+def test_lm_head_argument_errors():
+    L = lib()
+    need = sk.workspace_bytes(sk.OP_LM_HEAD, 8, 5120, 151936)
+    assert need >= 8 * 8 + 4
+    f = lambda **k: L.lm_head_gemm_argmax(k.get("w", A), k.get("x", A), k.get("idx", A), k.get("lg", None),
+                                          k.get("M", 1), 256, 512, k.get("ws", A), k.get("wsb", need), None)
+    assert f(idx=None) == sk.EINVAL
+    assert f(ws=None) == sk.EINVAL
+    assert f(wsb=need - 1) == sk.ESIZE
+    assert f(ws=MIS) == sk.EALIGN
+    assert f(lg=MIS) == sk.EALIGN
+    assert f(idx=A + 2) == sk.EALIGN
+    assert f(M=9) == sk.ESHAPE
+
+
+def test_workspace_sizes():
+    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 5120, 34816) == 0
+    assert sk.workspace_bytes(sk.OP_FP8, 4, 5120, 7168) == 0
+    assert sk.workspace_bytes(sk.OP_LM_HEAD, 0, 5120, 7168) == 0      # bad shape
+    assert sk.workspace_bytes(7, 1, 5120, 7168) == 0
+
+
+# ------------------------------------------------------------------- packer
+def _pack_raw(codes, scales, g, K, N, out, size):
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+    sz = ctypes.c_size_t(size)
+    st = lib().nvfp4_pack(p(codes), p(scales), g, K, N, p(out), ctypes.byref(sz))
+    return st, sz.value
+
+
+def test_pack_size_and_header():
+    for K, N in [(256, 512), (272, 100), (5120, 17408), (16, 1)]:
+        kc, nt = -(-K // 128), -(-N // 16)
+        sg = -(-kc // 8)
+        assert sk.packed_bytes(K, N) == 256 + nt * kc * 1024 + nt * sg * 1024
+    codes = np.zeros((100, 136), np.uint8)
+    scales = np.zeros((100, 17), np.uint8)
+    blob = sk.nvfp4_pack(codes, scales, 0.125, 272, 100)
+    h = blob[:64]
+    assert bytes(h[:4]) == b"SKN4"
+    assert list(h[4:28].view(np.uint32)) == [1, 272, 100, 3, 7, 1]
+    assert h[28:32].view(np.float32)[0] == np.float32(0.125)
+
+
+def test_pack_errors():
+    c = np.zeros((4, 128), np.uint8)
+    s = np.zeros((4, 16), np.uint8)
+    out = np.zeros(sk.packed_bytes(256, 4), np.uint8)
+    assert _pack_raw(c, s, 1.0, 256, 4, out, out.size)[0] == sk.OK
+    assert _pack_raw(c, s, 1.0, 256, 4, out, out.size - 1)[0] == sk.ESIZE
+    assert _pack_raw(None, s, 1.0, 256, 4, out, out.size)[0] == sk.EINVAL
+    assert _pack_raw(c, s, float("nan"), 256, 4, out, out.size)[0] == sk.EINVAL
+    assert _pack_raw(c, s, -1.0, 256, 4, out, out.size)[0] == sk.EINVAL
+    assert _pack_raw(c, s, 1.0, 250, 4, out, out.size)[0] == sk.ESHAPE
+    for bad in (0x7F, 0xFF):
+        s2 = s.copy()
+        s2[3, 15] = bad
+        assert _pack_raw(c, s2, 1.0, 256, 4, out, out.size)[0] == sk.EFORMAT
+
+
+@pytest.mark.parametrize("K,N", [(256, 32), (272, 20), (1040, 17)])
+def test_pack_places_every_byte_once(K, N):
+    """Distinct byte patterns go exactly where the documented layout says."""
+    rng = np.random.default_rng(K + N)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8)   # no NaN codes
+    blob = sk.nvfp4_pack(codes, scales, 1.0, K, N)
+    kc, nt = -(-K // 128), -(-N // 16)
+    sg = -(-kc // 8)
+    ctiles = blob[256:256 + nt * kc * 1024].reshape(nt, kc, 4, 16, 16)     # tile, chunk, grp, col, byte
+    stiles = blob[256 + nt * kc * 1024:].reshape(nt, sg, 4, 16, 8, 2)      # tile, group, grp, col, chunk, half
+    seen_c = np.zeros_like(codes, dtype=np.int64)
+    for n in range(N):
+        t, c = divmod(n, 16)
+        for k in range(0, K, 2):
+            kcc, r = divmod(k, 128)
+            grp, i = divmod(r, 32)
+            assert ctiles[t, kcc, grp, c, i // 2] == codes[n, k // 2]
+            seen_c[n, k // 2] += 1
+        for b in range(K // 16):
+            k = 16 * b
+            kcc, r = divmod(k, 128)
+            grp, rr = divmod(r, 32)
+            assert stiles[t, kcc // 8, grp, c, kcc % 8, rr // 16] == scales[n, b]
+    assert (seen_c == 1).all()
+    # padding (columns >= N, K >= real K) is zero
+    pad_cols = np.arange(nt * 16) >= N
+    assert not ctiles[:, :, :, :, :].reshape(nt, kc, 4, 16, 16).transpose(0, 3, 1, 2, 4).reshape(nt * 16, -1)[pad_cols].any()
+
+
+def test_pack_is_deterministic():
+    w, _ = synth.draw(1, 384, 48, seed=2)
+    c, s, g = sk.nvfp4_quantize(w)
+    assert np.array_equal(sk.nvfp4_pack(c, s, g, 384, 48), sk.nvfp4_pack(c, s, g, 384, 48))
+
+
+# --------------------------------------------------------------- quantizers
+@pytest.mark.parametrize("K,N,seed", [(256, 512, 0), (272, 100, 1), (16, 1, 2), (1040, 129, 3)])
+def test_host_quantizers_match_oracle_bit_exact(K, N, seed):
+    w, _ = synth.draw(1, K, N, seed=seed)
+    w[:16, 0] = 0.0                            # one all-zero block
+    w[min(20, K - 1), :] = -0.0                # negative zeros
+    c1, s1, g1 = sk.nvfp4_quantize(w)
+    c2, s2, g2 = oracle.nvfp4_quantize(w)
+    assert g1 == g2 and np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    a1, b1 = sk.fp8_quantize(w)
+    a2, b2 = oracle.fp8_quantize(w)
+    assert np.array_equal(a1, a2) and np.array_equal(b1, b2)
+
+
+def test_host_quantizer_special_inputs():
+    z = np.zeros((32, 8), np.float32)
+    c, s, g = sk.nvfp4_quantize(z)
+    assert g == 0 and not c.any() and not s.any()
+    bad = np.ones((32, 8), np.float32)
+    bad[3, 3] = np.inf
+    with pytest.raises(sk.SkinnyError):
+        sk.nvfp4_quantize(bad)
+    with pytest.raises(sk.SkinnyError):
+        sk.fp8_quantize(bad)
+    # huge dynamic range: saturation paths agree with the oracle
+    w = np.geomspace(1e-30, 1e30, 32 * 16).astype(np.float32).reshape(32, 16)
+    w[::3] *= -1
+    c1, s1, g1 = sk.nvfp4_quantize(w)
+    c2, s2, g2 = oracle.nvfp4_quantize(w)
+    assert g1 == g2 and np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    a1, b1 = sk.fp8_quantize(w)
+    a2, b2 = oracle.fp8_quantize(w)
+    assert np.array_equal(a1, a2) and np.array_equal(b1, b2)

@@ -1,0 +1,103 @@
+"""GPU parity at the full decode shapes, in the kernel choice the benchmark times.
+
+Outputs are checked on sampled columns, which the oracle computes one by one
+(first and last tiles plus 512 random columns); the lm_head argmax is checked
+against the oracle's full float64 logit rows.  Runs print their steps so a
+long input preparation is visible.
+"""
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_quantized_skinny_amd as sk
+from fp8_quantized_skinny_amd import workload, synth
+
+pytestmark = pytest.mark.gpu
+
+REL_FROB = 2e-3
+ROW_MAX = 1e-2
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _cols(N, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N), rng.choice(N, 512, replace=False)]))
+
+
+def _log(msg):
+    print(f"[full] {time.strftime('%H:%M:%S')} {msg}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["up", "gate_up", "down"])
+def test_nvfp4_full_shape_sampled(name):
+    _log(f"preparing {name}")
+    case = workload.named_case(name)
+    K, N = case["K"], case["N"]
+    blob = dev(case["blob"])
+    cols = _cols(N)
+    for M in synth.WORKLOADS[name][1]:
+        x = dev(case["x"][:M])
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        sk.nvfp4_gemm(blob, x, y)
+        y2 = torch.empty_like(y)
+        sk.nvfp4_gemm(blob, x, y2)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2), "not deterministic"
+        got = y.float().cpu().numpy()[:, cols]
+        ref = oracle.nvfp4_gemm(case["x"][:M], case["codes"], case["scales"], case["g"], cols=cols)
+        m = oracle.compare(got, ref)
+        _log(f"{name} M={M}: {m}")
+        assert m["rel_frob"] <= REL_FROB and m["row_max"] <= ROW_MAX, m
+        assert np.isfinite(y.float().cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("name", ["qkv", "o_proj"])
+def test_fp8_full_shape_sampled(name):
+    _log(f"preparing {name}")
+    case = workload.named_case(name)
+    K, N = case["K"], case["N"]
+    w, s = dev(case["codes"]), dev(case["scales"])
+    cols = _cols(N)
+    for M in synth.WORKLOADS[name][1]:
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        sk.fp8_gemm(w, s, dev(case["x"][:M]), y)
+        torch.cuda.synchronize()
+        got = y.float().cpu().numpy()[:, cols]
+        ref = oracle.fp8_gemm(case["x"][:M], case["codes"], case["scales"], cols=cols)
+        m = oracle.compare(got, ref)
+        _log(f"{name} M={M}: {m}")
+        assert m["rel_frob"] <= REL_FROB and m["row_max"] <= ROW_MAX, m
+
+
+def test_lm_head_full_shape_argmax_bit_exact():
+    _log("preparing lm_head")
+    case = workload.named_case("lm_head")
+    K, N = case["K"], case["N"]
+    blob = dev(case["blob"])
+    _log("oracle logits (float64, full rows)")
+    ref = oracle.nvfp4_gemm(case["x"], case["codes"], case["scales"], case["g"])
+    want, margin = oracle.argmax_rows(ref)
+    _log(f"oracle argmax {want} margins {np.round(margin, 4)}")
+    ws = torch.zeros(sk.workspace_bytes(sk.OP_LM_HEAD, 8, K, N), dtype=torch.uint8, device="cuda")
+    cols = _cols(N)
+    for M in (1, 8):
+        idx = torch.empty((M,), dtype=torch.int32, device="cuda")
+        lg = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        sk.lm_head_gemm_argmax(blob, dev(case["x"][:M]), idx, N, logits=lg, workspace=ws)
+        idx2 = torch.empty_like(idx)
+        sk.lm_head_gemm_argmax(blob, dev(case["x"][:M]), idx2, N, workspace=ws)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        _log(f"lm_head M={M}: gpu {got}")
+        assert np.array_equal(got, want[:M]), (got, want[:M], margin[:M])
+        assert torch.equal(idx, idx2)
+        m = oracle.compare(lg.float().cpu().numpy()[:, cols], ref[:M, cols])
+        assert m["rel_frob"] <= REL_FROB and m["row_max"] <= ROW_MAX, m
+        assert not ws.any()

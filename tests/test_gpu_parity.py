@@ -1,0 +1,219 @@
+"""GPU parity of the HIP kernels against the CPU oracle at small and ragged shapes.
+
+Bars (element by element, same seeded inputs on both sides):
+  * dequantized weights before the global scale: exact (one-hot activations)
+  * GEMM outputs: rel. Frobenius error <= 2e-3 and, per row,
+    max |error| <= 1e-2 * RMS of the oracle's row
+  * argmax indices: identical
+Every kernel variant (engine, column tiles per workgroup, wavefronts per
+workgroup) is covered, at shapes that span several tiles and chunks and leave
+ragged tails in K (not a multiple of 128) and N (not a multiple of 16).
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_quantized_skinny_amd as sk
+from fp8_quantized_skinny_amd import workload
+
+pytestmark = pytest.mark.gpu
+
+REL_FROB = 2e-3
+ROW_MAX = 1e-2
+CT_NW = list(itertools.product((1, 2, 4), (4, 8)))
+NVFP4_CFGS = [(1, ct, nw) for ct, nw in CT_NW]          # MFMA engine, any M
+VALU_CFGS = [(0, ct, nw) for ct, nw in CT_NW]           # VALU engine, M = 1
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _check(y_gpu, y_ref, what):
+    m = oracle.compare(y_gpu, y_ref)
+    assert m["rel_frob"] <= REL_FROB and m["row_max"] <= ROW_MAX, f"{what}: {m}"
+    return m
+
+
+def run_nvfp4(case, M=None, config=None, guard=0):
+    M = case["M"] if M is None else M
+    K, N = case["K"], case["N"]
+    blob = dev(case["blob"])
+    x = dev(case["x"][:M])
+    buf = torch.full((M * N + 2 * guard,), float("nan"), dtype=torch.float16, device="cuda")
+    y = buf[guard:guard + M * N].view(M, N)
+    sk.nvfp4_gemm(blob, x, y, config=config)
+    torch.cuda.synchronize()
+    if guard:
+        assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + M * N:]).all(), "guard overwritten"
+    return y.float().cpu().numpy()
+
+
+def run_fp8(case, M=None, config=None):
+    M = case["M"] if M is None else M
+    K, N = case["K"], case["N"]
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    sk.fp8_gemm(dev(case["codes"]), dev(case["scales"]), dev(case["x"][:M]), y, config=config)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy()
+
+
+def ref_nvfp4(case, M=None):
+    M = case["M"] if M is None else M
+    return oracle.nvfp4_gemm(case["x"][:M], case["codes"], case["scales"], case["g"])
+
+
+def ref_fp8(case, M=None):
+    M = case["M"] if M is None else M
+    return oracle.fp8_gemm(case["x"][:M], case["codes"], case["scales"])
+
+
+SMALL_NVFP4 = [(1, 256, 512), (1, 272, 100), (3, 400, 300), (8, 1040, 1000), (8, 2048, 48), (2, 16, 7)]
+
+
+@pytest.fixture(scope="module")
+def small_nvfp4():
+    return {s: workload.nvfp4_case(*s, seed=sum(s)) for s in SMALL_NVFP4}
+
+
+# ------------------------------------------------------------ exactness
+@pytest.mark.parametrize("K,N", [(256, 512), (272, 100)])
+def test_nvfp4_one_hot_reproduces_dequantized_weights_exactly(K, N):
+    """With g = 1 and one-hot rows, y equals e2m1(q) * e4m3(s) exactly (fp16 holds it)."""
+    case = workload.nvfp4_case(1, K, N, seed=5)
+    blob = dev(sk.nvfp4_pack(case["codes"], case["scales"], 1.0, K, N))
+    deq = oracle.nvfp4_dequant_unscaled(case["codes"], case["scales"], K)       # [K, N]
+    assert np.array_equal(deq.astype(np.float16).astype(np.float64), deq)
+    eye = torch.eye(K, dtype=torch.float16, device="cuda")
+    for cfg in NVFP4_CFGS + VALU_CFGS:
+        rows = 1 if cfg[0] == 0 else 8
+        out = np.empty((K, N))
+        for r0 in range(0, K, rows):
+            y = torch.empty((rows, N), dtype=torch.float16, device="cuda")
+            sk.nvfp4_gemm(blob, eye[r0:r0 + rows].contiguous(), y, config=cfg)
+            out[r0:r0 + rows] = y.float().cpu().numpy()
+        assert np.array_equal(out, deq), f"config {cfg}: {np.argwhere(out != deq)[:5]}"
+
+
+def test_fp8_one_hot_reproduces_codes_exactly():
+    """Random finite E4M3 codes, power-of-two block scales: y = e4m3(c) * S exactly."""
+    K, N = 272, 200
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C
+    scales = np.ldexp(1.0, rng.integers(-6, 2, size=(2, 3))).astype(np.float32)
+    case = {"codes": codes, "scales": scales, "K": K, "N": N}
+    deq = oracle.fp8_dequant(codes, scales)
+    assert np.array_equal(deq.astype(np.float16).astype(np.float64), deq)
+    eye = np.eye(K, dtype=np.float16)
+    for ct, nw in CT_NW:
+        out = np.empty((K, N))
+        for r0 in range(0, K, 8):
+            case["x"] = eye[r0:r0 + 8]
+            out[r0:r0 + 8] = run_fp8(case, M=8, config=(1, ct, nw))
+        assert np.array_equal(out, deq), f"config {(ct, nw)}"
+
+
+# -------------------------------------------------------- tolerance parity
+@pytest.mark.parametrize("shape", SMALL_NVFP4)
+def test_nvfp4_parity_all_configs(small_nvfp4, shape):
+    case = small_nvfp4[shape]
+    ref = ref_nvfp4(case)
+    cfgs = NVFP4_CFGS + (VALU_CFGS if case["M"] == 1 else [])
+    for cfg in cfgs:
+        _check(run_nvfp4(case, config=cfg), ref, f"{shape} {cfg}")
+    _check(run_nvfp4(case, guard=8), ref, f"{shape} default")
+
+
+def test_nvfp4_every_m():
+    case = workload.nvfp4_case(8, 1152, 520, seed=11)
+    for M in range(1, 9):
+        ref = ref_nvfp4(case, M)
+        _check(run_nvfp4(case, M=M), ref, f"M={M} default")
+        _check(run_nvfp4(case, M=M, config=(1, 2, 4)), ref, f"M={M} mfma")
+
+
+SMALL_FP8 = [(1, 256, 256), (2, 272, 100), (4, 400, 300), (8, 1040, 1000), (3, 16, 129)]
+
+
+@pytest.mark.parametrize("shape", SMALL_FP8)
+def test_fp8_parity_all_configs(shape):
+    case = workload.fp8_case(*shape, seed=sum(shape))
+    ref = ref_fp8(case)
+    for ct, nw in CT_NW:
+        _check(run_fp8(case, config=(1, ct, nw)), ref, f"{shape} {(ct, nw)}")
+    _check(run_fp8(case), ref, f"{shape} default")
+
+
+def test_deterministic_repeats(small_nvfp4):
+    case = small_nvfp4[(8, 1040, 1000)]
+    a = run_nvfp4(case)
+    b = run_nvfp4(case)
+    assert np.array_equal(a, b)
+    c1 = small_nvfp4[(1, 272, 100)]
+    assert np.array_equal(run_nvfp4(c1), run_nvfp4(c1))
+
+
+# ------------------------------------------------------------------ argmax
+def run_lm_head(case, M, config=None, logits=False, ws=None):
+    K, N = case["K"], case["N"]
+    idx = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    ws = ws if ws is not None else torch.zeros(sk.workspace_bytes(sk.OP_LM_HEAD, M, K, N), dtype=torch.uint8,
+                                               device="cuda")
+    lg = torch.empty((M, N), dtype=torch.float16, device="cuda") if logits else None
+    sk.lm_head_gemm_argmax(dev(case["blob"]), dev(case["x"][:M]), idx, N, logits=lg, workspace=ws, config=config)
+    torch.cuda.synchronize()
+    assert not ws.any(), "workspace not left zero-filled"
+    return idx.cpu().numpy(), (lg.float().cpu().numpy() if logits else None)
+
+
+@pytest.mark.parametrize("shape", [(1, 256, 1000), (8, 512, 3000), (5, 272, 777), (8, 1024, 16)])
+def test_lm_head_argmax_and_logits(shape):
+    M, K, N = shape
+    case = workload.nvfp4_case(*shape, seed=sum(shape))
+    ref = ref_nvfp4(case)
+    want, margin = oracle.argmax_rows(ref)
+    for cfg in NVFP4_CFGS:
+        idx, lg = run_lm_head(case, M, config=cfg, logits=True)
+        assert np.array_equal(idx, want), f"{shape} {cfg}: {idx} vs {want} (margins {margin})"
+        _check(lg, ref, f"{shape} {cfg} logits")
+    idx, _ = run_lm_head(case, M)
+    assert np.array_equal(idx, want)
+
+
+def test_lm_head_ties_go_to_lowest_column():
+    M, K, N = 4, 256, 700
+    case = workload.nvfp4_case(M, K, N, seed=21)
+    ref = ref_nvfp4(case)
+    best = oracle.argmax_rows(ref)[0]
+    codes, scales = case["codes"].copy(), case["scales"].copy()
+    # Copy each row's winning column into a lower and a higher column: exact ties.
+    for m, b in enumerate(best):
+        for dst in (max(int(b) - 37, 0) if m % 2 else 3, N - 1 - m):
+            codes[dst], scales[dst] = codes[b], scales[b]
+    case2 = dict(case, codes=codes, scales=scales, blob=sk.nvfp4_pack(codes, scales, case["g"], K, N))
+    ref2 = ref_nvfp4(case2)
+    want, _ = oracle.argmax_rows(ref2)
+    for cfg in NVFP4_CFGS:
+        idx, _ = run_lm_head(case2, M, config=cfg)
+        assert np.array_equal(idx, want), f"{cfg}: {idx} vs {want}"
+
+
+def test_lm_head_zero_weights_and_shared_workspace():
+    M, K, N = 8, 256, 300
+    case = workload.nvfp4_case(M, K, N, seed=22)
+    zc = np.zeros_like(case["codes"])
+    zs = np.zeros_like(case["scales"])
+    zero = dict(case, codes=zc, scales=zs, blob=sk.nvfp4_pack(zc, zs, case["g"], K, N))
+    idx, lg = run_lm_head(zero, M, logits=True)
+    assert np.array_equal(idx, np.zeros(M)) and not lg.any()
+    # one workspace reused across calls with different M
+    ws = torch.zeros(sk.workspace_bytes(sk.OP_LM_HEAD, 8, K, N), dtype=torch.uint8, device="cuda")
+    for Mi in (8, 1, 5, 8):
+        want, _ = oracle.argmax_rows(ref_nvfp4(case, Mi))
+        idx, _ = run_lm_head(case, Mi, ws=ws)
+        assert np.array_equal(idx, want), Mi
