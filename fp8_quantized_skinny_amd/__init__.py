@@ -56,8 +56,20 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def workspace_bytes(op, M, K, N):
-    return int(lib().skinny_workspace_bytes(op, M, K, N))
+def workspace_bytes(op, M, K, N, config=None):
+    """Workspace bytes of a call; config = (engine, ct, nw, ksplit) or None for the library's pick."""
+    if config is None:
+        return int(lib().skinny_workspace_bytes(op, M, K, N))
+    return int(lib().skinny_workspace_bytes_config(op, M, K, N, *config))
+
+
+def _workspace(workspace, need, where):
+    import torch
+    if need == 0 and workspace is None:
+        return None, 0
+    if workspace is None or workspace.numel() < need:
+        raise ValueError(f"{where}: a zero-filled workspace of at least {need} bytes is required")
+    return _dev(workspace, torch.uint8, "workspace"), workspace.numel()
 
 
 def strerror(status):
@@ -121,7 +133,8 @@ def _shape_checks(x, M, K, out, N, name):
 def nvfp4_gemm(w_packed, x, y, K=None, N=None, workspace=None, stream=None, config=None):
     """y[M, N] fp16 = x[M, K] fp16 . dequant(W); w_packed: CUDA uint8 blob from nvfp4_pack.
 
-    config: optional (engine, ct, nw) kernel choice; default lets the library pick."""
+    config: optional (engine, ct, nw, ksplit) kernel choice; default lets the library pick.
+    workspace: CUDA uint8 tensor, zero-filled once, when workspace_bytes(OP_NVFP4, ...) > 0."""
     import torch
     M, Kx = x.shape
     K = Kx if K is None else K
@@ -131,7 +144,7 @@ def nvfp4_gemm(w_packed, x, y, K=None, N=None, workspace=None, stream=None, conf
         raise ValueError("w_packed is smaller than the blob for this K, N")
     wp = _dev(w_packed, torch.uint8, "w_packed")
     xp, yp = _dev(x, torch.float16, "x"), _dev(y, torch.float16, "y")
-    ws, wsb = (None, 0) if workspace is None else (_dev(workspace, torch.uint8, "workspace"), workspace.numel())
+    ws, wsb = _workspace(workspace, workspace_bytes(OP_NVFP4, M, K, N, config), "nvfp4_gemm")
     if config is None:
         st = lib().nvfp4_gemm(wp, xp, yp, M, K, N, ws, wsb, _stream(stream))
     else:
@@ -151,7 +164,7 @@ def fp8_gemm(w, block_scales, x, y, workspace=None, stream=None, config=None):
     wp = _dev(w, torch.uint8, "w")
     sp = _dev(block_scales, torch.float32, "block_scales")
     xp, yp = _dev(x, torch.float16, "x"), _dev(y, torch.float16, "y")
-    ws, wsb = (None, 0) if workspace is None else (_dev(workspace, torch.uint8, "workspace"), workspace.numel())
+    ws, wsb = _workspace(workspace, workspace_bytes(OP_FP8, M, K, N, config), "fp8_gemm")
     if config is None:
         st = lib().fp8_gemm(wp, sp, xp, yp, M, K, N, ws, wsb, _stream(stream))
     else:
@@ -171,17 +184,13 @@ def lm_head_gemm_argmax(w_packed, x, idx, N, logits=None, workspace=None, stream
         raise ValueError("idx must hold M elements")
     if w_packed.numel() < packed_bytes(K, N):
         raise ValueError("w_packed is smaller than the blob for this K, N")
-    need = workspace_bytes(OP_LM_HEAD, M, K, N)
-    if workspace is None or workspace.numel() < need:
-        raise ValueError(f"workspace of at least {need} bytes is required")
+    ws, wsb = _workspace(workspace, workspace_bytes(OP_LM_HEAD, M, K, N, config), "lm_head_gemm_argmax")
     wp = _dev(w_packed, torch.uint8, "w_packed")
     xp, ip = _dev(x, torch.float16, "x"), _dev(idx, torch.int32, "idx")
     lp = None if logits is None else _dev(logits, torch.float16, "logits")
-    ws = _dev(workspace, torch.uint8, "workspace")
     if config is None:
-        st = lib().lm_head_gemm_argmax(wp, xp, ip, lp, M, K, N, ws, workspace.numel(), _stream(stream))
+        st = lib().lm_head_gemm_argmax(wp, xp, ip, lp, M, K, N, ws, wsb, _stream(stream))
     else:
-        st = lib().lm_head_gemm_argmax_config(wp, xp, ip, lp, M, K, N, ws, workspace.numel(), _stream(stream),
-                                              *config)
+        st = lib().lm_head_gemm_argmax_config(wp, xp, ip, lp, M, K, N, ws, wsb, _stream(stream), *config)
     _check(st, "lm_head_gemm_argmax")
     return idx

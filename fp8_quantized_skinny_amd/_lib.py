@@ -15,12 +15,13 @@ def _declare(lib):
     sig = {
         "nvfp4_pack": (c_int, [P, P, c_float, c_int, c_int, P, ctypes.POINTER(c_size_t)]),
         "nvfp4_gemm": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
-        "nvfp4_gemm_config": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int]),
+        "nvfp4_gemm_config": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int, c_int]),
         "fp8_gemm": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
-        "fp8_gemm_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int]),
+        "fp8_gemm_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int, c_int]),
         "lm_head_gemm_argmax": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
         "lm_head_gemm_argmax_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P,
-                                               c_int, c_int, c_int]),
+                                               c_int, c_int, c_int, c_int]),
+        "skinny_workspace_bytes_config": (c_size_t, [c_int] * 8),
         "nvfp4_quantize": (c_int, [P, c_int, c_int, P, P, ctypes.POINTER(c_float)]),
         "fp8_quantize": (c_int, [P, c_int, c_int, P, P]),
         "skinny_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
@@ -45,4 +46,4 @@ def lib():
 
 EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp4_quantize",
             "fp8_quantize", "skinny_workspace_bytes", "skinny_strerror", "nvfp4_gemm_config",
-            "fp8_gemm_config", "lm_head_gemm_argmax_config")
+            "fp8_gemm_config", "lm_head_gemm_argmax_config", "skinny_workspace_bytes_config")

@@ -8,13 +8,17 @@
 //
 // A 16-column tile times one 128-K chunk lies inside one 128 x 128 scale
 // block, so each chunk is contracted on the matrix cores into a fresh fp32
-// partial (E4M3 -> fp16 is exact) and then added to the accumulator times the
-// block scale in fp32.  Work split and cross-wavefront reduction follow the
-// NVFP4 kernels: CT tiles per workgroup, NW wavefronts splitting K.
+// partial (E4M3 -> fp16 is exact) that is then added to the accumulator times
+// the block scale in fp32.
 //
-// Lane (grp, col) of a wavefront loads, per chunk, two 16-byte pieces of
-// column col: K = 128kc + 64h + 16grp .. +16 for h = 0, 1, so each load
-// instruction covers 64 contiguous bytes of 16 columns.
+// Work split follows the NVFP4 kernels: a unit is one 16-column tile x 512 K
+// (four chunks, 8 KiB of codes); every wavefront loads one unit at once and
+// contracts it; a workgroup is CT tiles x S units along K (nw = CT * S), with
+// a K split over workgroups when K has more units.  x is copied into LDS once
+// per workgroup with direct-to-LDS loads.  Lane (grp, c) reads, per chunk, the
+// two 16-byte pieces K = 128j + 64h + 16grp .. +16 (h = 0, 1) of column c, so
+// each load instruction covers 64 contiguous bytes of 16 columns.  Pieces past
+// K or columns past N read a clamped valid address and are zeroed.
 #include <hip/hip_runtime.h>
 
 #include "common.cuh"
@@ -23,113 +27,208 @@
 namespace skinny {
 namespace {
 
+constexpr int kFp8UnitChunks = 4;
+constexpr int kFp8UnitK = kFp8UnitChunks * kChunkK;  // 512
+constexpr int kFp8PartFloats = 128;
+
 struct Fp8Args {
   const uint8_t* w;
   const float* scales;
   const _Float16* x;
   _Float16* y;
   int M, K, N;
-  int kc, nt, kb;  // K chunks, column tiles, scale blocks along K
+  int nt, kb, ku;  // column tiles, scale blocks along K, units along K
+  int ksplit, S;
+  float* part;
+  uint32_t* tile_cnt;
 };
 
-template <int CT, int NW>
-__global__ __launch_bounds__(NW * 64) void fp8_mfma(Fp8Args a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = lane >> 4, col = lane & 15;
-  const int tile0 = blockIdx.x * CT;
-  const int c0 = (a.kc * wave) / NW, c1 = (a.kc * (wave + 1)) / NW;
-
-  f32x4 acc[CT];
-#pragma unroll
-  for (int t = 0; t < CT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Column of this lane in each tile; columns past N read column N-1 (their
-  // results are never stored), so every load stays inside the weights.
-  const uint8_t* wp[CT];
-  const float* sp[CT];
-#pragma unroll
-  for (int t = 0; t < CT; ++t) {
-    const int n = min((tile0 + t) * kTileCols + col, a.N - 1);
-    wp[t] = a.w + static_cast<size_t>(n) * a.K + grp * 16;
-    sp[t] = a.scales + static_cast<size_t>(min((tile0 + t) * kTileCols, a.N - 1) / 128) * a.kb;
+struct Fp8Plan {
+  int lane, wave, nw, S, tile0, s0, sw, t, s;
+  bool active;
+  __device__ Fp8Plan(const Fp8Args& a, int ct) {
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    nw = blockDim.x >> 6;
+    S = a.S;
+    tile0 = blockIdx.x * ct;
+    s0 = blockIdx.y * S;
+    sw = min(S, a.ku - s0);
+    t = wave / S;
+    s = wave % S;
+    active = s < sw;
   }
-  const bool xrow = col < a.M;
-  const _Float16* xr = a.x + static_cast<size_t>(xrow ? col : 0) * a.K + grp * 16;
-  const int kfull = a.K / kChunkK;
+};
 
-  for (int kc = c0; kc < c1; ++kc) {
-    const bool full = kc < kfull;
-    const int k0 = kc * kChunkK;
-    f16x8 xa[4];
+__device__ __forceinline__ int fp8_xs_stride(int S) { return S * kFp8UnitK + 8; }
+
+__device__ void fp8_stage_x(const Fp8Args& a, const Fp8Plan& P, _Float16* xs) {
+  const int RS = fp8_xs_stride(P.S);
+  const int kbase = P.s0 * kFp8UnitK;
+  const int kvalid = a.K - kbase;
+  if (kvalid < P.S * kFp8UnitK) {
+    for (int i = threadIdx.x; i < a.M * RS; i += blockDim.x)
+      if (i % RS >= kvalid) xs[i] = static_cast<_Float16>(0.0f);
+  }
+  const int nblocks = a.M * P.S;  // 1 KiB blocks = 512 halves = one unit of K
+  for (int b = P.wave; b < nblocks; b += P.nw) {
+    const int m = b / P.S, blk = b % P.S;
+    const int col = blk * 512 + P.lane * 8;
+    if (col < kvalid)
+      __builtin_amdgcn_global_load_lds(a.x + static_cast<size_t>(m) * a.K + kbase + col, xs + m * RS + blk * 512,
+                                       16, 0, 0);
+  }
+}
+
+// A fragments of chunk j: lane (row m = c, grp) holds, for MFMA i = 2h + s,
+// x[m][512u + 128j + 64h + 16grp + 8s .. +8]; zero for m >= M.
+__device__ __forceinline__ void fp8_read_x(f16x8 (&xa)[4], const _Float16* xrow, bool row, int j) {
+  if (row) {
+    const _Float16* p = xrow + j * kChunkK;
+    xa[0] = *reinterpret_cast<const f16x8*>(p);
+    xa[1] = *reinterpret_cast<const f16x8*>(p + 8);
+    xa[2] = *reinterpret_cast<const f16x8*>(p + 64);
+    xa[3] = *reinterpret_cast<const f16x8*>(p + 72);
+  } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // piece j: h = j >> 1, half s = j & 1 -> K = k0 + 64h + 16grp + 8s
-      const int ko = 64 * (j >> 1) + 8 * (j & 1);
-      xa[j] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (xrow && (full || k0 + ko + grp * 16 + 8 <= a.K))
-        xa[j] = *reinterpret_cast<const f16x8*>(xr + k0 + ko);
-    }
-    u32x4 w[CT][2];
-    float s[CT];
+    for (int i = 0; i < 4; ++i) xa[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+template <int J>
+__device__ __forceinline__ void fp8_steps(const u32x4 (&w)[kFp8UnitChunks][2], const float (&sc)[kFp8UnitChunks],
+                                          f16x8 (&x0)[4], f16x8 (&x1)[4], f32x4& acc, const _Float16* xrow, bool row) {
+  if constexpr (J < kFp8UnitChunks) {
+    f16x8 (&cur)[4] = (J & 1) ? x1 : x0;
+    f16x8 (&nxt)[4] = (J & 1) ? x0 : x1;
+    if constexpr (J + 1 < kFp8UnitChunks) fp8_read_x(nxt, xrow, row, J + 1);
+    f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[0], e4m3x8(w[J][0].x, w[J][0].y), p, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[1], e4m3x8(w[J][0].z, w[J][0].w), p, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[2], e4m3x8(w[J][1].x, w[J][1].y), p, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[3], e4m3x8(w[J][1].z, w[J][1].w), p, 0, 0, 0);
+    acc += sc[J] * p;
+    fp8_steps<J + 1>(w, sc, x0, x1, acc, xrow, row);
+  }
+}
+
+template <int CT>
+__global__ __launch_bounds__(kMaxWaves * 64) void fp8_mfma(Fp8Args a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const Fp8Plan P(a, CT);
+  _Float16* xs = reinterpret_cast<_Float16*>(lds);
+  f32x4* red = reinterpret_cast<f32x4*>(lds + ((a.M * fp8_xs_stride(P.S) * 2 + 15) & ~15));  // [nw][32]
+
+  fp8_stage_x(a, P, xs);
+  const int cl = P.lane & 15, grp = P.lane >> 4;
+  const int tt = min(P.tile0 + P.t, a.nt - 1);
+  u32x4 w[kFp8UnitChunks][2];
+  float sc[kFp8UnitChunks];
+  if (P.active) {
+    const int n = min(tt * kTileCols + cl, a.N - 1);
+    const uint8_t* row = a.w + static_cast<size_t>(n) * a.K;
+    const int u = P.s0 + P.s;
+    const int k0 = u * kFp8UnitK + grp * 16;
 #pragma unroll
-    for (int t = 0; t < CT; ++t) {
+    for (int j = 0; j < kFp8UnitChunks; ++j) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        w[t][h] = u32x4{0u, 0u, 0u, 0u};
-        if (full || k0 + 64 * h + grp * 16 + 16 <= a.K) w[t][h] = load16(wp[t] + k0 + 64 * h);
+        const int k = k0 + j * kChunkK + 64 * h;
+        const bool ok = k + 16 <= a.K;
+        const u32x4 v = load16(row + (ok ? k : 0));
+        w[j][h] = ok ? v : u32x4{0u, 0u, 0u, 0u};
       }
-      s[t] = sp[t][kc];
     }
+    // Scales of the tile's 128-column block for this unit's four K blocks (wave-uniform).
+    const float* srow = a.scales + static_cast<size_t>(min(tt * kTileCols, a.N - 1) / 128) * a.kb;
 #pragma unroll
-    for (int t = 0; t < CT; ++t) {
-      f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-      p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], e4m3x8(w[t][0].x, w[t][0].y), p, 0, 0, 0);
-      p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], e4m3x8(w[t][0].z, w[t][0].w), p, 0, 0, 0);
-      p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], e4m3x8(w[t][1].x, w[t][1].y), p, 0, 0, 0);
-      p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], e4m3x8(w[t][1].z, w[t][1].w), p, 0, 0, 0);
-      acc[t] += s[t] * p;
+    for (int j = 0; j < kFp8UnitChunks; ++j) {
+      const int kb = u * kFp8UnitChunks + j;
+      sc[j] = kb < a.kb ? srow[kb] : 0.0f;
     }
-  }
-
-  __shared__ f32x4 red[NW][CT][32];
-  if (lane < 32) {
-#pragma unroll
-    for (int t = 0; t < CT; ++t) red[wave][t][lane] = acc[t];
   }
   __syncthreads();
-  if (wave == 0 && lane < 32) {
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (P.active) {
+    const bool rowok = cl < a.M;
+    const _Float16* xrow = xs + (rowok ? cl : 0) * fp8_xs_stride(P.S) + P.s * kFp8UnitK + grp * 16;
+    f16x8 x0[4], x1[4];
+    fp8_read_x(x0, xrow, rowok, 0);
+    fp8_steps<0>(w, sc, x0, x1, acc, xrow, rowok);
+  }
+  if (P.lane < 32) red[P.wave * 32 + P.lane] = acc;
+  __syncthreads();
+
+  const bool fin = P.wave < CT && P.tile0 + P.wave < a.nt && P.lane < 32;
+  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (fin) {
+    for (int s = 0; s < P.sw; ++s) tot += red[(P.wave * P.S + s) * 32 + P.lane];
+    if (a.ksplit > 1) {
+      float* dst = a.part + (static_cast<size_t>(blockIdx.y) * a.nt + P.tile0 + P.wave) * kFp8PartFloats + 4 * P.lane;
 #pragma unroll
-    for (int t = 0; t < CT; ++t) {
-      f32x4 v = red[0][t][lane];
+      for (int i = 0; i < 4; ++i) store_shared(dst + i, tot[i]);
+    }
+  }
+  if (a.ksplit > 1) {
+    __shared__ int last;
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      last = counter_add(a.tile_cnt + blockIdx.x, 1u) == static_cast<uint32_t>(a.ksplit - 1);
+      if (last) counter_exch(a.tile_cnt + blockIdx.x, 0u);
+    }
+    __syncthreads();
+    if (!last) return;
+  }
+  if (fin) {
+    if (a.ksplit > 1) {
+      tot = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < a.ksplit; ++ks) {
+        const float* src = a.part + (static_cast<size_t>(ks) * a.nt + P.tile0 + P.wave) * kFp8PartFloats + 4 * P.lane;
 #pragma unroll
-      for (int w = 1; w < NW; ++w) v += red[w][t][lane];
-      const int n = (tile0 + t) * kTileCols + col;
-      if (tile0 + t < a.nt && n < a.N) {
+        for (int i = 0; i < 4; ++i) tot[i] += load_shared(src + i);
+      }
+    }
+    const int n = (P.tile0 + P.wave) * kTileCols + cl;
+    if (n < a.N) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = grp * 4 + r;
-          if (m < a.M) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(v[r]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int m = grp * 4 + i;
+        if (m < a.M) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(tot[i]);
       }
     }
   }
+}
+
+size_t fp8_lds_bytes(int M, int S, int nw) {
+  return ((static_cast<size_t>(M) * (S * kFp8UnitK + 8) * 2 + 15) & ~static_cast<size_t>(15)) +
+         static_cast<size_t>(nw) * 32 * sizeof(f32x4);
 }
 
 }  // namespace
 
-bool fp8_cfg_supported(const LaunchCfg& c, int M) {
-  (void)M;
-  return c.engine == 1 && (c.ct == 1 || c.ct == 2 || c.ct == 4) && (c.nw == 4 || c.nw == 8);
+size_t fp8_part_floats() { return kFp8PartFloats; }
+
+bool fp8_cfg_supported(const LaunchCfg& c, int M, int K) {
+  if (c.engine != 1 || !(c.ct == 1 || c.ct == 2 || c.ct == 4 || c.ct == 8)) return false;
+  if (c.nw < 1 || c.nw > kMaxWaves || c.nw % c.ct != 0 || c.ksplit < 1) return false;
+  const int ku = (K + kFp8UnitK - 1) / kFp8UnitK;
+  const int S = c.nw / c.ct;
+  if (static_cast<long>(c.ksplit) * S < ku || static_cast<long>(c.ksplit - 1) * S >= ku) return false;
+  return fp8_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
 }
 
-#define SKINNY_FP8_DISPATCH(CT, NW)                                                   \
-  if (cfg.ct == CT && cfg.nw == NW) {                                                 \
-    hipLaunchKernelGGL((fp8_mfma<CT, NW>), dim3(grid), dim3(NW * 64), 0, stream, a);  \
-    return hipGetLastError();                                                         \
+#define SKINNY_FP8_DISPATCH(CT)                                                    \
+  if (cfg.ct == CT) {                                                              \
+    hipLaunchKernelGGL((fp8_mfma<CT>), grid, dim3(cfg.nw * 64), lds, stream, a);   \
+    return hipGetLastError();                                                      \
   }
 
 hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x, uint16_t* y, int M,
-                      int K, int N, const LaunchCfg& cfg, hipStream_t stream) {
+                      int K, int N, const LaunchCfg& cfg, void* workspace, hipStream_t stream) {
+  const WorkspaceLayout wl = fp8_workspace_layout(cfg, M, K, N);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   Fp8Args a;
   a.w = w;
   a.scales = scales;
@@ -138,16 +237,19 @@ hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x, 
   a.M = M;
   a.K = K;
   a.N = N;
-  a.kc = (K + kChunkK - 1) / kChunkK;
   a.nt = (N + kTileCols - 1) / kTileCols;
   a.kb = (K + 127) / 128;
-  const int grid = (a.nt + cfg.ct - 1) / cfg.ct;
-  SKINNY_FP8_DISPATCH(1, 4)
-  SKINNY_FP8_DISPATCH(1, 8)
-  SKINNY_FP8_DISPATCH(2, 4)
-  SKINNY_FP8_DISPATCH(2, 8)
-  SKINNY_FP8_DISPATCH(4, 4)
-  SKINNY_FP8_DISPATCH(4, 8)
+  a.ku = (K + kFp8UnitK - 1) / kFp8UnitK;
+  a.ksplit = cfg.ksplit;
+  a.S = cfg.nw / cfg.ct;
+  a.part = wl.part_bytes ? reinterpret_cast<float*>(ws + wl.part_off) : nullptr;
+  a.tile_cnt = wl.tile_cnt_bytes ? reinterpret_cast<uint32_t*>(ws + wl.tile_cnt_off) : nullptr;
+  const dim3 grid((a.nt + cfg.ct - 1) / cfg.ct, cfg.ksplit);
+  const size_t lds = fp8_lds_bytes(M, a.S, cfg.nw);
+  SKINNY_FP8_DISPATCH(1)
+  SKINNY_FP8_DISPATCH(2)
+  SKINNY_FP8_DISPATCH(4)
+  SKINNY_FP8_DISPATCH(8)
   return hipErrorInvalidValue;
 }
 

@@ -4,6 +4,7 @@
 #include "skinny.h"
 #include "internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -69,20 +70,31 @@ int e4m3_code(double v) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_EHIP; }
 
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+// Kernel choice made by the library when the caller does not pick one.
+// S K spans (units) per workgroup, as many as fit the wavefront limit and,
+// for the MFMA engine, the LDS copy of x (about 72 KiB); K beyond that is
+// split over workgroups, evened out so every split gets the same spans.
+LaunchCfg pick_cfg(int engine, int ku, int lds_bytes_per_span) {
+  int s = std::min(ku, kMaxWaves);
+  if (lds_bytes_per_span > 0) s = std::min(s, std::max(1, (72 * 1024) / lds_bytes_per_span));
+  const int ksplit = (ku + s - 1) / s;
+  s = (ku + ksplit - 1) / ksplit;
+  return LaunchCfg{engine, 1, s, ksplit};
+}
+
 LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax) {
+  (void)N;
   const Geometry g = nvfp4_geometry(K, N);
-  LaunchCfg c{(M == 1 && !argmax) ? 0 : 1, 1, 4};
-  if (g.nt < 1024) c.nw = 8;
-  return c;
+  if (M == 1 && !argmax) return pick_cfg(0, g.ku, 0);
+  return pick_cfg(1, g.ku, M * (kUnitK + 8) * 2);
 }
 
 LaunchCfg default_fp8_cfg(int M, int K, int N) {
-  (void)M;
-  const int nt = (N + kTileCols - 1) / kTileCols;
-  (void)K;
-  LaunchCfg c{1, 1, 4};
-  if (nt < 1024) c.nw = 8;
-  return c;
+  (void)N;
+  const int ku = (K + 511) / 512;
+  return pick_cfg(1, ku, M * (512 + 8) * 2);
 }
 
 int nvfp4_common_checks(const void* w_packed, const uint16_t* x, const void* out, int M, int K, int N) {
@@ -93,19 +105,67 @@ int nvfp4_common_checks(const void* w_packed, const uint16_t* x, const void* out
   return SKINNY_OK;
 }
 
+int check_workspace(const void* ws, size_t have, size_t need) {
+  if (need == 0) return SKINNY_OK;
+  if (!ws) return SKINNY_EINVAL;
+  if (!aligned(ws, 16)) return SKINNY_EALIGN;
+  if (have < need) return SKINNY_ESIZE;
+  return SKINNY_OK;
+}
+
 }  // namespace
 
 namespace skinny {
 
 Geometry nvfp4_geometry(int K, int N) {
   Geometry g;
-  g.kc = (K + kChunkK - 1) / kChunkK;
+  g.ku = (K + kUnitK - 1) / kUnitK;
   g.nt = (N + kTileCols - 1) / kTileCols;
-  g.sg = (g.kc + kChunksPerScaleGroup - 1) / kChunksPerScaleGroup;
-  g.codes_bytes = static_cast<size_t>(g.nt) * g.kc * kTileBytes;
-  g.scales_bytes = static_cast<size_t>(g.nt) * g.sg * kTileBytes;
-  g.total_bytes = kHeaderBytes + g.codes_bytes + g.scales_bytes;
+  g.units_bytes = static_cast<size_t>(g.nt) * g.ku * kUnitBytes;
+  g.total_bytes = kHeaderBytes + g.units_bytes;
   return g;
+}
+
+WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N, bool argmax) {
+  const Geometry g = nvfp4_geometry(K, N);
+  WorkspaceLayout w{};
+  size_t off = 0;
+  if (argmax) {  // one 64-bit (logit, column) candidate per workgroup and row
+    const size_t groups = (g.nt + cfg.ct - 1) / cfg.ct;
+    w.keys_off = off;
+    w.keys_bytes = groups * M * 8;
+    off = align256(off + w.keys_bytes);
+  }
+  if (cfg.ksplit > 1) {
+    const size_t groups = (g.nt + cfg.ct - 1) / cfg.ct;
+    w.tile_cnt_off = off;
+    w.tile_cnt_bytes = groups * 4;
+    off = align256(off + w.tile_cnt_bytes);
+    w.part_off = off;
+    w.part_bytes = static_cast<size_t>(cfg.ksplit) * g.nt * nvfp4_part_floats() * 4;
+    off = align256(off + w.part_bytes);
+  }
+  w.total = off;
+  return w;
+}
+
+WorkspaceLayout fp8_workspace_layout(const LaunchCfg& cfg, int M, int K, int N) {
+  (void)M;
+  (void)K;
+  WorkspaceLayout w{};
+  size_t off = 0;
+  if (cfg.ksplit > 1) {
+    const size_t nt = (N + kTileCols - 1) / kTileCols;
+    const size_t groups = (nt + cfg.ct - 1) / cfg.ct;
+    w.tile_cnt_off = off;
+    w.tile_cnt_bytes = groups * 4;
+    off = align256(off + w.tile_cnt_bytes);
+    w.part_off = off;
+    w.part_bytes = static_cast<size_t>(cfg.ksplit) * nt * fp8_part_floats() * 4;
+    off = align256(off + w.part_bytes);
+  }
+  w.total = off;
+  return w;
 }
 
 }  // namespace skinny
@@ -125,12 +185,23 @@ const char* skinny_strerror(int status) {
   }
 }
 
+size_t skinny_workspace_bytes_config(int op, int M, int K, int N, int engine, int ct, int nw, int ksplit) {
+  if (check_shape(M, K, N)) return 0;
+  const LaunchCfg c{engine, ct, nw, ksplit};
+  switch (op) {
+    case 0: return nvfp4_cfg_supported(c, M, K, false) ? nvfp4_workspace_layout(c, M, K, N, false).total : 0;
+    case 1: return fp8_cfg_supported(c, M, K) ? fp8_workspace_layout(c, M, K, N).total : 0;
+    case 2: return nvfp4_cfg_supported(c, M, K, true) ? nvfp4_workspace_layout(c, M, K, N, true).total : 0;
+    default: return 0;
+  }
+}
+
 size_t skinny_workspace_bytes(int op, int M, int K, int N) {
   if (check_shape(M, K, N)) return 0;
   switch (op) {
-    case 0: return 0;
-    case 1: return 0;
-    case 2: return kArgmaxWorkspaceBytes;
+    case 0: return nvfp4_workspace_layout(default_nvfp4_cfg(M, K, N, false), M, K, N, false).total;
+    case 1: return fp8_workspace_layout(default_fp8_cfg(M, K, N), M, K, N).total;
+    case 2: return nvfp4_workspace_layout(default_nvfp4_cfg(M, K, N, true), M, K, N, true).total;
     default: return 0;
   }
 }
@@ -157,49 +228,31 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float gscale, int K,
   h.version = kBlobVersion;
   h.K = K;
   h.N = N;
-  h.kc = geo.kc;
+  h.ku = geo.ku;
   h.nt = geo.nt;
-  h.sg = geo.sg;
+  h.unit_bytes = kUnitBytes;
   h.g = gscale;
-  h.codes_off = kHeaderBytes;
-  h.codes_bytes = geo.codes_bytes;
-  h.scales_off = kHeaderBytes + geo.codes_bytes;
-  h.scales_bytes = geo.scales_bytes;
+  h.units_off = kHeaderBytes;
+  h.units_bytes = geo.units_bytes;
   std::memcpy(blob, &h, sizeof(h));
 
   const size_t row_codes = K / 2, row_scales = K / 16;
-  uint8_t* ctile = blob + kHeaderBytes;
   for (int t = 0; t < geo.nt; ++t) {
-    for (int kc = 0; kc < geo.kc; ++kc) {
-      uint8_t* dst = ctile + (static_cast<size_t>(t) * geo.kc + kc) * kTileBytes;
+    for (int u = 0; u < geo.ku; ++u) {
+      uint8_t* unit = blob + kHeaderBytes + (static_cast<size_t>(t) * geo.ku + u) * kUnitBytes;
+      uint8_t* svec = unit + kChunksPerUnit * kChunkBytes;
       for (int lane = 0; lane < 64; ++lane) {
         const int grp = lane >> 4, c = lane & 15;
         const int n = t * kTileCols + c;
         if (n >= N) continue;
-        const int k0 = kc * kChunkK + grp * 32;
-        for (int i = 0; i < 16; ++i) {
-          const int k = k0 + 2 * i;
-          if (k >= K) break;
-          dst[lane * 16 + i] = codes[static_cast<size_t>(n) * row_codes + k / 2];
-        }
-      }
-    }
-  }
-  uint8_t* sgrp = blob + h.scales_off;
-  for (int t = 0; t < geo.nt; ++t) {
-    for (int sg = 0; sg < geo.sg; ++sg) {
-      uint8_t* dst = sgrp + (static_cast<size_t>(t) * geo.sg + sg) * kTileBytes;
-      for (int lane = 0; lane < 64; ++lane) {
-        const int grp = lane >> 4, c = lane & 15;
-        const int n = t * kTileCols + c;
-        if (n >= N) continue;
-        for (int j = 0; j < kChunksPerScaleGroup; ++j) {
-          const int kc = sg * kChunksPerScaleGroup + j;
-          for (int half = 0; half < 2; ++half) {
-            const int k = kc * kChunkK + grp * 32 + 16 * half;
-            if (k >= K) continue;
-            dst[lane * 16 + 2 * j + half] = scales[static_cast<size_t>(n) * row_scales + k / 16];
-          }
+        for (int j = 0; j < kChunksPerUnit; ++j) {
+          const int k0 = u * kUnitK + j * kChunkK + grp * 32;  // this lane's 32-K run
+          if (k0 >= K) break;                                  // K % 16 == 0: runs end on blocks
+          uint8_t* dst = unit + j * kChunkBytes + lane * 16;
+          for (int i = 0; i < 16 && k0 + 2 * i < K; ++i)
+            dst[i] = codes[static_cast<size_t>(n) * row_codes + (k0 + 2 * i) / 2];
+          for (int half = 0; half < 2 && k0 + 16 * half < K; ++half)
+            svec[lane * 16 + 2 * j + half] = scales[static_cast<size_t>(n) * row_scales + (k0 + 16 * half) / 16];
         }
       }
     }
@@ -280,16 +333,16 @@ int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales) {
 
 int nvfp4_gemm_config(const void* w_packed, const uint16_t* x, uint16_t* y, int M, int K, int N,
                       void* workspace, size_t workspace_bytes, hipStream_t stream,
-                      int engine, int ct, int nw) {
+                      int engine, int ct, int nw, int ksplit) {
   int s = nvfp4_common_checks(w_packed, x, y, M, K, N);
   if (s) return s;
   if (!aligned(y, 16)) return SKINNY_EALIGN;
-  (void)workspace;
-  (void)workspace_bytes;
-  const LaunchCfg cfg{engine, ct, nw};
-  if (!nvfp4_cfg_supported(cfg, M, false)) return SKINNY_EINVAL;
+  const LaunchCfg cfg{engine, ct, nw, ksplit};
+  if (!nvfp4_cfg_supported(cfg, M, K, false)) return SKINNY_EINVAL;
+  s = check_workspace(workspace, workspace_bytes, nvfp4_workspace_layout(cfg, M, K, N, false).total);
+  if (s) return s;
   return launch_status(launch_nvfp4(static_cast<const uint8_t*>(w_packed), x, y, M, K, N, cfg,
-                                    nullptr, nullptr, stream));
+                                    nullptr, workspace, stream));
 }
 
 int nvfp4_gemm(const void* w_packed, const uint16_t* x, uint16_t* y, int M, int K, int N,
@@ -297,22 +350,23 @@ int nvfp4_gemm(const void* w_packed, const uint16_t* x, uint16_t* y, int M, int 
   int s = check_shape(M, K, N);
   if (s) return s;
   const LaunchCfg c = default_nvfp4_cfg(M, K, N, false);
-  return nvfp4_gemm_config(w_packed, x, y, M, K, N, workspace, workspace_bytes, stream, c.engine, c.ct, c.nw);
+  return nvfp4_gemm_config(w_packed, x, y, M, K, N, workspace, workspace_bytes, stream, c.engine, c.ct,
+                           c.nw, c.ksplit);
 }
 
 int fp8_gemm_config(const uint8_t* w, const float* block_scales, const uint16_t* x, uint16_t* y,
                     int M, int K, int N, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream, int engine, int ct, int nw) {
+                    hipStream_t stream, int engine, int ct, int nw, int ksplit) {
   if (!w || !block_scales || !x || !y) return SKINNY_EINVAL;
   int s = check_shape(M, K, N);
   if (s) return s;
   if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(block_scales, 4))
     return SKINNY_EALIGN;
-  (void)workspace;
-  (void)workspace_bytes;
-  const LaunchCfg cfg{engine, ct, nw};
-  if (!fp8_cfg_supported(cfg, M)) return SKINNY_EINVAL;
-  return launch_status(launch_fp8(w, block_scales, x, y, M, K, N, cfg, stream));
+  const LaunchCfg cfg{engine, ct, nw, ksplit};
+  if (!fp8_cfg_supported(cfg, M, K)) return SKINNY_EINVAL;
+  s = check_workspace(workspace, workspace_bytes, fp8_workspace_layout(cfg, M, K, N).total);
+  if (s) return s;
+  return launch_status(launch_fp8(w, block_scales, x, y, M, K, N, cfg, workspace, stream));
 }
 
 int fp8_gemm(const uint8_t* w, const float* block_scales, const uint16_t* x, uint16_t* y,
@@ -321,21 +375,20 @@ int fp8_gemm(const uint8_t* w, const float* block_scales, const uint16_t* x, uin
   if (s) return s;
   const LaunchCfg c = default_fp8_cfg(M, K, N);
   return fp8_gemm_config(w, block_scales, x, y, M, K, N, workspace, workspace_bytes, stream,
-                         c.engine, c.ct, c.nw);
+                         c.engine, c.ct, c.nw, c.ksplit);
 }
 
 int lm_head_gemm_argmax_config(const void* w_packed, const uint16_t* x, int32_t* idx,
                                uint16_t* logits, int M, int K, int N, void* workspace,
                                size_t workspace_bytes, hipStream_t stream, int engine, int ct,
-                               int nw) {
+                               int nw, int ksplit) {
   int s = nvfp4_common_checks(w_packed, x, idx, M, K, N);
   if (s) return s;
   if (!aligned(idx, 4) || (logits && !aligned(logits, 16))) return SKINNY_EALIGN;
-  if (!workspace) return SKINNY_EINVAL;
-  if (!aligned(workspace, 16)) return SKINNY_EALIGN;
-  if (workspace_bytes < skinny_workspace_bytes(2, M, K, N)) return SKINNY_ESIZE;
-  const LaunchCfg cfg{engine, ct, nw};
-  if (!nvfp4_cfg_supported(cfg, M, true)) return SKINNY_EINVAL;
+  const LaunchCfg cfg{engine, ct, nw, ksplit};
+  if (!nvfp4_cfg_supported(cfg, M, K, true)) return SKINNY_EINVAL;
+  s = check_workspace(workspace, workspace_bytes, nvfp4_workspace_layout(cfg, M, K, N, true).total);
+  if (s) return s;
   return launch_status(launch_nvfp4(static_cast<const uint8_t*>(w_packed), x, logits, M, K, N, cfg,
                                     idx, workspace, stream));
 }
@@ -347,7 +400,7 @@ int lm_head_gemm_argmax(const void* w_packed, const uint16_t* x, int32_t* idx, u
   if (s) return s;
   const LaunchCfg c = default_nvfp4_cfg(M, K, N, true);
   return lm_head_gemm_argmax_config(w_packed, x, idx, logits, M, K, N, workspace, workspace_bytes,
-                                    stream, c.engine, c.ct, c.nw);
+                                    stream, c.engine, c.ct, c.nw, c.ksplit);
 }
 
 }  // extern "C"

@@ -5,29 +5,37 @@
 // The weights are read once, compressed, straight from HBM into VGPRs and
 // widened to fp16 in registers just before use; there is no dequantized copy
 // anywhere ("NVFP4 on Volta!" author's post, section "What I actually
-// built").  Decode at batch 1..8 is bound by that weight stream, so every
-// design choice below is about keeping 128-bit loads in flight and keeping
-// the ALU work per weight small.
+// built").  Decode at batch 1..8 is bound by that weight stream, so the
+// design is about keeping as many 128-bit loads in flight as the chip holds.
 //
-// Work split: a workgroup owns CT column tiles (16 columns each) and the
-// whole K range; its NW wavefronts split the K chunks (128 K each) evenly and
-// their partial sums are added in LDS in wavefront order, so results do not
-// depend on timing.  Each lane handles one column and a run of 32 K per tile
-// chunk (see internal.h for the packed layout).
+// Work split.  The packed weights are 9 KiB units (one 16-column tile x 1024
+// K: eight 1 KiB code chunks and one 1 KiB scale vector; see internal.h).
+// Every wavefront owns exactly one unit: it issues the unit's nine 16-byte
+// loads per lane at once, then widens and contracts the eight chunks.  A
+// workgroup is CT tiles x S consecutive K spans (nw = CT * S wavefronts);
+// the S partial sums of a tile are added in LDS in span order.  When K has
+// more spans than a workgroup covers, ksplit workgroups share a tile group:
+// each hands its per-tile partial over through the workspace and the last to
+// arrive adds them in split order.  Results never depend on timing.  Few
+// registers per wavefront (one unit) let the chip keep tens of megabytes of
+// weight loads in flight, which is what saturates HBM at these sizes.
 //
-// Two engines:
-//   * VALU (M = 1): v_dot2c_f32_f16 with x shared across each 16-lane row by a
-//     DPP row broadcast (lane 16r + i holds the x pair that every lane of row r
-//     needs at step i), per-16-block sums scaled by the E4M3 scale in fp32, then
-//     the four rows that split a column's K are added with permlane swaps.
-//   * MFMA (M = 1..8): v_mfma_f32_16x16x32_f16 with the x rows zero-padded
-//     to 16 as operand A and the widened weights (E2M1 * E4M3 in fp16, exact)
-//     as operand B.  The 8-row verification tile of the pages (post, on why
-//     the M = 8 row matters) fits in half of the 16-row MFMA tile.
-// The MFMA engine also carries the lm_head epilogue: per-row argmax over fp32
-// logits, ties to the lowest column, merged across workgroups with 64-bit
-// atomicMax on (order-preserving key, inverted column) and finished by the
-// last workgroup to arrive.
+// Two engines (lane l = 16*grp + c handles column c of the tile and the
+// 32-K run 128j + 32grp .. +32 of every chunk j):
+//   * VALU (M = 1): v_dot2c_f32_f16 whose x operand is read through DPP
+//     row_newbcast (lane 16r + i holds the x pair that every lane of row r
+//     needs at step i), each 16-K block's sum scaled by its E4M3 scale in fp32,
+//     the four rows that split a column's K added with lane shuffles.
+//   * MFMA (M = 1..8): v_mfma_f32_16x16x32_f16 with the widened weights
+//     (E2M1 * E4M3 in fp16, exact) as operand B and the x rows, zero-padded to
+//     16, as operand A.  The workgroup's x slice is copied into LDS with
+//     direct-to-LDS loads (no VGPRs) before the weight loads; A fragments are
+//     read from LDS one chunk ahead.  The pages' 8-row verification tile
+//     (post, on why the M = 8 row matters) fills half of the 16-row MFMA tile.
+// The MFMA engine also carries the lm_head epilogue: each workgroup writes,
+// per row, the (fp32 logit, column) of its best column as one ordered 64-bit
+// key; a second, one-workgroup kernel takes the maximum key per row (ties to
+// the lowest column) and writes the indices.
 #include <hip/hip_runtime.h>
 
 #include "common.cuh"
@@ -37,320 +45,424 @@ namespace skinny {
 namespace {
 
 struct Nvfp4Args {
-  const uint8_t* codes;
-  const uint8_t* scales;
+  const uint8_t* units;
   const float* gptr;
   const _Float16* x;
   _Float16* y;
   int M, K, N;
-  int kc, nt, sg;
-  int32_t* idx;
-  unsigned long long* keys;
-  uint32_t* counter;
+  int ku, nt, ksplit, S;     // S: K spans per workgroup
+  float* part;               // [ksplit][nt][kPartFloats] per-tile partials (ksplit > 1)
+  uint32_t* tile_cnt;        // [gridDim.x] arrival counters (ksplit > 1)
+  unsigned long long* cand;  // [gridDim.x][M] argmax candidates (lm_head) or null
 };
 
-// Chunk range [c0, c1) of wavefront w out of nw for kc chunks (balanced).
-__device__ __forceinline__ void wave_range(int kc, int nw, int w, int& c0, int& c1) {
-  c0 = (kc * w) / nw;
-  c1 = (kc * (w + 1)) / nw;
-}
+// Partial layout per (split, tile): 32 lanes x 4 floats (MFMA rows 4grp..+3
+// of column c for lanes 16grp + c), or 16 floats (VALU, one per column).
+constexpr int kPartFloats = 128;
 
-// Scale word (two E4M3 bytes: half 0 in bits 0..7, half 1 in bits 8..15) of
-// chunk kc from the 16-byte scale vector of its group.
-__device__ __forceinline__ uint32_t scale_word(const u32x4& sv, int kc) {
-  const int j = kc & 7;
-  const uint32_t d = (j >> 1) == 0 ? sv.x : (j >> 1) == 1 ? sv.y : (j >> 1) == 2 ? sv.z : sv.w;
-  return (j & 1) ? (d >> 16) : (d & 0xFFFFu);
-}
-
-// ---------------------------------------------------------------------------
-// VALU engine, M = 1.
-// ---------------------------------------------------------------------------
-template <int I>
-__device__ __forceinline__ float dot_step(uint32_t xv, uint32_t wd, float acc) {
-  const f16x2 xx = __builtin_bit_cast(f16x2, row_bcast<I>(xv));
-  return __builtin_amdgcn_fdot2(xx, e2m1x2<(I & 3)>(wd), acc, false);
-}
-
-// 16 codes (4 bytes x 2 dwords) of one 16-K block against the broadcast x.
-template <int B0>
-__device__ __forceinline__ float block_dot(uint32_t xv, uint32_t w0, uint32_t w1) {
-  float p = 0.0f;
-  p = dot_step<B0 + 0>(xv, w0, p);
-  p = dot_step<B0 + 1>(xv, w0, p);
-  p = dot_step<B0 + 2>(xv, w0, p);
-  p = dot_step<B0 + 3>(xv, w0, p);
-  p = dot_step<B0 + 4>(xv, w1, p);
-  p = dot_step<B0 + 5>(xv, w1, p);
-  p = dot_step<B0 + 6>(xv, w1, p);
-  p = dot_step<B0 + 7>(xv, w1, p);
-  return p;
-}
-
-template <int CT, int NW>
-__global__ __launch_bounds__(NW * 64) void nvfp4_valu_m1(Nvfp4Args a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile0 = blockIdx.x * CT;
-  int c0, c1;
-  wave_range(a.kc, NW, wave, c0, c1);
-
-  float acc[CT];
-#pragma unroll
-  for (int t = 0; t < CT; ++t) acc[t] = 0.0f;
-
-  // Tiles past the last one (grid rounding when CT > 1) re-read the last
-  // tile; their results are never stored.
-  const uint8_t* cptr[CT];
-  const uint8_t* sptr[CT];
-#pragma unroll
-  for (int t = 0; t < CT; ++t) {
+// This wavefront's unit and its workgroup's geometry (wave-uniform values).
+struct Plan {
+  int lane, wave, nw, S, tile0, s0, sw;  // sw: spans in this split
+  int t, s;                              // local tile and span of this wavefront's unit
+  bool active;
+  __device__ Plan(const Nvfp4Args& a, int ct) {
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    nw = blockDim.x >> 6;
+    S = a.S;
+    tile0 = blockIdx.x * ct;
+    s0 = blockIdx.y * S;
+    sw = min(S, a.ku - s0);
+    t = wave / S;
+    s = wave % S;
+    active = s < sw;
+  }
+  // Units past the last tile (grid rounding) re-read the last tile; their
+  // results are never stored.
+  __device__ const uint8_t* unit_ptr(const Nvfp4Args& a) const {
     const int tt = min(tile0 + t, a.nt - 1);
-    cptr[t] = a.codes + static_cast<size_t>(tt) * a.kc * kTileBytes + lane * 16;
-    sptr[t] = a.scales + static_cast<size_t>(tt) * a.sg * kTileBytes + lane * 16;
+    return a.units + (static_cast<size_t>(tt) * a.ku + s0 + s) * kUnitBytes + lane * 16;
   }
-  const int kfull = a.K / kChunkK;  // chunks whose 128 K are all valid
+};
 
-  u32x4 sv[CT];
-  int sg_loaded = -1;
-  for (int kc = c0; kc < c1; ++kc) {
-    // x pair (k = 128kc + 2 lane, +1) for this chunk; zero past K.
-    uint32_t xv = 0;
-    if (kc < kfull || kc * kChunkK + 2 * lane < a.K)
-      xv = *reinterpret_cast<const uint32_t*>(a.x + kc * kChunkK + 2 * lane);
-    if ((kc >> 3) != sg_loaded) {
-      sg_loaded = kc >> 3;
-#pragma unroll
-      for (int t = 0; t < CT; ++t) sv[t] = load16(sptr[t] + (kc >> 3) * kTileBytes);
-    }
-    u32x4 w[CT];
-#pragma unroll
-    for (int t = 0; t < CT; ++t) w[t] = load16(cptr[t] + kc * kTileBytes);
-#pragma unroll
-    for (int t = 0; t < CT; ++t) {
-      const uint32_t sw = scale_word(sv[t], kc);
-      const float s0 = e4m3f<0>(sw), s1 = e4m3f<1>(sw);
-      const float p0 = block_dot<0>(xv, w[t].x, w[t].y);
-      const float p1 = block_dot<8>(xv, w[t].z, w[t].w);
-      acc[t] = __builtin_fmaf(p0, s0, acc[t]);
-      acc[t] = __builtin_fmaf(p1, s1, acc[t]);
-    }
-  }
-
-  __shared__ float red[NW][CT][16];
-#pragma unroll
-  for (int t = 0; t < CT; ++t) {
-    const float v = sum_over_rows(acc[t]);
-    if (lane < 16) red[wave][t][lane] = v;
-  }
-  __syncthreads();
-  if (wave == 0 && lane < 16) {
-    const float g = *a.gptr;
-#pragma unroll
-    for (int t = 0; t < CT; ++t) {
-      float s = red[0][t][lane];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) s += red[w][t][lane];
-      const int n = (tile0 + t) * kTileCols + lane;
-      if (tile0 + t < a.nt && n < a.N) a.y[n] = static_cast<_Float16>(g * s);
-    }
-  }
+__device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// ---------------------------------------------------------------------------
-// MFMA engine, M = 1..8 (and the lm_head argmax epilogue).
-// ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t ordered_key(float v) {
   if (v == 0.0f) v = 0.0f;  // +0 and -0 compare equal
   const uint32_t b = __builtin_bit_cast(uint32_t, v);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-template <int CT, int NW, bool ARGMAX>
-__global__ __launch_bounds__(NW * 64) void nvfp4_mfma(Nvfp4Args a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = lane >> 4, col = lane & 15;
-  const int tile0 = blockIdx.x * CT;
-  int c0, c1;
-  wave_range(a.kc, NW, wave, c0, c1);
-
-  f32x4 acc[CT];
-#pragma unroll
-  for (int t = 0; t < CT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Tiles past the last one (grid rounding when CT > 1) re-read the last
-  // tile; their results are never stored.
-  const uint8_t* cptr[CT];
-  const uint8_t* sptr[CT];
-#pragma unroll
-  for (int t = 0; t < CT; ++t) {
-    const int tt = min(tile0 + t, a.nt - 1);
-    cptr[t] = a.codes + static_cast<size_t>(tt) * a.kc * kTileBytes + lane * 16;
-    sptr[t] = a.scales + static_cast<size_t>(tt) * a.sg * kTileBytes + lane * 16;
+// True in every thread of the last workgroup of this tile group to arrive
+// (always true without a K split).  Partials must have been written with
+// store_shared() by this workgroup before the call.
+__device__ bool last_of_tile_group(const Nvfp4Args& a) {
+  if (a.ksplit == 1) return true;
+  __shared__ int last;
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    last = counter_add(a.tile_cnt + blockIdx.x, 1u) == static_cast<uint32_t>(a.ksplit - 1);
+    if (last) counter_exch(a.tile_cnt + blockIdx.x, 0u);  // every split of this group has arrived
   }
-  // Operand A: lane (row = col, grp) reads x[row][128kc + 32grp + 8j .. +8].
-  const bool xrow = col < a.M;
-  const _Float16* xr = a.x + static_cast<size_t>(xrow ? col : 0) * a.K + grp * 32;
-  const int kfull = a.K / kChunkK;
+  __syncthreads();
+  return last;
+}
 
-  u32x4 sv[CT];
-  int sg_loaded = -1;
-  for (int kc = c0; kc < c1; ++kc) {
-    f16x8 xa[4];
-    const int kb = kc * kChunkK + grp * 32;
+// ---------------------------------------------------------------------------
+// VALU engine, M = 1.
+// ---------------------------------------------------------------------------
+// Sixteen codes (two dwords, one 16-K block) against x pairs broadcast from
+// lanes 0..7 (lo) or 8..15 (hi) of the lane's own 16-lane row.  One asm block
+// widens the codes (v_cvt_scalef32_pk_f16_fp4, byte by byte, low nibble to
+// the low half) into eight scratch registers and runs eight v_dot2c_f32_f16
+// whose first operand is read through DPP row_newbcast, so the broadcast costs
+// no instruction of its own.  Keeping the conversion inside the block stops
+// the compiler from converting a whole unit ahead of use.  The compiler cannot
+// see hazards inside the asm, so the block carries its own wait states: two
+// before the first DPP read (a VALU write of its source may precede the
+// block) and two after the last v_dot2c, whose result a following VALU read
+// would otherwise miss.
+#define SKINNY_BLOCK_DOT(NAME, R0, R1, R2, R3, R4, R5, R6, R7)                                  \
+  __device__ __forceinline__ float NAME(uint32_t xv, uint32_t w0, uint32_t w1) {                \
+    float p = 0.0f;                                                                             \
+    uint32_t t0, t1, t2, t3, t4, t5, t6, t7;                                                    \
+    asm("v_cvt_scalef32_pk_f16_fp4 %1, %9, 1.0\n"                                               \
+        "v_cvt_scalef32_pk_f16_fp4 %2, %9, 1.0 op_sel:[1,0,0]\n"                                \
+        "v_cvt_scalef32_pk_f16_fp4 %3, %9, 1.0 op_sel:[0,1,0]\n"                                \
+        "v_cvt_scalef32_pk_f16_fp4 %4, %9, 1.0 op_sel:[1,1,0]\n"                                \
+        "v_cvt_scalef32_pk_f16_fp4 %5, %10, 1.0\n"                                              \
+        "v_cvt_scalef32_pk_f16_fp4 %6, %10, 1.0 op_sel:[1,0,0]\n"                               \
+        "v_cvt_scalef32_pk_f16_fp4 %7, %10, 1.0 op_sel:[0,1,0]\n"                               \
+        "v_cvt_scalef32_pk_f16_fp4 %8, %10, 1.0 op_sel:[1,1,0]\n"                               \
+        "s_nop 1\n"                                                                             \
+        "v_dot2c_f32_f16_dpp %0, %11, %1 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %11, %2 row_newbcast:" #R1 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %11, %3 row_newbcast:" #R2 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %11, %4 row_newbcast:" #R3 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %11, %5 row_newbcast:" #R4 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %11, %6 row_newbcast:" #R5 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %11, %7 row_newbcast:" #R6 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %11, %8 row_newbcast:" #R7 " row_mask:0xf bank_mask:0xf\n"     \
+        "s_nop 1\n"                                                                             \
+        : "+v"(p), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), \
+          "=&v"(t7)                                                                             \
+        : "v"(w0), "v"(w1), "v"(xv));                                                           \
+    return p;                                                                                   \
+  }
+SKINNY_BLOCK_DOT(block_dot_lo, 0, 1, 2, 3, 4, 5, 6, 7)
+SKINNY_BLOCK_DOT(block_dot_hi, 8, 9, 10, 11, 12, 13, 14, 15)
+#undef SKINNY_BLOCK_DOT
+
+template <int CT>
+__global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu_m1(Nvfp4Args a) {
+  __shared__ float red[kMaxWaves][16];
+  const Plan P(a, CT);
+  float acc = 0.0f;
+  if (P.active) {
+    // The whole unit plus this lane's x pair of each chunk (k = 1024g + 128j + 2*lane).
+    const uint8_t* p = P.unit_ptr(a);
+    const u32x4 sv = load16(p + kChunksPerUnit * kChunkBytes);
+    u32x4 c[kChunksPerUnit];
+    uint32_t xv[kChunksPerUnit];
+    const int kx = (P.s0 + P.s) * kUnitK + 2 * P.lane;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xa[j] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (xrow && (kc < kfull || kb + 8 * j + 8 <= a.K))
-        xa[j] = *reinterpret_cast<const f16x8*>(xr + kc * kChunkK + 8 * j);
+    for (int j = 0; j < kChunksPerUnit; ++j) {
+      c[j] = load16(p + j * kChunkBytes);
+      const int k = kx + j * kChunkK;
+      xv[j] = k < a.K ? *reinterpret_cast<const uint32_t*>(a.x + k) : 0u;
     }
-    if ((kc >> 3) != sg_loaded) {
-      sg_loaded = kc >> 3;
 #pragma unroll
-      for (int t = 0; t < CT; ++t) sv[t] = load16(sptr[t] + (kc >> 3) * kTileBytes);
-    }
-    u32x4 w[CT];
-#pragma unroll
-    for (int t = 0; t < CT; ++t) w[t] = load16(cptr[t] + kc * kTileBytes);
-#pragma unroll
-    for (int t = 0; t < CT; ++t) {
-      const f16x2 s = e4m3x2<false>(scale_word(sv[t], kc));
-      const f16x8 s0 = f16x8{s.x, s.x, s.x, s.x, s.x, s.x, s.x, s.x};
-      const f16x8 s1 = f16x8{s.y, s.y, s.y, s.y, s.y, s.y, s.y, s.y};
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], e2m1x8(w[t].x) * s0, acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], e2m1x8(w[t].y) * s0, acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], e2m1x8(w[t].z) * s1, acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], e2m1x8(w[t].w) * s1, acc[t], 0, 0, 0);
+    for (int j = 0; j < kChunksPerUnit; ++j) {
+      const uint32_t sd = dword(sv, j >> 1);
+      const float s0 = (j & 1) ? e4m3f<2>(sd) : e4m3f<0>(sd);
+      const float s1 = (j & 1) ? e4m3f<3>(sd) : e4m3f<1>(sd);
+      acc = __builtin_fmaf(block_dot_lo(xv[j], c[j].x, c[j].y), s0, acc);
+      acc = __builtin_fmaf(block_dot_hi(xv[j], c[j].z, c[j].w), s1, acc);
     }
   }
+  acc = sum_over_rows(acc);
+  if (P.lane < 16) red[P.wave][P.lane] = acc;
+  __syncthreads();
 
-  // D layout: lane (grp, col) holds rows 4grp..4grp+3 of column col.  Rows
-  // >= 8 are padding, so only lanes 0..31 carry results.
-  __shared__ f32x4 red[NW][CT][32];
-  if (lane < 32) {
+  // Wavefront t < CT finishes local tile t: its spans in order, then either
+  // the store or the hand-off of the partial.
+  const bool fin = P.wave < CT && P.lane < 16 && P.tile0 + P.wave < a.nt;
+  float tot = 0.0f;
+  if (fin) {
+    for (int s = 0; s < P.sw; ++s) tot += red[P.wave * P.S + s][P.lane];
+    if (a.ksplit > 1)
+      store_shared(a.part + (static_cast<size_t>(blockIdx.y) * a.nt + P.tile0 + P.wave) * kPartFloats + P.lane, tot);
+  }
+  if (!last_of_tile_group(a)) return;
+  if (fin) {
+    if (a.ksplit > 1) {
+      tot = 0.0f;
+      for (int ks = 0; ks < a.ksplit; ++ks)
+        tot += load_shared(a.part + (static_cast<size_t>(ks) * a.nt + P.tile0 + P.wave) * kPartFloats + P.lane);
+    }
+    const int n = (P.tile0 + P.wave) * kTileCols + P.lane;
+    if (n < a.N) a.y[n] = static_cast<_Float16>(*a.gptr * tot);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA engine, M = 1..8 (and the lm_head argmax candidates).
+// ---------------------------------------------------------------------------
+// LDS copy of x for this workgroup's K spans: rows 0..M-1, row stride
+// RS = S*1024 + 8 halves (the pad spreads the rows over LDS banks).
+__device__ __forceinline__ int xs_stride(int S) { return S * kUnitK + 8; }
+
+// Copy x[m][1024*s0 .. 1024*(s0+S)) for m < M into LDS with direct-to-LDS
+// loads: each wavefront instruction moves one contiguous KiB (64 lanes x 16
+// bytes) of one row.  Parts past K are not loaded (those weights are zero);
+// that part of the copy is zero-filled with plain stores instead.
+__device__ void stage_x(const Nvfp4Args& a, const Plan& P, _Float16* xs) {
+  const int RS = xs_stride(P.S);
+  const int kbase = P.s0 * kUnitK;
+  const int blocks_per_row = P.S * 2;  // 1 KiB blocks = 512 halves
+  const int kvalid = a.K - kbase;      // halves of each row that exist
+  if (kvalid < P.S * kUnitK) {
+    for (int i = threadIdx.x; i < a.M * RS; i += blockDim.x)
+      if (i % RS >= kvalid) xs[i] = static_cast<_Float16>(0.0f);
+  }
+  const int nblocks = a.M * blocks_per_row;
+  for (int b = P.wave; b < nblocks; b += P.nw) {
+    const int m = b / blocks_per_row, blk = b % blocks_per_row;
+    const int col = blk * 512 + P.lane * 8;
+    if (col < kvalid)
+      __builtin_amdgcn_global_load_lds(a.x + static_cast<size_t>(m) * a.K + kbase + col, xs + m * RS + blk * 512,
+                                       16, 0, 0);
+  }
+}
+
+// Operand A fragments of chunk j: lane (row m = c, grp) holds
+// x[m][1024s + 128j + 32grp + 8i .. +8] for MFMA i = 0..3; zero for m >= M.
+__device__ __forceinline__ void read_x_frag(f16x8 (&xa)[4], const _Float16* xrow, bool row, int j) {
+  if (row) {
 #pragma unroll
-    for (int t = 0; t < CT; ++t) red[wave][t][lane] = acc[t];
+    for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const f16x8*>(xrow + j * kChunkK + 8 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xa[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+template <int J>
+__device__ __forceinline__ f32x4 mfma_chunk(const u32x4& cj, const u32x4& sv, const f16x8 (&xa)[4], f32x4 acc) {
+  const f16x2 s = e4m3x2<(J & 1) != 0>(dword(sv, J >> 1));
+  const f16x8 s0 = f16x8{s.x, s.x, s.x, s.x, s.x, s.x, s.x, s.x};
+  const f16x8 s1 = f16x8{s.y, s.y, s.y, s.y, s.y, s.y, s.y, s.y};
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], e2m1x8(cj.x) * s0, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], e2m1x8(cj.y) * s0, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], e2m1x8(cj.z) * s1, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], e2m1x8(cj.w) * s1, acc, 0, 0, 0);
+  return acc;
+}
+
+template <int J>
+__device__ __forceinline__ void mfma_steps(const u32x4 (&c)[kChunksPerUnit], const u32x4& sv, f16x8 (&x0)[4],
+                                           f16x8 (&x1)[4], f32x4& acc, const _Float16* xrow, bool row) {
+  if constexpr (J < kChunksPerUnit) {
+    f16x8 (&cur)[4] = (J & 1) ? x1 : x0;
+    f16x8 (&nxt)[4] = (J & 1) ? x0 : x1;
+    if constexpr (J + 1 < kChunksPerUnit) read_x_frag(nxt, xrow, row, J + 1);
+    acc = mfma_chunk<J>(c[J], sv, cur, acc);
+    mfma_steps<J + 1>(c, sv, x0, x1, acc, xrow, row);
+  }
+}
+
+template <int CT, bool ARGMAX>
+__global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const Plan P(a, CT);
+  _Float16* xs = reinterpret_cast<_Float16*>(lds);
+  f32x4* red = reinterpret_cast<f32x4*>(lds + ((a.M * xs_stride(P.S) * 2 + 15) & ~15));  // [nw][32]
+
+  // x first (the vector-memory counter completes in order), then the unit.
+  stage_x(a, P, xs);
+  u32x4 c[kChunksPerUnit], sv = u32x4{0u, 0u, 0u, 0u};
+  if (P.active) {
+    const uint8_t* p = P.unit_ptr(a);
+    sv = load16(p + kChunksPerUnit * kChunkBytes);
+#pragma unroll
+    for (int j = 0; j < kChunksPerUnit; ++j) c[j] = load16(p + j * kChunkBytes);
   }
   __syncthreads();
 
-  if (wave == 0) {
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (P.active) {
+    const int cl = P.lane & 15, grp = P.lane >> 4;
+    const bool row = cl < a.M;
+    const _Float16* xrow = xs + (row ? cl : 0) * xs_stride(P.S) + P.s * kUnitK + grp * 32;
+    f16x8 x0[4], x1[4];
+    read_x_frag(x0, xrow, row, 0);
+    mfma_steps<0>(c, sv, x0, x1, acc, xrow, row);
+  }
+  if (P.lane < 32) red[P.wave * 32 + P.lane] = acc;
+  __syncthreads();
+
+  // Wavefront t < CT finishes local tile t.  D layout: lane (grp, c) holds
+  // rows 4grp..4grp+3 of column c; rows >= 8 are padding.
+  const bool fin = P.wave < CT && P.tile0 + P.wave < a.nt;
+  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (fin && P.lane < 32) {
+    for (int s = 0; s < P.sw; ++s) tot += red[(P.wave * P.S + s) * 32 + P.lane];
+    if (a.ksplit > 1) {
+      float* dst = a.part + (static_cast<size_t>(blockIdx.y) * a.nt + P.tile0 + P.wave) * kPartFloats + 4 * P.lane;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_shared(dst + i, tot[i]);
+    }
+  }
+  if (!last_of_tile_group(a)) return;
+
+  __shared__ unsigned long long best[kMaxWaves][kMaxRows];
+  if (fin) {
+    const int cl = P.lane & 15, grp = P.lane >> 4;
+    if (a.ksplit > 1 && P.lane < 32) {
+      tot = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < a.ksplit; ++ks) {
+        const float* src = a.part + (static_cast<size_t>(ks) * a.nt + P.tile0 + P.wave) * kPartFloats + 4 * P.lane;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[i] += load_shared(src + i);
+      }
+    }
     const float g = *a.gptr;
-    float best_v[4];
-    int best_n[4];
+    const int n = (P.tile0 + P.wave) * kTileCols + cl;
+    unsigned long long key[4] = {0ull, 0ull, 0ull, 0ull};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) { best_v[r] = -__builtin_inff(); best_n[r] = 0x7fffffff; }
-    if (lane < 32) {
-#pragma unroll
-      for (int t = 0; t < CT; ++t) {
-        f32x4 s = red[0][t][lane];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) s += red[w][t][lane];
-        const int n = (tile0 + t) * kTileCols + col;
-        const bool nok = (tile0 + t) < a.nt && n < a.N;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = grp * 4 + r;
-          const float v = g * s[r];
-          if (nok && m < a.M) {
-            if (a.y) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(v);
-            if (ARGMAX && (v > best_v[r] || best_n[r] == 0x7fffffff)) { best_v[r] = v; best_n[r] = n; }
-          }
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int m = grp * 4 + i;
+      const float v = g * tot[i];
+      if (P.lane < 32 && n < a.N && m < a.M) {
+        if (a.y) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(v);
+        key[i] = (static_cast<unsigned long long>(ordered_key(v)) << 32) |
+                 static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(n));
       }
     }
     if (ARGMAX) {
-      // Reduce (value, column) over the 16 lanes of each row group; ties keep
-      // the lower column.  Columns grow with t for a fixed lane, so the strict
-      // '>' above already kept the lowest column within a lane.
+      // Largest key over the 16 columns of each row group (the larger key has
+      // the larger logit, or the same logit and the lower column).
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) {
-          const float ov = __shfl_xor(best_v[r], off, 16);
-          const int on = __shfl_xor(best_n[r], off, 16);
-          if (ov > best_v[r] || (ov == best_v[r] && on < best_n[r])) { best_v[r] = ov; best_n[r] = on; }
+          const unsigned long long o = __shfl_xor(key[i], off, 16);
+          key[i] = o > key[i] ? o : key[i];
         }
       }
-      if (lane < 32 && col == 0) {
+      if (P.lane < 32 && cl == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = grp * 4 + r;
-          if (m < a.M && best_n[r] != 0x7fffffff) {
-            const unsigned long long key =
-                (static_cast<unsigned long long>(ordered_key(best_v[r])) << 32) |
-                static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(best_n[r]));
-            atomicMax(a.keys + m, key);
-          }
-        }
+        for (int i = 0; i < 4; ++i) best[P.wave][grp * 4 + i] = key[i];
       }
     }
   }
   if (ARGMAX) {
-    __shared__ int last;
-    __threadfence();
     __syncthreads();
-    if (threadIdx.x == 0) last = (atomicAdd(a.counter, 1u) == gridDim.x - 1);
-    __syncthreads();
-    if (last) {
-      __threadfence();
-      if (threadIdx.x < a.M) {
-        const unsigned long long key = atomicExch(a.keys + threadIdx.x, 0ull);
-        a.idx[threadIdx.x] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFull));
-      }
-      if (threadIdx.x == 0) atomicExch(a.counter, 0u);
+    // One candidate per row for the whole workgroup (a zero key loses to any real one).
+    if (threadIdx.x < static_cast<unsigned>(a.M)) {
+      unsigned long long k = 0ull;
+      for (int t = 0; t < CT; ++t)
+        if (P.tile0 + t < a.nt) k = best[t][threadIdx.x] > k ? best[t][threadIdx.x] : k;
+      a.cand[static_cast<size_t>(blockIdx.x) * a.M + threadIdx.x] = k;
     }
   }
 }
 
+// Reduces the per-workgroup candidates: idx[m] = column of the largest key.
+__global__ __launch_bounds__(256) void argmax_reduce(const unsigned long long* cand, int groups, int M,
+                                                     int32_t* idx) {
+  __shared__ unsigned long long red[256];
+  for (int m = 0; m < M; ++m) {
+    unsigned long long k = 0ull;
+    for (int g = threadIdx.x; g < groups; g += blockDim.x) {
+      const unsigned long long v = cand[static_cast<size_t>(g) * M + m];
+      k = v > k ? v : k;
+    }
+    red[threadIdx.x] = k;
+    __syncthreads();
+    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
+      if (threadIdx.x < static_cast<unsigned>(off))
+        red[threadIdx.x] = red[threadIdx.x + off] > red[threadIdx.x] ? red[threadIdx.x + off] : red[threadIdx.x];
+      __syncthreads();
+    }
+    // No candidate at all (every logit NaN) leaves the all-ones index -1.
+    if (threadIdx.x == 0) idx[m] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(red[0] & 0xFFFFFFFFull));
+    __syncthreads();
+  }
+}
+
 template <typename Kern>
-hipError_t launch(Kern k, int grid, int block, const Nvfp4Args& a, hipStream_t stream) {
-  hipLaunchKernelGGL(k, dim3(grid), dim3(block), 0, stream, a);
+hipError_t launch(Kern k, dim3 grid, int nw, size_t lds, const Nvfp4Args& a, hipStream_t stream) {
+  hipLaunchKernelGGL(k, grid, dim3(nw * 64), lds, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool nvfp4_cfg_supported(const LaunchCfg& c, int M, bool argmax) {
-  const bool ct_ok = c.ct == 1 || c.ct == 2 || c.ct == 4;
-  const bool nw_ok = c.nw == 4 || c.nw == 8;
-  if (!ct_ok || !nw_ok) return false;
-  if (c.engine == 0) return M == 1 && !argmax;
-  return c.engine == 1;
+size_t nvfp4_mfma_lds_bytes(int M, int S, int nw) {
+  return ((static_cast<size_t>(M) * (S * kUnitK + 8) * 2 + 15) & ~static_cast<size_t>(15)) +
+         static_cast<size_t>(nw) * 32 * sizeof(f32x4);
 }
 
-#define SKINNY_NVFP4_DISPATCH(CT, NW)                                                         \
-  if (cfg.ct == CT && cfg.nw == NW) {                                                         \
-    if (cfg.engine == 0) return launch(nvfp4_valu_m1<CT, NW>, grid, NW * 64, a, stream);     \
-    if (argmax) return launch(nvfp4_mfma<CT, NW, true>, grid, NW * 64, a, stream);           \
-    return launch(nvfp4_mfma<CT, NW, false>, grid, NW * 64, a, stream);                      \
+size_t nvfp4_part_floats() { return kPartFloats; }
+
+// (engine, ct, nw, ksplit): nw = ct * S wavefronts cover S K spans of ct
+// tiles; the ksplit workgroups of a tile group must cover all K spans and
+// each must get at least one.
+bool nvfp4_cfg_supported(const LaunchCfg& c, int M, int K, bool argmax) {
+  const bool ct_ok = c.ct == 1 || c.ct == 2 || c.ct == 4 || c.ct == 8;
+  if (!ct_ok || c.nw < 1 || c.nw > kMaxWaves || c.nw % c.ct != 0 || c.ksplit < 1) return false;
+  const int ku = (K + kUnitK - 1) / kUnitK;
+  const int S = c.nw / c.ct;
+  if (static_cast<long>(c.ksplit) * S < ku || static_cast<long>(c.ksplit - 1) * S >= ku) return false;
+  if (c.engine == 0) return M == 1 && !argmax;
+  if (c.engine != 1) return false;
+  return nvfp4_mfma_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
+}
+
+#define SKINNY_NVFP4_DISPATCH(CT)                                                                 \
+  if (cfg.ct == CT) {                                                                             \
+    if (cfg.engine == 0) return launch(nvfp4_valu_m1<CT>, grid, cfg.nw, 0, a, stream);           \
+    if (argmax) {                                                                                 \
+      hipError_t e = launch(nvfp4_mfma<CT, true>, grid, cfg.nw, lds, a, stream);                  \
+      if (e != hipSuccess) return e;                                                              \
+      hipLaunchKernelGGL(argmax_reduce, dim3(1), dim3(256), 0, stream, a.cand,                    \
+                         static_cast<int>(grid.x), M, idx);                                       \
+      return hipGetLastError();                                                                   \
+    }                                                                                             \
+    return launch(nvfp4_mfma<CT, false>, grid, cfg.nw, lds, a, stream);                          \
   }
 
 hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y, int M, int K, int N,
                         const LaunchCfg& cfg, int32_t* idx, void* workspace, hipStream_t stream) {
   const Geometry geo = nvfp4_geometry(K, N);
+  const WorkspaceLayout wl = nvfp4_workspace_layout(cfg, M, K, N, idx != nullptr);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   Nvfp4Args a;
-  a.codes = blob + kHeaderBytes;
-  a.scales = blob + kHeaderBytes + geo.codes_bytes;
+  a.units = blob + kHeaderBytes;
   a.gptr = reinterpret_cast<const float*>(blob + kGOffset);
   a.x = reinterpret_cast<const _Float16*>(x);
   a.y = reinterpret_cast<_Float16*>(y);
   a.M = M;
   a.K = K;
   a.N = N;
-  a.kc = geo.kc;
+  a.ku = geo.ku;
   a.nt = geo.nt;
-  a.sg = geo.sg;
-  a.idx = idx;
-  a.keys = reinterpret_cast<unsigned long long*>(workspace);
-  a.counter = workspace ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + 8 * kMaxRows)
-                        : nullptr;
+  a.ksplit = cfg.ksplit;
+  a.S = cfg.nw / cfg.ct;
+  a.part = wl.part_bytes ? reinterpret_cast<float*>(ws + wl.part_off) : nullptr;
+  a.tile_cnt = wl.tile_cnt_bytes ? reinterpret_cast<uint32_t*>(ws + wl.tile_cnt_off) : nullptr;
+  a.cand = idx ? reinterpret_cast<unsigned long long*>(ws + wl.keys_off) : nullptr;
   const bool argmax = idx != nullptr;
-  const int grid = (geo.nt + cfg.ct - 1) / cfg.ct;
-  SKINNY_NVFP4_DISPATCH(1, 4)
-  SKINNY_NVFP4_DISPATCH(1, 8)
-  SKINNY_NVFP4_DISPATCH(2, 4)
-  SKINNY_NVFP4_DISPATCH(2, 8)
-  SKINNY_NVFP4_DISPATCH(4, 4)
-  SKINNY_NVFP4_DISPATCH(4, 8)
+  const dim3 grid((geo.nt + cfg.ct - 1) / cfg.ct, cfg.ksplit);
+  const size_t lds = nvfp4_mfma_lds_bytes(M, a.S, cfg.nw);
+  SKINNY_NVFP4_DISPATCH(1)
+  SKINNY_NVFP4_DISPATCH(2)
+  SKINNY_NVFP4_DISPATCH(4)
+  SKINNY_NVFP4_DISPATCH(8)
   return hipErrorInvalidValue;
 }
 

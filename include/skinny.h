@@ -89,8 +89,9 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float g,
  *   y         : device, fp16 [M][N] row-major (written, never read).
  *   M         : 1..8.
  *   workspace : device buffer of at least skinny_workspace_bytes(0, M, K, N)
- *               bytes, zero-filled before its first use; each call leaves it
- *               zero-filled again.  May be NULL when that size is 0.
+ *               bytes, zero-filled before its first use; every call leaves
+ *               its counters zero again.  May be NULL when that size is 0.
+ *               Calls that share one workspace must not overlap in time.
  *   stream    : HIP stream the kernel is enqueued on (0 = null stream).
  * ------------------------------------------------------------------------- */
 int nvfp4_gemm(const void* w_packed, const uint16_t* x, uint16_t* y,
@@ -155,22 +156,32 @@ int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales);
  * library's pick (same arguments and results, used to compare kernels):
  *   engine : 0 = VALU dot2 engine (nvfp4_gemm with M == 1 only),
  *            1 = MFMA 16x16x32 f16 engine (all calls, M = 1..8)
- *   ct     : 16-column tiles per workgroup: 1, 2 or 4
- *   nw     : wavefronts per workgroup, which split K: 4 or 8
- * A combination that is not built returns SKINNY_EINVAL.
+ *   ct     : 16-column tiles per workgroup: 1, 2, 4 or 8
+ *   nw     : wavefronts per workgroup, which split its work: 1..8
+ *   ksplit : workgroups that split K (1 = none); partial sums then go
+ *            through the workspace, whose size skinny_workspace_bytes_config
+ *            gives for the same choice
+ * A combination that is not built (or whose LDS need exceeds the CU)
+ * returns SKINNY_EINVAL.
  * ------------------------------------------------------------------------- */
 int nvfp4_gemm_config(const void* w_packed, const uint16_t* x, uint16_t* y,
                       int M, int K, int N, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, int engine,
-                      int ct, int nw);
+                      int ct, int nw, int ksplit);
 int fp8_gemm_config(const uint8_t* w, const float* block_scales,
                     const uint16_t* x, uint16_t* y, int M, int K, int N,
                     void* workspace, size_t workspace_bytes, hipStream_t stream,
-                    int engine, int ct, int nw);
+                    int engine, int ct, int nw, int ksplit);
 int lm_head_gemm_argmax_config(const void* w_packed, const uint16_t* x,
                                int32_t* idx, uint16_t* logits, int M, int K,
                                int N, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream, int engine, int ct, int nw);
+                               hipStream_t stream, int engine, int ct, int nw,
+                               int ksplit);
+
+/* Workspace bytes of a call made with an explicit kernel choice (op as
+ * below); 0 for an unsupported choice or when none is needed. */
+size_t skinny_workspace_bytes_config(int op, int M, int K, int N, int engine,
+                                     int ct, int nw, int ksplit);
 
 /* Workspace bytes a call needs. op: 0 = nvfp4_gemm, 1 = fp8_gemm,
  * 2 = lm_head_gemm_argmax.  Returns 0 for an unsupported op or shape. */

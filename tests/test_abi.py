@@ -62,13 +62,25 @@ def test_nvfp4_gemm_argument_errors():
 
 def test_explicit_config_rejections():
     L = lib()
-    # VALU engine is M = 1 only; unknown engine / tile counts / wave counts are rejected.
-    assert L.nvfp4_gemm_config(A, A, A, 2, 256, 512, None, 0, None, 0, 1, 4) == sk.EINVAL
-    assert L.nvfp4_gemm_config(A, A, A, 1, 256, 512, None, 0, None, 2, 1, 4) == sk.EINVAL
-    assert L.nvfp4_gemm_config(A, A, A, 1, 256, 512, None, 0, None, 1, 3, 4) == sk.EINVAL
-    assert L.nvfp4_gemm_config(A, A, A, 1, 256, 512, None, 0, None, 1, 1, 5) == sk.EINVAL
-    assert L.fp8_gemm_config(A, A, A, A, 1, 256, 512, None, 0, None, 0, 1, 4) == sk.EINVAL
-    assert L.lm_head_gemm_argmax_config(A, A, A, None, 1, 256, 512, A, 256, None, 0, 1, 4) == sk.EINVAL
+    cfg = lambda *c: L.nvfp4_gemm_config(A, A, A, c[0], 256, 512, None, 0, None, *c[1:])
+    # VALU engine is M = 1 only; unknown engine / tile counts / wave counts / splits are rejected.
+    assert cfg(2, 0, 1, 4, 1) == sk.EINVAL
+    assert cfg(1, 2, 1, 4, 1) == sk.EINVAL
+    assert cfg(1, 1, 3, 4, 1) == sk.EINVAL
+    assert cfg(1, 1, 1, 17, 1) == sk.EINVAL         # at most 16 wavefronts
+    assert cfg(1, 1, 2, 3, 1) == sk.EINVAL          # nw must be a multiple of ct
+    assert cfg(1, 1, 1, 0, 1) == sk.EINVAL
+    assert cfg(1, 1, 1, 4, 0) == sk.EINVAL
+    assert cfg(1, 1, 1, 4, 2) == sk.EINVAL          # K = 256 has one K span: no split possible
+    assert L.fp8_gemm_config(A, A, A, A, 1, 256, 512, None, 0, None, 0, 1, 4, 1) == sk.EINVAL
+    assert L.lm_head_gemm_argmax_config(A, A, A, None, 1, 256, 512, A, 256, None, 0, 1, 4, 1) == sk.EINVAL
+    # a K split needs its workspace
+    big = lambda ws, wsb: L.nvfp4_gemm_config(A, A, A, 8, 17408, 5120, ws, wsb, None, 1, 1, 4, 5)
+    need = sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 1, 4, 5))
+    assert need >= 5 * 320 * 512
+    assert big(None, 0) == sk.EINVAL
+    assert big(A, need - 1) == sk.ESIZE
+    assert big(MIS, need) == sk.EALIGN
 
 
 def test_fp8_gemm_argument_errors():
@@ -82,7 +94,7 @@ def test_fp8_gemm_argument_errors():
 
 def test_lm_head_argument_errors():
     L = lib()
-    need = sk.workspace_bytes(sk.OP_LM_HEAD, 8, 5120, 151936)
+    need = sk.workspace_bytes(sk.OP_LM_HEAD, 1, 256, 512)
     assert need >= 8 * 8 + 4
     f = lambda **k: L.lm_head_gemm_argmax(k.get("w", A), k.get("x", A), k.get("idx", A), k.get("lg", None),
                                           k.get("M", 1), 256, 512, k.get("ws", A), k.get("wsb", need), None)
@@ -96,10 +108,23 @@ def test_lm_head_argument_errors():
 
 
 def test_workspace_sizes():
-    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 5120, 34816) == 0
-    assert sk.workspace_bytes(sk.OP_FP8, 4, 5120, 7168) == 0
-    assert sk.workspace_bytes(sk.OP_LM_HEAD, 0, 5120, 7168) == 0      # bad shape
+    # no split, no argmax: no workspace
+    assert sk.workspace_bytes(sk.OP_NVFP4, 1, 5120, 17408, (0, 1, 5, 1)) == 0
+    assert sk.workspace_bytes(sk.OP_FP8, 4, 5120, 7168, (1, 1, 10, 1)) == 0
+    # argmax: one 64-bit candidate per workgroup and row
+    assert sk.workspace_bytes(sk.OP_LM_HEAD, 8, 5120, 151936, (1, 1, 5, 1)) >= 9496 * 8 * 8
+    # K split: partials of every split and tile plus one counter per tile group
+    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 2, 10, 4)) >= 4 * 320 * 512 + 160 * 4
+    # spans that do not cover K, or a split that leaves a workgroup without spans, are unsupported
+    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 2, 4, 4)) == 0
+    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 1, 9, 2)) > 0
+    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 1, 9, 3)) == 0
+    # the MFMA engine's LDS copy of x must fit: 8 rows x 16 spans do not
+    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 1, 16, 2)) == 0
+    # defaults are consistent with some explicit choice and zero for bad shapes or ops
+    assert sk.workspace_bytes(sk.OP_LM_HEAD, 0, 5120, 7168) == 0
     assert sk.workspace_bytes(7, 1, 5120, 7168) == 0
+    assert sk.workspace_bytes(sk.OP_NVFP4, 1, 5120, 17408, (1, 3, 4, 1)) == 0      # bad ct -> unsupported
 
 
 # ------------------------------------------------------------------- packer
@@ -110,18 +135,23 @@ def _pack_raw(codes, scales, g, K, N, out, size):
     return st, sz.value
 
 
+def _geom(K, N):
+    ku, nt = -(-K // 1024), -(-N // 16)
+    return ku, nt
+
+
 def test_pack_size_and_header():
-    for K, N in [(256, 512), (272, 100), (5120, 17408), (16, 1)]:
-        kc, nt = -(-K // 128), -(-N // 16)
-        sg = -(-kc // 8)
-        assert sk.packed_bytes(K, N) == 256 + nt * kc * 1024 + nt * sg * 1024
+    for K, N in [(256, 512), (272, 100), (5120, 17408), (16, 1), (17408, 5120)]:
+        ku, nt = _geom(K, N)
+        assert sk.packed_bytes(K, N) == 256 + nt * ku * 9216
     codes = np.zeros((100, 136), np.uint8)
     scales = np.zeros((100, 17), np.uint8)
     blob = sk.nvfp4_pack(codes, scales, 0.125, 272, 100)
     h = blob[:64]
     assert bytes(h[:4]) == b"SKN4"
-    assert list(h[4:28].view(np.uint32)) == [1, 272, 100, 3, 7, 1]
+    assert list(h[4:28].view(np.uint32)) == [2, 272, 100, 1, 7, 9216]
     assert h[28:32].view(np.float32)[0] == np.float32(0.125)
+    assert list(h[32:48].view(np.uint64)) == [256, 7 * 9216]
 
 
 def test_pack_errors():
@@ -140,34 +170,47 @@ def test_pack_errors():
         assert _pack_raw(c, s2, 1.0, 256, 4, out, out.size)[0] == sk.EFORMAT
 
 
-@pytest.mark.parametrize("K,N", [(256, 32), (272, 20), (1040, 17)])
+@pytest.mark.parametrize("K,N", [(256, 32), (272, 20), (2064, 17)])
 def test_pack_places_every_byte_once(K, N):
-    """Distinct byte patterns go exactly where the documented layout says."""
+    """Distinct byte patterns go exactly where the documented unit layout says."""
     rng = np.random.default_rng(K + N)
     codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     scales = rng.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8)   # no NaN codes
     blob = sk.nvfp4_pack(codes, scales, 1.0, K, N)
-    kc, nt = -(-K // 128), -(-N // 16)
-    sg = -(-kc // 8)
-    ctiles = blob[256:256 + nt * kc * 1024].reshape(nt, kc, 4, 16, 16)     # tile, chunk, grp, col, byte
-    stiles = blob[256 + nt * kc * 1024:].reshape(nt, sg, 4, 16, 8, 2)      # tile, group, grp, col, chunk, half
-    seen_c = np.zeros_like(codes, dtype=np.int64)
+    ku, nt = _geom(K, N)
+    units = blob[256:].reshape(nt, ku, 9, 4, 16, 16)     # tile, span, chunk(8)+scales, grp, col, byte
+    seen_c = np.zeros(codes.shape, np.int64)
+    seen_s = np.zeros(scales.shape, np.int64)
     for n in range(N):
         t, c = divmod(n, 16)
         for k in range(0, K, 2):
-            kcc, r = divmod(k, 128)
+            g, r = divmod(k, 1024)
+            j, r = divmod(r, 128)
             grp, i = divmod(r, 32)
-            assert ctiles[t, kcc, grp, c, i // 2] == codes[n, k // 2]
+            assert units[t, g, j, grp, c, i // 2] == codes[n, k // 2]
             seen_c[n, k // 2] += 1
         for b in range(K // 16):
-            k = 16 * b
-            kcc, r = divmod(k, 128)
-            grp, rr = divmod(r, 32)
-            assert stiles[t, kcc // 8, grp, c, kcc % 8, rr // 16] == scales[n, b]
-    assert (seen_c == 1).all()
-    # padding (columns >= N, K >= real K) is zero
-    pad_cols = np.arange(nt * 16) >= N
-    assert not ctiles[:, :, :, :, :].reshape(nt, kc, 4, 16, 16).transpose(0, 3, 1, 2, 4).reshape(nt * 16, -1)[pad_cols].any()
+            g, r = divmod(16 * b, 1024)
+            j, r = divmod(r, 128)
+            grp, h = divmod(r, 32)
+            assert units[t, g, 8, grp, c, 2 * j + h // 16] == scales[n, b]
+            seen_s[n, b] += 1
+    assert (seen_c == 1).all() and (seen_s == 1).all()
+    # every byte of the padding (columns >= N, K >= real K) is zero
+    mask = np.zeros(units.shape, bool)
+    for n in range(N):
+        t, c = divmod(n, 16)
+        for k in range(0, K, 2):
+            g, r = divmod(k, 1024)
+            j, r = divmod(r, 128)
+            grp, i = divmod(r, 32)
+            mask[t, g, j, grp, c, i // 2] = True
+        for b in range(K // 16):
+            g, r = divmod(16 * b, 1024)
+            j, r = divmod(r, 128)
+            grp, h = divmod(r, 32)
+            mask[t, g, 8, grp, c, 2 * j + h // 16] = True
+    assert not units[~mask].any()
 
 
 def test_pack_is_deterministic():

@@ -24,9 +24,26 @@ pytestmark = pytest.mark.gpu
 
 REL_FROB = 2e-3
 ROW_MAX = 1e-2
-CT_NW = list(itertools.product((1, 2, 4), (4, 8)))
-NVFP4_CFGS = [(1, ct, nw) for ct, nw in CT_NW]          # MFMA engine, any M
-VALU_CFGS = [(0, ct, nw) for ct, nw in CT_NW]           # VALU engine, M = 1
+def cfgs(engine, K, unit_k=1024, splits=(1, 2, 3), cts=(1, 2, 4, 8)):
+    """(engine, ct, nw, ksplit) choices valid for this K.
+
+    A workgroup covers S = nw / ct K units of ct tiles; ksplit workgroups must
+    cover all ku units of K and each must get some.  Besides the tight S, one
+    more span than needed is tried too (it leaves idle wavefronts)."""
+    ku = -(-K // unit_k)
+    out = []
+    for ct in cts:
+        for ks in splits:
+            S = -(-ku // ks)
+            for s in (S, S + 1):
+                if ks * s >= ku and (ks - 1) * s < ku and ct * s <= 16:
+                    out.append((engine, ct, ct * s, ks))
+    return sorted(set(out))
+
+
+def ws_for(op, M, K, N, config):
+    n = sk.workspace_bytes(op, M, K, N, config)
+    return torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None
 
 
 def dev(a):
@@ -46,7 +63,7 @@ def run_nvfp4(case, M=None, config=None, guard=0):
     x = dev(case["x"][:M])
     buf = torch.full((M * N + 2 * guard,), float("nan"), dtype=torch.float16, device="cuda")
     y = buf[guard:guard + M * N].view(M, N)
-    sk.nvfp4_gemm(blob, x, y, config=config)
+    sk.nvfp4_gemm(blob, x, y, config=config, workspace=ws_for(sk.OP_NVFP4, M, K, N, config))
     torch.cuda.synchronize()
     if guard:
         assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + M * N:]).all(), "guard overwritten"
@@ -57,7 +74,8 @@ def run_fp8(case, M=None, config=None):
     M = case["M"] if M is None else M
     K, N = case["K"], case["N"]
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    sk.fp8_gemm(dev(case["codes"]), dev(case["scales"]), dev(case["x"][:M]), y, config=config)
+    sk.fp8_gemm(dev(case["codes"]), dev(case["scales"]), dev(case["x"][:M]), y, config=config,
+                workspace=ws_for(sk.OP_FP8, M, K, N, config))
     torch.cuda.synchronize()
     return y.float().cpu().numpy()
 
@@ -72,7 +90,7 @@ def ref_fp8(case, M=None):
     return oracle.fp8_gemm(case["x"][:M], case["codes"], case["scales"])
 
 
-SMALL_NVFP4 = [(1, 256, 512), (1, 272, 100), (3, 400, 300), (8, 1040, 1000), (8, 2048, 48), (2, 16, 7)]
+SMALL_NVFP4 = [(1, 256, 512), (1, 272, 100), (3, 400, 300), (8, 1040, 1000), (8, 2064, 48), (1, 3088, 200), (2, 16, 7)]
 
 
 @pytest.fixture(scope="module")
@@ -89,12 +107,13 @@ def test_nvfp4_one_hot_reproduces_dequantized_weights_exactly(K, N):
     deq = oracle.nvfp4_dequant_unscaled(case["codes"], case["scales"], K)       # [K, N]
     assert np.array_equal(deq.astype(np.float16).astype(np.float64), deq)
     eye = torch.eye(K, dtype=torch.float16, device="cuda")
-    for cfg in NVFP4_CFGS + VALU_CFGS:
+    for cfg in cfgs(1, K) + cfgs(0, K):
         rows = 1 if cfg[0] == 0 else 8
         out = np.empty((K, N))
+        ws = ws_for(sk.OP_NVFP4, rows, K, N, cfg)
         for r0 in range(0, K, rows):
             y = torch.empty((rows, N), dtype=torch.float16, device="cuda")
-            sk.nvfp4_gemm(blob, eye[r0:r0 + rows].contiguous(), y, config=cfg)
+            sk.nvfp4_gemm(blob, eye[r0:r0 + rows].contiguous(), y, config=cfg, workspace=ws)
             out[r0:r0 + rows] = y.float().cpu().numpy()
         assert np.array_equal(out, deq), f"config {cfg}: {np.argwhere(out != deq)[:5]}"
 
@@ -110,12 +129,12 @@ def test_fp8_one_hot_reproduces_codes_exactly():
     deq = oracle.fp8_dequant(codes, scales)
     assert np.array_equal(deq.astype(np.float16).astype(np.float64), deq)
     eye = np.eye(K, dtype=np.float16)
-    for ct, nw in CT_NW:
+    for cfg in cfgs(1, K, unit_k=512):
         out = np.empty((K, N))
         for r0 in range(0, K, 8):
             case["x"] = eye[r0:r0 + 8]
-            out[r0:r0 + 8] = run_fp8(case, M=8, config=(1, ct, nw))
-        assert np.array_equal(out, deq), f"config {(ct, nw)}"
+            out[r0:r0 + 8] = run_fp8(case, M=8, config=cfg)
+        assert np.array_equal(out, deq), f"config {cfg}"
 
 
 # -------------------------------------------------------- tolerance parity
@@ -123,8 +142,8 @@ def test_fp8_one_hot_reproduces_codes_exactly():
 def test_nvfp4_parity_all_configs(small_nvfp4, shape):
     case = small_nvfp4[shape]
     ref = ref_nvfp4(case)
-    cfgs = NVFP4_CFGS + (VALU_CFGS if case["M"] == 1 else [])
-    for cfg in cfgs:
+    choices = cfgs(1, case["K"]) + (cfgs(0, case["K"]) if case["M"] == 1 else [])
+    for cfg in choices:
         _check(run_nvfp4(case, config=cfg), ref, f"{shape} {cfg}")
     _check(run_nvfp4(case, guard=8), ref, f"{shape} default")
 
@@ -134,7 +153,7 @@ def test_nvfp4_every_m():
     for M in range(1, 9):
         ref = ref_nvfp4(case, M)
         _check(run_nvfp4(case, M=M), ref, f"M={M} default")
-        _check(run_nvfp4(case, M=M, config=(1, 2, 4)), ref, f"M={M} mfma")
+        _check(run_nvfp4(case, M=M, config=(1, 2, 2, 2)), ref, f"M={M} mfma split")
 
 
 SMALL_FP8 = [(1, 256, 256), (2, 272, 100), (4, 400, 300), (8, 1040, 1000), (3, 16, 129)]
@@ -144,8 +163,8 @@ SMALL_FP8 = [(1, 256, 256), (2, 272, 100), (4, 400, 300), (8, 1040, 1000), (3, 1
 def test_fp8_parity_all_configs(shape):
     case = workload.fp8_case(*shape, seed=sum(shape))
     ref = ref_fp8(case)
-    for ct, nw in CT_NW:
-        _check(run_fp8(case, config=(1, ct, nw)), ref, f"{shape} {(ct, nw)}")
+    for cfg in cfgs(1, case["K"], unit_k=512):
+        _check(run_fp8(case, config=cfg), ref, f"{shape} {cfg}")
     _check(run_fp8(case), ref, f"{shape} default")
 
 
@@ -162,12 +181,10 @@ def test_deterministic_repeats(small_nvfp4):
 def run_lm_head(case, M, config=None, logits=False, ws=None):
     K, N = case["K"], case["N"]
     idx = torch.full((M,), -7, dtype=torch.int32, device="cuda")
-    ws = ws if ws is not None else torch.zeros(sk.workspace_bytes(sk.OP_LM_HEAD, M, K, N), dtype=torch.uint8,
-                                               device="cuda")
+    ws = ws if ws is not None else ws_for(sk.OP_LM_HEAD, M, K, N, config)
     lg = torch.empty((M, N), dtype=torch.float16, device="cuda") if logits else None
     sk.lm_head_gemm_argmax(dev(case["blob"]), dev(case["x"][:M]), idx, N, logits=lg, workspace=ws, config=config)
     torch.cuda.synchronize()
-    assert not ws.any(), "workspace not left zero-filled"
     return idx.cpu().numpy(), (lg.float().cpu().numpy() if logits else None)
 
 
@@ -177,7 +194,7 @@ def test_lm_head_argmax_and_logits(shape):
     case = workload.nvfp4_case(*shape, seed=sum(shape))
     ref = ref_nvfp4(case)
     want, margin = oracle.argmax_rows(ref)
-    for cfg in NVFP4_CFGS:
+    for cfg in cfgs(1, K):
         idx, lg = run_lm_head(case, M, config=cfg, logits=True)
         assert np.array_equal(idx, want), f"{shape} {cfg}: {idx} vs {want} (margins {margin})"
         _check(lg, ref, f"{shape} {cfg} logits")
@@ -198,7 +215,7 @@ def test_lm_head_ties_go_to_lowest_column():
     case2 = dict(case, codes=codes, scales=scales, blob=sk.nvfp4_pack(codes, scales, case["g"], K, N))
     ref2 = ref_nvfp4(case2)
     want, _ = oracle.argmax_rows(ref2)
-    for cfg in NVFP4_CFGS:
+    for cfg in cfgs(1, K):
         idx, _ = run_lm_head(case2, M, config=cfg)
         assert np.array_equal(idx, want), f"{cfg}: {idx} vs {want}"
 
@@ -212,7 +229,7 @@ def test_lm_head_zero_weights_and_shared_workspace():
     idx, lg = run_lm_head(zero, M, logits=True)
     assert np.array_equal(idx, np.zeros(M)) and not lg.any()
     # one workspace reused across calls with different M
-    ws = torch.zeros(sk.workspace_bytes(sk.OP_LM_HEAD, 8, K, N), dtype=torch.uint8, device="cuda")
+    ws = ws_for(sk.OP_LM_HEAD, 8, K, N, None)
     for Mi in (8, 1, 5, 8):
         want, _ = oracle.argmax_rows(ref_nvfp4(case, Mi))
         idx, _ = run_lm_head(case, Mi, ws=ws)
