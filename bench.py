@@ -2,21 +2,23 @@
 """Benchmark of the weight-only quantized skinny GEMM on one MI355X.
 
 Metric: effective weight-read bandwidth in GB/s, i.e. compressed weight bytes
-(codes + scales + the 4-byte global scale) per step divided by the time per
-step, with every input already resident in HBM.  The headline workload is the
-NVFP4 GEMV at M = 1, K = 5120, N = 17408 (an MLP up-projection at decode);
-one step is one nvfp4_gemm call.  Each step reads a different one of R
-byte-identical copies of the packed weights (R copies exceed 512 MB) so that
-the 256 MB Infinity Cache cannot serve them.
+(E2M1 codes + E4M3 scales + the 4-byte global scale; FP8: codes + fp32 block
+scales) per step divided by the time per step, with every input already
+resident in HBM.  The headline workload is the NVFP4 GEMV at M = 1,
+K = 5120, N = 17408 (an MLP up-projection at decode): one step is one
+nvfp4_gemm call.  The same line also carries the two NVFP4 M = 8 shapes (fused
+gate+up 5120 x 34816 and down 17408 x 5120), timed the same way.
 
-    python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head]
+    python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head] [--M m]
 
+Each step reads a different one of R byte-identical copies of the weights
+(R copies exceed 600 MB) so that the 256 MB Infinity Cache cannot serve them.
 Timing: W eager warm-up steps, then the K steps are captured once into a HIP
-graph and the timed region is one replay of that graph, bracketed by device
-synchronisation.  A second pass launches the same K steps eagerly with a HIP
-event pair around each launch on the launch stream; the mean of those
-durations is the kernel duration used for the roofline figure.
-The CPU oracle is timed on a bounded sample of the same workload on the host.
+graph; the timed region is one replay of that graph, bracketed by device
+synchronisation, with a HIP event pair recorded on the replay stream.  The
+kernels of a replay run back to back, so the per-launch kernel duration is the
+event time divided by K.  The CPU oracle is timed beside it on the host, on a
+bounded sample of the headline workload.
 """
 
 import argparse
@@ -32,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective weight-read GB/s (% of MI355X HBM peak), NVFP4 GEMM at M=1 and M=8"
 MIN_ROTATION_BYTES = 600e6
+CPU_BASELINE_SECONDS = 10.0
 
 
 def parse():
@@ -41,19 +44,27 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="up")
     ap.add_argument("--M", type=int, default=None, help="row count (default: the workload's largest)")
-    ap.add_argument("--config", default=None, help="explicit kernel choice engine,ct,nw")
+    ap.add_argument("--config", default=None, help="explicit kernel choice engine,ct,nw,ksplit")
+    ap.add_argument("--headline-only", action="store_true", help="skip the M = 8 companion shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-cols", type=int, default=None)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run five device-to-device copies of MB megabytes (the known-size "
+                         "kernel that scales the HBM byte counters)")
     return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {time.strftime('%H:%M:%S')} {msg}", file=sys.stderr, flush=True)
 
 
 def describe(case, name):
     fmt = "NVFP4 W4A16" if case["fmt"] == "nvfp4" else "FP8 E4M3 W8A16"
-    return f"{fmt} {name} M={case['M']} K={case['K']} N={case['N']}"
+    extra = " + fused argmax" if name == "lm_head" else ""
+    return f"{fmt} {name} M={case['M']} K={case['K']} N={case['N']}{extra}"
 
 
-def cpu_baseline(case, sample_cols):
-    """Time the CPU oracle on a bounded column sample; GB/s of weight bytes it covers."""
+def cpu_baseline(case):
+    """Time the CPU oracle on the whole headline workload, repeated for about 10 s."""
     import numpy as np
     import oracle
     try:
@@ -61,138 +72,172 @@ def cpu_baseline(case, sample_cols):
         blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    N = case["N"]
-    cols = np.arange(min(sample_cols, N))
-    frac = len(cols) / N
-    t0 = time.perf_counter()
-    if case["fmt"] == "nvfp4":
-        oracle.nvfp4_gemm(case["x"], case["codes"], case["scales"], case["g"], cols=cols)
-    else:
-        oracle.fp8_gemm(case["x"], case["codes"], case["scales"], cols=cols)
-    dt = time.perf_counter() - t0
-    gbs = case["weight_bytes"] * frac / dt / 1e9
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        if case["fmt"] == "nvfp4":
+            oracle.nvfp4_gemm(case["x"], case["codes"], case["scales"], case["g"])
+        else:
+            oracle.fp8_gemm(case["x"], case["codes"], case["scales"])
+        calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_BASELINE_SECONDS:
+            break
+    gbs = case["weight_bytes"] * calls / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
-            "sample": f"first {len(cols)} of {N} columns ({frac:.3%} of the weights), one call, {dt:.1f} s; "
-                      f"decode+dequant on 1 thread, float64 matmul on {blas_threads} BLAS threads; "
-                      f"host has {os.cpu_count()} CPUs"}
+            "sample": f"the whole workload ({case['N']} columns), {calls} calls in {dt:.1f} s; "
+                      f"decode and dequantize on 1 thread, float64 matmul on {blas_threads} BLAS "
+                      f"threads; host has {os.cpu_count()} CPUs"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
-        sys.exit(2)
+def recorded_traffic(name, M):
+    """HBM bytes per launch from a committed counter summary under profiles/.
+
+    Used only if that summary was taken on the current kernel sources (same
+    SHA-256) for this workload; otherwise None."""
+    import glob
+    from fp8_quantized_skinny_amd.profile_summary import sources_sha256
+    sha = sources_sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
+        fields = {}
+        with open(path) as f:
+            for line in f:
+                key, sep, val = line.partition(":")
+                if sep and key.strip() and " " not in key.strip():
+                    fields.setdefault(key.strip(), val.strip())
+        if (fields.get("workload") == f"{name} M={M}" and fields.get("kernel_sources_sha256") == sha
+                and "traffic_bytes_per_launch" in fields):
+            return int(fields["traffic_bytes_per_launch"].split()[0])
+    return None
+
+
+def measure(name, M, cfg, steps, warmup, keep_case=False):
+    """Time `steps` launches of one workload; returns (result dict, case or None)."""
     import numpy as np
     import torch
     import fp8_quantized_skinny_amd as sk
     from fp8_quantized_skinny_amd import workload, synth
     from fp8_quantized_skinny_amd._lib import lib
 
-    name = args.workload
     fmt, ms, K, N = synth.WORKLOADS[name]
-    M = args.M or max(ms)
-    t_prep = time.perf_counter()
+    M = M or max(ms)
+    t = time.perf_counter()
     case = workload.nvfp4_case(M, K, N) if fmt == "nvfp4" else workload.fp8_case(M, K, N)
-    print(f"[bench] prepared {describe(case, name)} in {time.perf_counter() - t_prep:.1f} s", file=sys.stderr,
-          flush=True)
+    log(f"prepared {describe(case, name)} in {time.perf_counter() - t:.1f} s")
     wbytes = case["weight_bytes"]
     R = max(2, math.ceil(MIN_ROTATION_BYTES / wbytes))
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     L = lib()
     x = dev(case["x"])
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    cfg = tuple(int(v) for v in args.config.split(",")) if args.config else None
+    idx = torch.empty((M,), dtype=torch.int32, device="cuda")
     if fmt == "nvfp4":
         copies = [dev(case["blob"]) for _ in range(R)]
         scales = None
     else:
         copies = [dev(case["codes"]) for _ in range(R)]
         scales = dev(case["scales"])
-    idx = torch.empty((M,), dtype=torch.int32, device="cuda")
-    ws = torch.zeros(max(sk.workspace_bytes(sk.OP_LM_HEAD, M, K, N), 256), dtype=torch.uint8, device="cuda")
+    op = sk.OP_LM_HEAD if name == "lm_head" else (sk.OP_NVFP4 if fmt == "nvfp4" else sk.OP_FP8)
+    ws = torch.zeros(max(sk.workspace_bytes(op, M, K, N, cfg), 256), dtype=torch.uint8, device="cuda")
+    wsp, wsn = ws.data_ptr(), ws.numel()
+    xp, yp = x.data_ptr(), y.data_ptr()
 
-    def step(i, stream):
+    def step(i, s):
         w = copies[i % R].data_ptr()
-        if name == "lm_head":
-            if cfg:
-                st = L.lm_head_gemm_argmax_config(w, x.data_ptr(), idx.data_ptr(), None, M, K, N, ws.data_ptr(),
-                                                  ws.numel(), stream, *cfg)
-            else:
-                st = L.lm_head_gemm_argmax(w, x.data_ptr(), idx.data_ptr(), None, M, K, N, ws.data_ptr(),
-                                           ws.numel(), stream)
-        elif fmt == "nvfp4":
-            st = (L.nvfp4_gemm_config(w, x.data_ptr(), y.data_ptr(), M, K, N, None, 0, stream, *cfg) if cfg
-                  else L.nvfp4_gemm(w, x.data_ptr(), y.data_ptr(), M, K, N, None, 0, stream))
+        if op == sk.OP_LM_HEAD:
+            st = (L.lm_head_gemm_argmax_config(w, xp, idx.data_ptr(), None, M, K, N, wsp, wsn, s, *cfg) if cfg
+                  else L.lm_head_gemm_argmax(w, xp, idx.data_ptr(), None, M, K, N, wsp, wsn, s))
+        elif op == sk.OP_NVFP4:
+            st = (L.nvfp4_gemm_config(w, xp, yp, M, K, N, wsp, wsn, s, *cfg) if cfg
+                  else L.nvfp4_gemm(w, xp, yp, M, K, N, wsp, wsn, s))
         else:
-            st = (L.fp8_gemm_config(w, scales.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, N, None, 0, stream, *cfg)
-                  if cfg else L.fp8_gemm(w, scales.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, N, None, 0, stream))
+            st = (L.fp8_gemm_config(w, scales.data_ptr(), xp, yp, M, K, N, wsp, wsn, s, *cfg) if cfg
+                  else L.fp8_gemm(w, scales.data_ptr(), xp, yp, M, K, N, wsp, wsn, s))
         if st != 0:
             raise RuntimeError(f"launch failed: {sk.strerror(st)}")
 
     stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, stream.cuda_stream)
     torch.cuda.synchronize()
 
-    # Timed region: one replay of a graph holding exactly K steps.
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     with torch.cuda.stream(cap):
         with torch.cuda.graph(g, stream=cap):
-            for i in range(args.steps):
+            for i in range(steps):
                 step(i, torch.cuda.current_stream().cuda_stream)
     g.replay()
     torch.cuda.synchronize()
+
+    # Timed region: one replay of the K-step graph on `stream`.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
+    e0.record(stream)
     g.replay()
-    e1.record()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
-    ms_per_step = gpu_ms / args.steps
-    value = wbytes * args.steps / (gpu_ms * 1e-3) / 1e9
-
-    # Per-launch kernel durations (event pair around each launch, same stream).
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    log(f"{name} M={M}: graph replay {gpu_ms:.3f} ms GPU, {wall * 1e3:.3f} ms wall for {steps} steps")
+    us = gpu_ms * 1e3 / steps
+    gbs = wbytes / (us * 1e-6) / 1e9
+    res = {"workload": describe(case, name), "M": M, "K": K, "N": N, "weight_bytes": wbytes, "weight_copies": R,
+           "kernel_choice": list(cfg) if cfg else "default", "us_per_step": round(us, 3),
+           "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del g, copies
     torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        step(i, stream.cuda_stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    durs = np.array([a.elapsed_time(b) for a, b in evs])
-    kern_ms = float(durs.mean())
-    achieved = wbytes / (kern_ms * 1e-3) / 1e9
+    return res, (case if keep_case else None)
 
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels have no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        import torch
+        nbytes = args.copy_calibration * 1000 * 1000
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes, "copies": 5}), flush=True)
+        return
+    cfg = tuple(int(v) for v in args.config.split(",")) if args.config else None
+    head, case = measure(args.workload, args.M, cfg, args.steps, args.warmup,
+                         keep_case=not args.no_cpu_baseline)
+    companions = []
+    if not args.headline_only and args.workload == "up" and cfg is None:
+        for name in ("gate_up", "down"):
+            r, _ = measure(name, 8, None, args.steps, args.warmup)
+            companions.append(r)
+    value = head["GB/s"]
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": value,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(head["us_per_step"] * 1e-3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": describe(case, name), "M": M, "K": K, "N": N, "weight_bytes": wbytes,
-                   "weight_copies": R, "kernel_choice": list(cfg) if cfg else "default",
-                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4), "timed": "one HIP-graph replay of K steps"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel_us_mean": round(kern_ms * 1e3, 3), "kernel_us_p50": round(float(np.median(durs)) * 1e3, 3)},
+        "config": {**head, "timed": "one HIP-graph replay of K steps, weights rotated over R copies",
+                   "m8_shapes": companions},
+        "roofline": {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4),
+                     "traffic": None if cfg else recorded_traffic(args.workload, head["M"]),
+                     "kernel_us": head["us_per_step"]},
     }
-    print(f"[bench] graph replay: {gpu_ms:.3f} ms GPU, {wall * 1e3:.3f} ms wall for {args.steps} steps",
-          file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
-        cols = args.cpu_sample_cols or max(256, min(N, int(N * 0.25)))
-        out["cpu_baseline"] = cpu_baseline(case, cols)
+    if case is not None:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(out), flush=True)
 
 

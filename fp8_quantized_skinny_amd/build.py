@@ -29,7 +29,7 @@ def build(verbose=False):
     """Compile every source and link libskinny.so; returns the library path."""
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    common = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+    common = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-Wall", "-I", INCLUDE, "-I", CSRC]
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
@@ -40,7 +40,7 @@ def build(verbose=False):
         _run(cmd, verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    _run([hipcc(), "-shared", "-fPIC", "-pthread", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

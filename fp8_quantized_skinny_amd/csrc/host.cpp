@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <thread>
 #include <vector>
 
 using namespace skinny;
@@ -68,33 +69,68 @@ int e4m3_code(double v) {
   return sign | i;
 }
 
+// Host worker threads for the quantizers: the machine's hardware threads, at most 16.
+int host_threads() {
+  const unsigned hw = std::thread::hardware_concurrency();
+  return static_cast<int>(std::max(1u, std::min(hw, 16u)));
+}
+
+// Runs fn(thread_index, begin, end) over [0, count) split into contiguous ranges.
+template <typename Fn>
+void parallel_for(int count, Fn fn) {
+  const int nt = std::max(1, std::min(host_threads(), count));
+  std::vector<std::thread> pool;
+  for (int t = 0; t < nt; ++t) {
+    const int b = static_cast<int>(static_cast<long long>(count) * t / nt);
+    const int e = static_cast<int>(static_cast<long long>(count) * (t + 1) / nt);
+    pool.emplace_back(fn, t, b, e);
+  }
+  for (auto& th : pool) th.join();
+}
+
 int launch_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_EHIP; }
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-// Kernel choice made by the library when the caller does not pick one.
-// S K spans (units) per workgroup, as many as fit the wavefront limit and,
-// for the MFMA engine, the LDS copy of x (about 72 KiB); K beyond that is
-// split over workgroups, evened out so every split gets the same spans.
-LaunchCfg pick_cfg(int engine, int ku, int lds_bytes_per_span) {
+// Kernel choice made by the library when the caller does not pick one; each
+// rule is the fastest kernel choice measured on the decode shapes.
+//
+// Up to four rows: one tile per workgroup and as many K spans (units) per
+// workgroup as the 16-wavefront limit allows; K beyond that is split over
+// workgroups, evened out so that every split gets the same spans.  This is
+// the VALU engine for a plain M = 1 GEMV and the MFMA engine otherwise.
+//
+// Five to eight rows (MFMA): four tiles per workgroup (fewer when N has fewer
+// tiles) and the fewest K spans per workgroup that keep the K split at most
+// six ways.  The x slice a workgroup stages in LDS grows with M; short
+// workgroups keep it small, so more workgroups fit on a CU, and a split of at
+// most six keeps the partial-sum hand-off small next to the weight stream.
+LaunchCfg pick_whole_k_cfg(int engine, int ku) {
   int s = std::min(ku, kMaxWaves);
-  if (lds_bytes_per_span > 0) s = std::min(s, std::max(1, (72 * 1024) / lds_bytes_per_span));
   const int ksplit = (ku + s - 1) / s;
   s = (ku + ksplit - 1) / ksplit;
   return LaunchCfg{engine, 1, s, ksplit};
 }
 
+LaunchCfg pick_short_cfg(int ku, int nt) {
+  constexpr int kMaxSplit = 6;
+  const int ct = nt >= 4 ? 4 : (nt >= 2 ? 2 : 1);
+  int s = std::min((ku + kMaxSplit - 1) / kMaxSplit, kMaxWaves / ct);
+  const int ksplit = (ku + s - 1) / s;
+  s = (ku + ksplit - 1) / ksplit;
+  return LaunchCfg{1, ct, ct * s, ksplit};
+}
+
 LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax) {
-  (void)N;
   const Geometry g = nvfp4_geometry(K, N);
-  if (M == 1 && !argmax) return pick_cfg(0, g.ku, 0);
-  return pick_cfg(1, g.ku, M * (kUnitK + 8) * 2);
+  if (M > 4) return pick_short_cfg(g.ku, g.nt);
+  return pick_whole_k_cfg(M == 1 && !argmax ? 0 : 1, g.ku);
 }
 
 LaunchCfg default_fp8_cfg(int M, int K, int N) {
-  (void)N;
   const int ku = (K + 511) / 512;
-  return pick_cfg(1, ku, M * (512 + 8) * 2);
+  if (M > 4) return pick_short_cfg(ku, (N + 15) / 16);
+  return pick_whole_k_cfg(1, ku);
 }
 
 int nvfp4_common_checks(const void* w_packed, const uint16_t* x, const void* out, int M, int K, int N) {
@@ -265,11 +301,21 @@ int nvfp4_quantize(const float* w, int K, int N, uint8_t* codes, uint8_t* scales
   if (!w || !codes || !scales || !g_out) return SKINNY_EINVAL;
   if (K < 16 || K % 16 != 0 || K > kMaxK || N < 1 || N > kMaxN) return SKINNY_ESHAPE;
   const size_t total = static_cast<size_t>(K) * N;
+  std::vector<double> part_amax(host_threads(), 0.0);
+  std::vector<char> part_bad(part_amax.size(), 0);
+  parallel_for(K, [&](int t, int k0, int k1) {
+    double a = 0.0;
+    for (size_t i = static_cast<size_t>(k0) * N; i < static_cast<size_t>(k1) * N; ++i) {
+      const float v = w[i];
+      if (!std::isfinite(v)) { part_bad[t] = 1; return; }
+      a = std::fmax(a, std::fabs(static_cast<double>(v)));
+    }
+    part_amax[t] = a;
+  });
   double amax = 0.0;
-  for (size_t i = 0; i < total; ++i) {
-    const float v = w[i];
-    if (!std::isfinite(v)) return SKINNY_EINVAL;
-    amax = std::fmax(amax, std::fabs(static_cast<double>(v)));
+  for (size_t t = 0; t < part_amax.size(); ++t) {
+    if (part_bad[t]) return SKINNY_EINVAL;
+    amax = std::fmax(amax, part_amax[t]);
   }
   const float g = static_cast<float>(amax / (6.0 * 448.0));
   *g_out = g;
@@ -278,56 +324,66 @@ int nvfp4_quantize(const float* w, int K, int N, uint8_t* codes, uint8_t* scales
   std::memset(scales, 0, row_scales * N);
   if (g == 0.0f) return SKINNY_OK;
   const double gd = g;
-  std::vector<double> blk(16);
-  for (int n = 0; n < N; ++n) {
-    for (int b = 0; b < K / 16; ++b) {
-      double bmax = 0.0;
-      for (int i = 0; i < 16; ++i) {
-        blk[i] = static_cast<double>(w[static_cast<size_t>(b * 16 + i) * N + n]);
-        bmax = std::fmax(bmax, std::fabs(blk[i]));
+  // One 16-row K block at a time, every column of it (rows of w are contiguous in n).
+  parallel_for(K / 16, [&](int, int b0, int b1) {
+    std::vector<double> bmax(N), denom(N);
+    for (int b = b0; b < b1; ++b) {
+      const float* rows = w + static_cast<size_t>(b) * 16 * N;
+      std::fill(bmax.begin(), bmax.end(), 0.0);
+      for (int i = 0; i < 16; ++i)
+        for (int n = 0; n < N; ++n)
+          bmax[n] = std::fmax(bmax[n], std::fabs(static_cast<double>(rows[static_cast<size_t>(i) * N + n])));
+      for (int n = 0; n < N; ++n) {
+        const int sc = e4m3_code((bmax[n] / 6.0) / gd);
+        scales[static_cast<size_t>(n) * row_scales + b] = static_cast<uint8_t>(sc);
+        denom[n] = e4m3_value(sc & 0x7F) * gd;
       }
-      const double t = (bmax / 6.0) / gd;
-      const int sc = e4m3_code(t);
-      scales[static_cast<size_t>(n) * row_scales + b] = static_cast<uint8_t>(sc);
-      const double denom = e4m3_value(sc & 0x7F) * gd;
-      if (denom == 0.0) continue;
-      uint8_t* dst = codes + static_cast<size_t>(n) * row_codes + b * 8;
       for (int i = 0; i < 8; ++i) {
-        const int lo = e2m1_code(blk[2 * i] / denom);
-        const int hi = e2m1_code(blk[2 * i + 1] / denom);
-        dst[i] = static_cast<uint8_t>(lo | (hi << 4));
+        const float* lo_row = rows + static_cast<size_t>(2 * i) * N;
+        const float* hi_row = lo_row + N;
+        for (int n = 0; n < N; ++n) {
+          if (denom[n] == 0.0) continue;
+          const int lo = e2m1_code(static_cast<double>(lo_row[n]) / denom[n]);
+          const int hi = e2m1_code(static_cast<double>(hi_row[n]) / denom[n]);
+          codes[static_cast<size_t>(n) * row_codes + b * 8 + i] = static_cast<uint8_t>(lo | (hi << 4));
+        }
       }
     }
-  }
+  });
   return SKINNY_OK;
 }
 
 int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales) {
   if (!w || !codes || !scales) return SKINNY_EINVAL;
   if (K < 1 || K > kMaxK || N < 1 || N > kMaxN) return SKINNY_ESHAPE;
-  const size_t total = static_cast<size_t>(K) * N;
-  for (size_t i = 0; i < total; ++i)
-    if (!std::isfinite(w[i])) return SKINNY_EINVAL;
+  std::vector<char> part_bad(host_threads(), 0);
+  parallel_for(K, [&](int t, int k0, int k1) {
+    for (size_t i = static_cast<size_t>(k0) * N; i < static_cast<size_t>(k1) * N; ++i)
+      if (!std::isfinite(w[i])) { part_bad[t] = 1; return; }
+  });
+  for (char bad : part_bad)
+    if (bad) return SKINNY_EINVAL;
   const int KB = (K + 127) / 128, NB = (N + 127) / 128;
-  std::memset(codes, 0, total);
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n1 = std::min(N, nb * 128 + 128);
-    for (int kb = 0; kb < KB; ++kb) {
+  std::memset(codes, 0, static_cast<size_t>(K) * N);
+  // One 128-row K block at a time, every column block of it.
+  parallel_for(KB, [&](int, int kb0, int kb1) {
+    std::vector<double> bmax(NB);
+    for (int kb = kb0; kb < kb1; ++kb) {
       const int k1 = std::min(K, kb * 128 + 128);
-      double bmax = 0.0;
+      std::fill(bmax.begin(), bmax.end(), 0.0);
       for (int k = kb * 128; k < k1; ++k)
-        for (int n = nb * 128; n < n1; ++n)
-          bmax = std::fmax(bmax, std::fabs(static_cast<double>(w[static_cast<size_t>(k) * N + n])));
-      const float S = static_cast<float>(bmax / 448.0);
-      scales[static_cast<size_t>(nb) * KB + kb] = S;
-      if (S == 0.0f) continue;
-      const double Sd = S;
-      for (int n = nb * 128; n < n1; ++n)
-        for (int k = kb * 128; k < k1; ++k)
+        for (int n = 0; n < N; ++n)
+          bmax[n / 128] = std::fmax(bmax[n / 128], std::fabs(static_cast<double>(w[static_cast<size_t>(k) * N + n])));
+      for (int nb = 0; nb < NB; ++nb) scales[static_cast<size_t>(nb) * KB + kb] = static_cast<float>(bmax[nb] / 448.0);
+      for (int k = kb * 128; k < k1; ++k)
+        for (int n = 0; n < N; ++n) {
+          const double Sd = scales[static_cast<size_t>(n / 128) * KB + kb];
+          if (Sd == 0.0) continue;
           codes[static_cast<size_t>(n) * K + k] =
               static_cast<uint8_t>(e4m3_code(static_cast<double>(w[static_cast<size_t>(k) * N + n]) / Sd));
+        }
     }
-  }
+  });
   return SKINNY_OK;
 }
 

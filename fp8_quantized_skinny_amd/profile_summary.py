@@ -1,0 +1,107 @@
+"""Text summaries of rocprofv3 result databases for the kernels of this package.
+
+    python -m fp8_quantized_skinny_amd.profile_summary trace DB [--match SUBSTR]
+    python -m fp8_quantized_skinny_amd.profile_summary counters DB [--match SUBSTR]
+    python -m fp8_quantized_skinny_amd.profile_summary traffic FETCH_DB WRITE_DB COPY_FETCH_DB COPY_WRITE_DB
+            --match SUBSTR --copy-bytes BYTES
+    python -m fp8_quantized_skinny_amd.profile_summary sources
+
+`trace` prints, per kernel, the dispatch count and the mean / median / p10 /
+p90 duration in microseconds from a `rocprofv3 --kernel-trace` run.
+`counters` prints, per kernel and counter, the median value per dispatch from a
+`rocprofv3 --pmc` run (FETCH_SIZE and WRITE_SIZE are in KiB).  `traffic`
+turns one FETCH_SIZE run and one WRITE_SIZE run of a kernel into HBM bytes per
+dispatch, each counter scaled by what it reads for a device-to-device copy of
+known size (runs of `bench.py --copy-calibration`): bytes = count * copy_bytes
+/ copy_count.  `sources`
+prints the SHA-256 of the kernel sources, which ties a counter measurement to
+the code it was taken on.
+"""
+
+import argparse
+import collections
+import hashlib
+import os
+import sqlite3
+import sys
+
+import numpy as np
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+KERNEL_SOURCES = ("common.cuh", "internal.h", "nvfp4_gemm.hip", "fp8_gemm.hip")
+
+
+def sources_sha256():
+    """SHA-256 over the kernel source files, in a fixed order."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _short(name):
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0][:48]
+
+
+def trace_rows(db, match=""):
+    cur = sqlite3.connect(db).cursor()
+    durs = collections.defaultdict(list)
+    for name, d in cur.execute("select name, duration from kernels"):
+        if match in name:
+            durs[_short(name)].append(d / 1e3)
+    return {k: np.array(v) for k, v in durs.items()}
+
+
+def counter_rows(db, match=""):
+    cur = sqlite3.connect(db).cursor()
+    vals = collections.defaultdict(list)
+    for name, counter, value in cur.execute("select kernel_name, counter_name, value from counters_collection"):
+        if match in name:
+            vals[(_short(name), counter)].append(value)
+    return {k: np.array(v) for k, v in vals.items()}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("mode", choices=("trace", "counters", "traffic", "sources"))
+    ap.add_argument("db", nargs="*")
+    ap.add_argument("--match", default="")
+    ap.add_argument("--copy-bytes", type=float, default=512e6)
+    a = ap.parse_args(argv)
+    if a.mode == "traffic":
+        fetch_db, write_db, copy_fetch_db, copy_write_db = a.db
+        def one(db, counter, match):
+            rows = {k: v for k, v in counter_rows(db, match).items() if k[1] == counter}
+            if len(rows) != 1:
+                raise SystemExit(f"{db}: expected one kernel matching {match!r} with {counter}, got {list(rows)}")
+            return float(np.median(next(iter(rows.values()))))
+        f, w = one(fetch_db, "FETCH_SIZE", a.match), one(write_db, "WRITE_SIZE", a.match)
+        cf = one(copy_fetch_db, "FETCH_SIZE", "copyBuffer")
+        cw = one(copy_write_db, "WRITE_SIZE", "copyBuffer")
+        kf, kw = a.copy_bytes / cf, a.copy_bytes / cw
+        print(f"copy of {a.copy_bytes:.0f} bytes: FETCH_SIZE {cf:.4f}, WRITE_SIZE {cw:.4f} per dispatch "
+              f"-> {kf:.4f} and {kw:.4f} bytes per count")
+        print(f"kernel: FETCH_SIZE {f:.4f}, WRITE_SIZE {w:.4f} per dispatch")
+        print(f"hbm_read_bytes_per_launch: {f * kf:.0f}")
+        print(f"hbm_write_bytes_per_launch: {w * kw:.0f}")
+        print(f"traffic_bytes_per_launch: {f * kf + w * kw:.0f}")
+        return
+    a.db = a.db[0] if len(a.db) == 1 else a.db
+    if a.mode == "sources":
+        print(f"kernel_sources_sha256: {sources_sha256()}")
+        return
+    if a.mode == "trace":
+        print(f"{'kernel':48s} {'calls':>6s} {'mean_us':>9s} {'median_us':>9s} {'p10_us':>8s} {'p90_us':>8s}")
+        for k, v in sorted(trace_rows(a.db, a.match).items(), key=lambda kv: -kv[1].sum()):
+            print(f"{k:48s} {len(v):6d} {v.mean():9.3f} {np.median(v):9.3f} "
+                  f"{np.percentile(v, 10):8.3f} {np.percentile(v, 90):8.3f}")
+    else:
+        print(f"{'kernel':48s} {'counter':14s} {'dispatches':>10s} {'median_per_dispatch':>20s}")
+        for (k, c), v in sorted(counter_rows(a.db, a.match).items()):
+            print(f"{k:48s} {c:14s} {len(v):10d} {np.median(v):20.4f}")
+
+
+if __name__ == "__main__":
+    sys.exit(main())

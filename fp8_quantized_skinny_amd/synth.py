@@ -32,8 +32,12 @@ WORKLOADS = {
 }
 
 
-def draw_weights(rng, K, N, scale=0.02, chunk_rows=256):
-    """float32 [K, N] = float32(standard_normal * scale), drawn in row chunks."""
+def draw_weights(rng, K, N, scale=0.02, chunk_rows=None):
+    """float32 [K, N] = float32(standard_normal * scale), drawn in row chunks.
+
+    The default chunk holds about 4 MB of float64 draws, which stays in cache."""
+    if chunk_rows is None:
+        chunk_rows = max(1, (1 << 19) // N)
     w = np.empty((K, N), np.float32)
     buf = np.empty((min(chunk_rows, K), N), np.float64)
     for r0 in range(0, K, chunk_rows):

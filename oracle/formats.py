@@ -29,9 +29,8 @@ E2M1_MAX = 6.0
 E4M3_MAX = 448.0
 
 
-def e2m1_decode(codes):
-    """4-bit codes (values 0..15, any integer dtype) -> float64 values."""
-    c = np.asarray(codes).astype(np.int64)
+def _e2m1_from_bits(c):
+    """E2M1 value of each 4-bit code in the int64 array c, from the bit fields."""
     s = (c >> 3) & 1
     e = (c >> 1) & 3
     m = c & 1
@@ -39,9 +38,8 @@ def e2m1_decode(codes):
     return np.where(s == 1, -mag, mag)
 
 
-def e4m3_decode(codes):
-    """8-bit E4M3FN codes (values 0..255) -> float64 values (NaN for 0x7F/0xFF)."""
-    c = np.asarray(codes).astype(np.int64)
+def _e4m3_from_bits(c):
+    """E4M3FN value of each 8-bit code in the int64 array c, from the bit fields (NaN at s.1111.111)."""
     s = (c >> 7) & 1
     e = (c >> 3) & 15
     m = c & 7
@@ -50,6 +48,22 @@ def e4m3_decode(codes):
     mag = np.where(e == 0, sub, normal)
     mag = np.where((e == 15) & (m == 7), np.nan, mag)
     return np.where(s == 1, -mag, mag)
+
+
+# Each format has only 16 / 256 codes: decode every code once from its bits
+# and look large arrays up in that list (same values, far less work per weight).
+_E2M1_VALUES = _e2m1_from_bits(np.arange(16, dtype=np.int64))
+_E4M3_VALUES = _e4m3_from_bits(np.arange(256, dtype=np.int64))
+
+
+def e2m1_decode(codes):
+    """4-bit codes (values 0..15, any integer dtype) -> float64 values."""
+    return np.take(_E2M1_VALUES, np.asarray(codes).astype(np.uint8, copy=False) & np.uint8(15))
+
+
+def e4m3_decode(codes):
+    """8-bit E4M3FN codes (values 0..255) -> float64 values (NaN for 0x7F/0xFF)."""
+    return np.take(_E4M3_VALUES, np.asarray(codes).astype(np.uint8, copy=False))
 
 
 def _round_half_even_to_grid(a, exp_floor, mant_bits, max_val):

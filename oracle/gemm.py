@@ -50,7 +50,7 @@ def nvfp4_dequant_unscaled(codes, scales, K, cols=None):
     return (q * s).T
 
 
-def nvfp4_gemm(x, codes, scales, g, cols=None, chunk=8192):
+def nvfp4_gemm(x, codes, scales, g, cols=None, chunk=1024):
     """y = x @ (E2M1(q) * E4M3(s) * g) in float64.  x: [M, K] (fp16 values).
 
     cols: optional array of output columns to compute (others are skipped).
@@ -78,7 +78,7 @@ def fp8_dequant(codes, scales, cols=None):
     return (c * S).T
 
 
-def fp8_gemm(x, codes, scales, cols=None, chunk=8192):
+def fp8_gemm(x, codes, scales, cols=None, chunk=1024):
     """y = x @ (E4M3(c) * S) in float64."""
     x64 = np.asarray(x).astype(np.float64)
     n_all = np.asarray(codes).shape[0] if cols is None else len(cols)
