@@ -68,7 +68,7 @@ def _workspace(workspace, need, where):
     if need == 0 and workspace is None:
         return None, 0
     if workspace is None or workspace.numel() < need:
-        raise ValueError(f"{where}: a zero-filled workspace of at least {need} bytes is required")
+        raise ValueError(f"{where}: a workspace of at least {need} bytes is required")
     return _dev(workspace, torch.uint8, "workspace"), workspace.numel()
 
 
@@ -134,7 +134,8 @@ def nvfp4_gemm(w_packed, x, y, K=None, N=None, workspace=None, stream=None, conf
     """y[M, N] fp16 = x[M, K] fp16 . dequant(W); w_packed: CUDA uint8 blob from nvfp4_pack.
 
     config: optional (engine, ct, nw, ksplit) kernel choice; default lets the library pick.
-    workspace: CUDA uint8 tensor, zero-filled once, when workspace_bytes(OP_NVFP4, ...) > 0."""
+    workspace: CUDA uint8 tensor of at least workspace_bytes(OP_NVFP4, ...) bytes when that is > 0
+    (scratch: any contents, not shared by calls that overlap in time)."""
     import torch
     M, Kx = x.shape
     K = Kx if K is None else K
@@ -176,7 +177,7 @@ def fp8_gemm(w, block_scales, x, y, workspace=None, stream=None, config=None):
 def lm_head_gemm_argmax(w_packed, x, idx, N, logits=None, workspace=None, stream=None, config=None):
     """idx[M] int32 = per-row argmax over the fp32 logits of x . dequant(W) (ties -> lowest n).
 
-    workspace: CUDA uint8 tensor of workspace_bytes(OP_LM_HEAD, ...) bytes, zero-filled once."""
+    workspace: CUDA uint8 tensor of at least workspace_bytes(OP_LM_HEAD, ...) bytes (scratch)."""
     import torch
     M, K = x.shape
     _shape_checks(x, M, K, logits, N, "logits")

@@ -45,12 +45,6 @@ __device__ __forceinline__ float e4m3f(uint32_t w) {
   return __builtin_amdgcn_cvt_f32_fp8(w, B);
 }
 
-// Lane (16r + i) receives lane (16r + I)'s value: DPP row_newbcast.
-template <int I>
-__device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x150 + I, 0xf, 0xf, true));
-}
-
 // Sum of v over lanes {l, l^16, l^32, l^48}: the four 16-lane rows of a
 // wavefront, exchanged with ds_bpermute lane shuffles.  Every lane ends with
 // the same value, (v0 + v2) + (v1 + v3) for rows 0..3.
@@ -64,31 +58,25 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Cross-workgroup hand-off without cache write-backs.  Data that another
-// workgroup (possibly on another XCD, with its own L2) reads back is written
-// and read with system-scope atomic accesses, which go to the coherence point
-// instead of a private L2 copy; wait_stores() makes them complete before the
-// arrival counter is bumped.  Counters and keys are system-scope atomic
-// read-modify-writes whose results are waited for, so each one is performed
-// before the next is issued.
-__device__ __forceinline__ void store_shared(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+// Ordered argmax key of logit v at column n: the top 32 bits order like the
+// fp32 value (+0 and -0 made equal), the low 32 bits are the inverted column,
+// so the larger key is the larger logit or, on a tie, the lower column.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
+  if (v == 0.0f) v = 0.0f;
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<unsigned long long>(ord) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(n));
 }
-__device__ __forceinline__ float load_shared(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ uint32_t counter_add(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ uint32_t counter_exch(uint32_t* p, uint32_t v) {
-  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ unsigned long long key_max(unsigned long long* p, unsigned long long v) {
-  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ unsigned long long key_exch(unsigned long long* p, unsigned long long v) {
-  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+
+// Largest key over the WIDTH lanes of each lane group (every lane gets it).
+template <int WIDTH = 64>
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+#pragma unroll
+  for (int off = WIDTH / 2; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(k, off, WIDTH);
+    k = o > k ? o : k;
+  }
+  return k;
 }
 
 }  // namespace skinny

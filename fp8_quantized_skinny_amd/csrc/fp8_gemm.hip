@@ -14,7 +14,8 @@
 // Work split follows the NVFP4 kernels: a unit is one 16-column tile x 512 K
 // (four chunks, 8 KiB of codes); every wavefront loads one unit at once and
 // contracts it; a workgroup is CT tiles x S units along K (nw = CT * S), with
-// a K split over workgroups when K has more units.  x is copied into LDS once
+// a K split over workgroups when K has more units (partial sums stored with
+// plain stores and added in split order by the reduction kernel).  x is copied into LDS once
 // per workgroup with direct-to-LDS loads.  Lane (grp, c) reads, per chunk, the
 // two 16-byte pieces K = 128j + 64h + 16grp .. +16 (h = 0, 1) of column c, so
 // each load instruction covers 64 contiguous bytes of 16 columns.  Pieces past
@@ -29,7 +30,6 @@ namespace {
 
 constexpr int kFp8UnitChunks = 4;
 constexpr int kFp8UnitK = kFp8UnitChunks * kChunkK;  // 512
-constexpr int kFp8PartFloats = 128;
 
 struct Fp8Args {
   const uint8_t* w;
@@ -39,8 +39,7 @@ struct Fp8Args {
   int M, K, N;
   int nt, kb, ku;  // column tiles, scale blocks along K, units along K
   int ksplit, S;
-  float* part;
-  uint32_t* tile_cnt;
+  float* part;  // [ksplit][M][N] fp32 partial sums (ksplit > 1)
 };
 
 struct Fp8Plan {
@@ -80,35 +79,31 @@ __device__ void fp8_stage_x(const Fp8Args& a, const Fp8Plan& P, _Float16* xs) {
   }
 }
 
-// A fragments of chunk j: lane (row m = c, grp) holds, for MFMA i = 2h + s,
-// x[m][512u + 128j + 64h + 16grp + 8s .. +8]; zero for m >= M.
-__device__ __forceinline__ void fp8_read_x(f16x8 (&xa)[4], const _Float16* xrow, bool row, int j) {
-  if (row) {
-    const _Float16* p = xrow + j * kChunkK;
-    xa[0] = *reinterpret_cast<const f16x8*>(p);
-    xa[1] = *reinterpret_cast<const f16x8*>(p + 8);
-    xa[2] = *reinterpret_cast<const f16x8*>(p + 64);
-    xa[3] = *reinterpret_cast<const f16x8*>(p + 72);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
+// A fragments of chunk j: lane (row c, grp) holds, for MFMA i = 2h + s,
+// x[min(c, M-1)][512u + 128j + 64h + 16grp + 8s .. +8].  Rows c >= M only
+// feed output rows that are never stored, so they repeat row M-1.
+__device__ __forceinline__ void fp8_read_x(f16x8 (&xa)[4], const _Float16* xrow, int j) {
+  const _Float16* p = xrow + j * kChunkK;
+  xa[0] = *reinterpret_cast<const f16x8*>(p);
+  xa[1] = *reinterpret_cast<const f16x8*>(p + 8);
+  xa[2] = *reinterpret_cast<const f16x8*>(p + 64);
+  xa[3] = *reinterpret_cast<const f16x8*>(p + 72);
 }
 
 template <int J>
 __device__ __forceinline__ void fp8_steps(const u32x4 (&w)[kFp8UnitChunks][2], const float (&sc)[kFp8UnitChunks],
-                                          f16x8 (&x0)[4], f16x8 (&x1)[4], f32x4& acc, const _Float16* xrow, bool row) {
+                                          f16x8 (&x0)[4], f16x8 (&x1)[4], f32x4& acc, const _Float16* xrow) {
   if constexpr (J < kFp8UnitChunks) {
     f16x8 (&cur)[4] = (J & 1) ? x1 : x0;
     f16x8 (&nxt)[4] = (J & 1) ? x0 : x1;
-    if constexpr (J + 1 < kFp8UnitChunks) fp8_read_x(nxt, xrow, row, J + 1);
+    if constexpr (J + 1 < kFp8UnitChunks) fp8_read_x(nxt, xrow, J + 1);
     f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[0], e4m3x8(w[J][0].x, w[J][0].y), p, 0, 0, 0);
     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[1], e4m3x8(w[J][0].z, w[J][0].w), p, 0, 0, 0);
     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[2], e4m3x8(w[J][1].x, w[J][1].y), p, 0, 0, 0);
     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[3], e4m3x8(w[J][1].z, w[J][1].w), p, 0, 0, 0);
     acc += sc[J] * p;
-    fp8_steps<J + 1>(w, sc, x0, x1, acc, xrow, row);
+    fp8_steps<J + 1>(w, sc, x0, x1, acc, xrow);
   }
 }
 
@@ -151,52 +146,27 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_mfma(Fp8Args a) {
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (P.active) {
-    const bool rowok = cl < a.M;
-    const _Float16* xrow = xs + (rowok ? cl : 0) * fp8_xs_stride(P.S) + P.s * kFp8UnitK + grp * 16;
+    const _Float16* xrow = xs + min(cl, a.M - 1) * fp8_xs_stride(P.S) + P.s * kFp8UnitK + grp * 16;
     f16x8 x0[4], x1[4];
-    fp8_read_x(x0, xrow, rowok, 0);
-    fp8_steps<0>(w, sc, x0, x1, acc, xrow, rowok);
+    fp8_read_x(x0, xrow, 0);
+    fp8_steps<0>(w, sc, x0, x1, acc, xrow);
   }
   if (P.lane < 32) red[P.wave * 32 + P.lane] = acc;
   __syncthreads();
 
   const bool fin = P.wave < CT && P.tile0 + P.wave < a.nt && P.lane < 32;
-  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (fin) {
+  const int n = (P.tile0 + P.wave) * kTileCols + cl;
+  if (fin && n < a.N) {
+    f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < P.sw; ++s) tot += red[(P.wave * P.S + s) * 32 + P.lane];
-    if (a.ksplit > 1) {
-      float* dst = a.part + (static_cast<size_t>(blockIdx.y) * a.nt + P.tile0 + P.wave) * kFp8PartFloats + 4 * P.lane;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) store_shared(dst + i, tot[i]);
-    }
-  }
-  if (a.ksplit > 1) {
-    __shared__ int last;
-    wait_stores();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      last = counter_add(a.tile_cnt + blockIdx.x, 1u) == static_cast<uint32_t>(a.ksplit - 1);
-      if (last) counter_exch(a.tile_cnt + blockIdx.x, 0u);
-    }
-    __syncthreads();
-    if (!last) return;
-  }
-  if (fin) {
-    if (a.ksplit > 1) {
-      tot = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < a.ksplit; ++ks) {
-        const float* src = a.part + (static_cast<size_t>(ks) * a.nt + P.tile0 + P.wave) * kFp8PartFloats + 4 * P.lane;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tot[i] += load_shared(src + i);
-      }
-    }
-    const int n = (P.tile0 + P.wave) * kTileCols + cl;
-    if (n < a.N) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = grp * 4 + i;
-        if (m < a.M) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(tot[i]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int m = grp * 4 + i;
+      if (m >= a.M) continue;
+      if (a.ksplit > 1)
+        a.part[(static_cast<size_t>(blockIdx.y) * a.M + m) * a.N + n] = tot[i];
+      else
+        a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(tot[i]);
     }
   }
 }
@@ -207,8 +177,6 @@ size_t fp8_lds_bytes(int M, int S, int nw) {
 }
 
 }  // namespace
-
-size_t fp8_part_floats() { return kFp8PartFloats; }
 
 bool fp8_cfg_supported(const LaunchCfg& c, int M, int K) {
   if (c.engine != 1 || !(c.ct == 1 || c.ct == 2 || c.ct == 4 || c.ct == 8)) return false;
@@ -222,7 +190,7 @@ bool fp8_cfg_supported(const LaunchCfg& c, int M, int K) {
 #define SKINNY_FP8_DISPATCH(CT)                                                    \
   if (cfg.ct == CT) {                                                              \
     hipLaunchKernelGGL((fp8_mfma<CT>), grid, dim3(cfg.nw * 64), lds, stream, a);   \
-    return hipGetLastError();                                                      \
+    e = hipGetLastError();                                                         \
   }
 
 hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x, uint16_t* y, int M,
@@ -243,14 +211,15 @@ hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x, 
   a.ksplit = cfg.ksplit;
   a.S = cfg.nw / cfg.ct;
   a.part = wl.part_bytes ? reinterpret_cast<float*>(ws + wl.part_off) : nullptr;
-  a.tile_cnt = wl.tile_cnt_bytes ? reinterpret_cast<uint32_t*>(ws + wl.tile_cnt_off) : nullptr;
   const dim3 grid((a.nt + cfg.ct - 1) / cfg.ct, cfg.ksplit);
   const size_t lds = fp8_lds_bytes(M, a.S, cfg.nw);
+  hipError_t e = hipErrorInvalidValue;
   SKINNY_FP8_DISPATCH(1)
   SKINNY_FP8_DISPATCH(2)
   SKINNY_FP8_DISPATCH(4)
   SKINNY_FP8_DISPATCH(8)
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || cfg.ksplit == 1) return e;
+  return launch_finalize(a.part, cfg.ksplit, M, N, nullptr, y, nullptr, stream);
 }
 
 }  // namespace skinny

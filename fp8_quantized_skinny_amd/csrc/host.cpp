@@ -102,9 +102,9 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 //
 // Five to eight rows (MFMA): four tiles per workgroup (fewer when N has fewer
 // tiles) and the fewest K spans per workgroup that keep the K split at most
-// six ways.  The x slice a workgroup stages in LDS grows with M; short
-// workgroups keep it small, so more workgroups fit on a CU, and a split of at
-// most six keeps the partial-sum hand-off small next to the weight stream.
+// nine ways.  The x slice a workgroup stages in LDS grows with M and with its
+// spans; short workgroups keep it small, so that more of them fit on a CU,
+// and the split reduction stays a single short pass.
 LaunchCfg pick_whole_k_cfg(int engine, int ku) {
   int s = std::min(ku, kMaxWaves);
   const int ksplit = (ku + s - 1) / s;
@@ -113,7 +113,7 @@ LaunchCfg pick_whole_k_cfg(int engine, int ku) {
 }
 
 LaunchCfg pick_short_cfg(int ku, int nt) {
-  constexpr int kMaxSplit = 6;
+  constexpr int kMaxSplit = 9;
   const int ct = nt >= 4 ? 4 : (nt >= 2 ? 2 : 1);
   int s = std::min((ku + kMaxSplit - 1) / kMaxSplit, kMaxWaves / ct);
   const int ksplit = (ku + s - 1) / s;
@@ -162,23 +162,22 @@ Geometry nvfp4_geometry(int K, int N) {
   return g;
 }
 
+// Partial sums of a K split: fp32 part[split][m][n] for the M real rows.
+// Argmax candidates: one 64-bit key per row for each workgroup of the GEMM
+// kernel (no split) or each column block of the split reduction.
 WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N, bool argmax) {
   const Geometry g = nvfp4_geometry(K, N);
   WorkspaceLayout w{};
   size_t off = 0;
-  if (argmax) {  // one 64-bit (logit, column) candidate per workgroup and row
-    const size_t groups = (g.nt + cfg.ct - 1) / cfg.ct;
+  if (argmax) {
+    const size_t groups = cfg.ksplit > 1 ? finalize_groups(N) : (g.nt + cfg.ct - 1) / cfg.ct;
     w.keys_off = off;
     w.keys_bytes = groups * M * 8;
     off = align256(off + w.keys_bytes);
   }
   if (cfg.ksplit > 1) {
-    const size_t groups = (g.nt + cfg.ct - 1) / cfg.ct;
-    w.tile_cnt_off = off;
-    w.tile_cnt_bytes = groups * 4;
-    off = align256(off + w.tile_cnt_bytes);
     w.part_off = off;
-    w.part_bytes = static_cast<size_t>(cfg.ksplit) * g.nt * nvfp4_part_floats() * 4;
+    w.part_bytes = static_cast<size_t>(cfg.ksplit) * M * N * 4;
     off = align256(off + w.part_bytes);
   }
   w.total = off;
@@ -186,18 +185,12 @@ WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N
 }
 
 WorkspaceLayout fp8_workspace_layout(const LaunchCfg& cfg, int M, int K, int N) {
-  (void)M;
   (void)K;
   WorkspaceLayout w{};
   size_t off = 0;
   if (cfg.ksplit > 1) {
-    const size_t nt = (N + kTileCols - 1) / kTileCols;
-    const size_t groups = (nt + cfg.ct - 1) / cfg.ct;
-    w.tile_cnt_off = off;
-    w.tile_cnt_bytes = groups * 4;
-    off = align256(off + w.tile_cnt_bytes);
     w.part_off = off;
-    w.part_bytes = static_cast<size_t>(cfg.ksplit) * nt * fp8_part_floats() * 4;
+    w.part_bytes = static_cast<size_t>(cfg.ksplit) * M * N * 4;
     off = align256(off + w.part_bytes);
   }
   w.total = off;

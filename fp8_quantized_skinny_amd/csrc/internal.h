@@ -67,10 +67,12 @@ struct LaunchCfg {
 constexpr int kMaxWaves = 16;
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 
-// Workspace of one call (all offsets in bytes, 256-aligned).  Counters and
-// argmax keys must be zero before the first call; every call leaves them zero.
+// Workspace of one call (offsets in bytes, 256-aligned): argmax candidate
+// keys (lm_head) and the fp32 partial sums part[split][m][n] of a K split.
+// Every byte is written by the call before it is read, so no initialisation
+// is needed.
 struct WorkspaceLayout {
-  size_t keys_off, keys_bytes, tile_cnt_off, tile_cnt_bytes, part_off, part_bytes, total;
+  size_t keys_off, keys_bytes, part_off, part_bytes, total;
 };
 WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N, bool argmax);
 WorkspaceLayout fp8_workspace_layout(const LaunchCfg& cfg, int M, int K, int N);
@@ -85,8 +87,17 @@ hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x,
 bool nvfp4_cfg_supported(const LaunchCfg& cfg, int M, int K, bool argmax);
 bool fp8_cfg_supported(const LaunchCfg& cfg, int M, int K);
 size_t nvfp4_mfma_lds_bytes(int M, int S, int nw);
-size_t nvfp4_part_floats();
-size_t fp8_part_floats();
+
+// Second pass of a K split (reduce.hip): adds part[split][m][n] over the
+// splits in order, scales by *gptr (1 if null) and writes fp16 y (if non-null)
+// and, if cand is non-null, one argmax key per row for each of the
+// finalize_groups(N) column blocks.  launch_argmax_reduce turns `groups`
+// candidate keys per row into idx.
+int finalize_groups(int N);
+hipError_t launch_finalize(const float* part, int ksplit, int M, int N, const float* gptr, uint16_t* y,
+                           unsigned long long* cand, hipStream_t stream);
+hipError_t launch_argmax_reduce(const unsigned long long* cand, int groups, int M, int32_t* idx,
+                                hipStream_t stream);
 
 // Largest row count (the target token plus seven drafts).
 constexpr int kMaxRows = 8;

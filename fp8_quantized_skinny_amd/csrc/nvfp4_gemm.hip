@@ -15,10 +15,14 @@
 // workgroup is CT tiles x S consecutive K spans (nw = CT * S wavefronts);
 // the S partial sums of a tile are added in LDS in span order.  When K has
 // more spans than a workgroup covers, ksplit workgroups share a tile group:
-// each hands its per-tile partial over through the workspace and the last to
-// arrive adds them in split order.  Results never depend on timing.  Few
-// registers per wavefront (one unit) let the chip keep tens of megabytes of
-// weight loads in flight, which is what saturates HBM at these sizes.
+// each stores its fp32 partial sums with plain stores and exits, and a second
+// small kernel (reduce.hip) adds the splits in split order, so results never
+// depend on timing.  (Handing partials over inside one kernel needs
+// system-scope stores, a wait for them and an arrival counter; on MI355X that
+// kept finished workgroups resident for microseconds and cost more than the
+// second launch.)  Few registers per wavefront (one unit) let the chip keep
+// tens of megabytes of weight loads in flight, which is what saturates HBM at
+// these sizes.
 //
 // Two engines (lane l = 16*grp + c handles column c of the tile and the
 // 32-K run 128j + 32grp .. +32 of every chunk j):
@@ -32,10 +36,11 @@
 //     direct-to-LDS loads (no VGPRs) before the weight loads; A fragments are
 //     read from LDS one chunk ahead.  The pages' 8-row verification tile
 //     (post, on why the M = 8 row matters) fills half of the 16-row MFMA tile.
-// The MFMA engine also carries the lm_head epilogue: each workgroup writes,
-// per row, the (fp32 logit, column) of its best column as one ordered 64-bit
-// key; a second, one-workgroup kernel takes the maximum key per row (ties to
-// the lowest column) and writes the indices.
+// The MFMA engine also carries the lm_head epilogue: each workgroup (or, with
+// a K split, each block of the split reduction) writes, per row, the (fp32
+// logit, column) of its best column as one ordered 64-bit key; a one-workgroup
+// kernel takes the maximum key per row (ties to the lowest column) and writes
+// the indices.
 #include <hip/hip_runtime.h>
 
 #include "common.cuh"
@@ -51,14 +56,9 @@ struct Nvfp4Args {
   _Float16* y;
   int M, K, N;
   int ku, nt, ksplit, S;     // S: K spans per workgroup
-  float* part;               // [ksplit][nt][kPartFloats] per-tile partials (ksplit > 1)
-  uint32_t* tile_cnt;        // [gridDim.x] arrival counters (ksplit > 1)
-  unsigned long long* cand;  // [gridDim.x][M] argmax candidates (lm_head) or null
+  float* part;               // [ksplit][M][N] fp32 partial sums (ksplit > 1)
+  unsigned long long* cand;  // [gridDim.x][M] argmax candidates (lm_head, ksplit == 1)
 };
-
-// Partial layout per (split, tile): 32 lanes x 4 floats (MFMA rows 4grp..+3
-// of column c for lanes 16grp + c), or 16 floats (VALU, one per column).
-constexpr int kPartFloats = 128;
 
 // This wavefront's unit and its workgroup's geometry (wave-uniform values).
 struct Plan {
@@ -87,28 +87,6 @@ struct Plan {
 
 __device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ uint32_t ordered_key(float v) {
-  if (v == 0.0f) v = 0.0f;  // +0 and -0 compare equal
-  const uint32_t b = __builtin_bit_cast(uint32_t, v);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// True in every thread of the last workgroup of this tile group to arrive
-// (always true without a K split).  Partials must have been written with
-// store_shared() by this workgroup before the call.
-__device__ bool last_of_tile_group(const Nvfp4Args& a) {
-  if (a.ksplit == 1) return true;
-  __shared__ int last;
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    last = counter_add(a.tile_cnt + blockIdx.x, 1u) == static_cast<uint32_t>(a.ksplit - 1);
-    if (last) counter_exch(a.tile_cnt + blockIdx.x, 0u);  // every split of this group has arrived
-  }
-  __syncthreads();
-  return last;
 }
 
 // ---------------------------------------------------------------------------
@@ -187,24 +165,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu_m1(Nvfp4Args a) {
   if (P.lane < 16) red[P.wave][P.lane] = acc;
   __syncthreads();
 
-  // Wavefront t < CT finishes local tile t: its spans in order, then either
-  // the store or the hand-off of the partial.
+  // Wavefront t < CT finishes local tile t: its spans in order, then the
+  // output or, with a K split, this split's partial sum.
   const bool fin = P.wave < CT && P.lane < 16 && P.tile0 + P.wave < a.nt;
-  float tot = 0.0f;
   if (fin) {
+    float tot = 0.0f;
     for (int s = 0; s < P.sw; ++s) tot += red[P.wave * P.S + s][P.lane];
-    if (a.ksplit > 1)
-      store_shared(a.part + (static_cast<size_t>(blockIdx.y) * a.nt + P.tile0 + P.wave) * kPartFloats + P.lane, tot);
-  }
-  if (!last_of_tile_group(a)) return;
-  if (fin) {
-    if (a.ksplit > 1) {
-      tot = 0.0f;
-      for (int ks = 0; ks < a.ksplit; ++ks)
-        tot += load_shared(a.part + (static_cast<size_t>(ks) * a.nt + P.tile0 + P.wave) * kPartFloats + P.lane);
-    }
     const int n = (P.tile0 + P.wave) * kTileCols + P.lane;
-    if (n < a.N) a.y[n] = static_cast<_Float16>(*a.gptr * tot);
+    if (n < a.N) {
+      if (a.ksplit > 1)
+        a.part[static_cast<size_t>(blockIdx.y) * a.N + n] = tot;
+      else
+        a.y[n] = static_cast<_Float16>(*a.gptr * tot);
+    }
   }
 }
 
@@ -238,16 +211,14 @@ __device__ void stage_x(const Nvfp4Args& a, const Plan& P, _Float16* xs) {
   }
 }
 
-// Operand A fragments of chunk j: lane (row m = c, grp) holds
-// x[m][1024s + 128j + 32grp + 8i .. +8] for MFMA i = 0..3; zero for m >= M.
-__device__ __forceinline__ void read_x_frag(f16x8 (&xa)[4], const _Float16* xrow, bool row, int j) {
-  if (row) {
+// Operand A fragments of chunk j: lane (row c, grp) holds
+// x[min(c, M-1)][1024s + 128j + 32grp + 8i .. +8] for MFMA i = 0..3.  Rows
+// c >= M of the 16-row tile repeat row M-1 instead of being zeroed: they only
+// feed output rows >= M, which are never stored, and reading them costs
+// nothing where zeroing costs a branch and sixteen moves per chunk.
+__device__ __forceinline__ void read_x_frag(f16x8 (&xa)[4], const _Float16* xrow, int j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const f16x8*>(xrow + j * kChunkK + 8 * i);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
+  for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const f16x8*>(xrow + j * kChunkK + 8 * i);
 }
 
 template <int J>
@@ -264,13 +235,13 @@ __device__ __forceinline__ f32x4 mfma_chunk(const u32x4& cj, const u32x4& sv, co
 
 template <int J>
 __device__ __forceinline__ void mfma_steps(const u32x4 (&c)[kChunksPerUnit], const u32x4& sv, f16x8 (&x0)[4],
-                                           f16x8 (&x1)[4], f32x4& acc, const _Float16* xrow, bool row) {
+                                           f16x8 (&x1)[4], f32x4& acc, const _Float16* xrow) {
   if constexpr (J < kChunksPerUnit) {
     f16x8 (&cur)[4] = (J & 1) ? x1 : x0;
     f16x8 (&nxt)[4] = (J & 1) ? x0 : x1;
-    if constexpr (J + 1 < kChunksPerUnit) read_x_frag(nxt, xrow, row, J + 1);
+    if constexpr (J + 1 < kChunksPerUnit) read_x_frag(nxt, xrow, J + 1);
     acc = mfma_chunk<J>(c[J], sv, cur, acc);
-    mfma_steps<J + 1>(c, sv, x0, x1, acc, xrow, row);
+    mfma_steps<J + 1>(c, sv, x0, x1, acc, xrow);
   }
 }
 
@@ -295,102 +266,62 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (P.active) {
     const int cl = P.lane & 15, grp = P.lane >> 4;
-    const bool row = cl < a.M;
-    const _Float16* xrow = xs + (row ? cl : 0) * xs_stride(P.S) + P.s * kUnitK + grp * 32;
+    const _Float16* xrow = xs + min(cl, a.M - 1) * xs_stride(P.S) + P.s * kUnitK + grp * 32;
     f16x8 x0[4], x1[4];
-    read_x_frag(x0, xrow, row, 0);
-    mfma_steps<0>(c, sv, x0, x1, acc, xrow, row);
+    read_x_frag(x0, xrow, 0);
+    mfma_steps<0>(c, sv, x0, x1, acc, xrow);
   }
   if (P.lane < 32) red[P.wave * 32 + P.lane] = acc;
   __syncthreads();
 
   // Wavefront t < CT finishes local tile t.  D layout: lane (grp, c) holds
   // rows 4grp..4grp+3 of column c; rows >= 8 are padding.
-  const bool fin = P.wave < CT && P.tile0 + P.wave < a.nt;
+  const bool fin = P.wave < CT && P.tile0 + P.wave < a.nt && P.lane < 32;
+  const int cl = P.lane & 15, grp = P.lane >> 4;
+  const int n = (P.tile0 + P.wave) * kTileCols + cl;
   f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (fin && P.lane < 32) {
+  if (fin)
     for (int s = 0; s < P.sw; ++s) tot += red[(P.wave * P.S + s) * 32 + P.lane];
-    if (a.ksplit > 1) {
-      float* dst = a.part + (static_cast<size_t>(blockIdx.y) * a.nt + P.tile0 + P.wave) * kPartFloats + 4 * P.lane;
+  if (a.ksplit > 1) {  // this split's partial sums; the split reduction finishes
+    if (fin && n < a.N) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) store_shared(dst + i, tot[i]);
-    }
-  }
-  if (!last_of_tile_group(a)) return;
-
-  __shared__ unsigned long long best[kMaxWaves][kMaxRows];
-  if (fin) {
-    const int cl = P.lane & 15, grp = P.lane >> 4;
-    if (a.ksplit > 1 && P.lane < 32) {
-      tot = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < a.ksplit; ++ks) {
-        const float* src = a.part + (static_cast<size_t>(ks) * a.nt + P.tile0 + P.wave) * kPartFloats + 4 * P.lane;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tot[i] += load_shared(src + i);
+      for (int i = 0; i < 4; ++i) {
+        const int m = grp * 4 + i;
+        if (m < a.M) a.part[(static_cast<size_t>(blockIdx.y) * a.M + m) * a.N + n] = tot[i];
       }
     }
-    const float g = *a.gptr;
-    const int n = (P.tile0 + P.wave) * kTileCols + cl;
-    unsigned long long key[4] = {0ull, 0ull, 0ull, 0ull};
+    return;
+  }
+
+  const float g = *a.gptr;
+  unsigned long long key[4] = {0ull, 0ull, 0ull, 0ull};
+  if (fin && n < a.N) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = grp * 4 + i;
       const float v = g * tot[i];
-      if (P.lane < 32 && n < a.N && m < a.M) {
+      if (m < a.M) {
         if (a.y) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(v);
-        key[i] = (static_cast<unsigned long long>(ordered_key(v)) << 32) |
-                 static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(n));
-      }
-    }
-    if (ARGMAX) {
-      // Largest key over the 16 columns of each row group (the larger key has
-      // the larger logit, or the same logit and the lower column).
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) {
-          const unsigned long long o = __shfl_xor(key[i], off, 16);
-          key[i] = o > key[i] ? o : key[i];
-        }
-      }
-      if (P.lane < 32 && cl == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) best[P.wave][grp * 4 + i] = key[i];
+        key[i] = argmax_key(v, n);
       }
     }
   }
   if (ARGMAX) {
+    // Largest key over the 16 columns of each row group, then over the
+    // workgroup's tiles: one candidate per row.
+    __shared__ unsigned long long best[kMaxWaves][kMaxRows];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = wave_max_key<16>(key[i]);
+    if (P.wave < CT && P.lane < 32 && cl == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) best[P.wave][grp * 4 + i] = key[i];
+    }
     __syncthreads();
-    // One candidate per row for the whole workgroup (a zero key loses to any real one).
     if (threadIdx.x < static_cast<unsigned>(a.M)) {
       unsigned long long k = 0ull;
-      for (int t = 0; t < CT; ++t)
-        if (P.tile0 + t < a.nt) k = best[t][threadIdx.x] > k ? best[t][threadIdx.x] : k;
+      for (int t = 0; t < CT; ++t) k = best[t][threadIdx.x] > k ? best[t][threadIdx.x] : k;
       a.cand[static_cast<size_t>(blockIdx.x) * a.M + threadIdx.x] = k;
     }
-  }
-}
-
-// Reduces the per-workgroup candidates: idx[m] = column of the largest key.
-__global__ __launch_bounds__(256) void argmax_reduce(const unsigned long long* cand, int groups, int M,
-                                                     int32_t* idx) {
-  __shared__ unsigned long long red[256];
-  for (int m = 0; m < M; ++m) {
-    unsigned long long k = 0ull;
-    for (int g = threadIdx.x; g < groups; g += blockDim.x) {
-      const unsigned long long v = cand[static_cast<size_t>(g) * M + m];
-      k = v > k ? v : k;
-    }
-    red[threadIdx.x] = k;
-    __syncthreads();
-    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
-      if (threadIdx.x < static_cast<unsigned>(off))
-        red[threadIdx.x] = red[threadIdx.x + off] > red[threadIdx.x] ? red[threadIdx.x + off] : red[threadIdx.x];
-      __syncthreads();
-    }
-    // No candidate at all (every logit NaN) leaves the all-ones index -1.
-    if (threadIdx.x == 0) idx[m] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(red[0] & 0xFFFFFFFFull));
-    __syncthreads();
   }
 }
 
@@ -407,8 +338,6 @@ size_t nvfp4_mfma_lds_bytes(int M, int S, int nw) {
          static_cast<size_t>(nw) * 32 * sizeof(f32x4);
 }
 
-size_t nvfp4_part_floats() { return kPartFloats; }
-
 // (engine, ct, nw, ksplit): nw = ct * S wavefronts cover S K spans of ct
 // tiles; the ksplit workgroups of a tile group must cover all K spans and
 // each must get at least one.
@@ -423,23 +352,34 @@ bool nvfp4_cfg_supported(const LaunchCfg& c, int M, int K, bool argmax) {
   return nvfp4_mfma_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
 }
 
-#define SKINNY_NVFP4_DISPATCH(CT)                                                                 \
-  if (cfg.ct == CT) {                                                                             \
-    if (cfg.engine == 0) return launch(nvfp4_valu_m1<CT>, grid, cfg.nw, 0, a, stream);           \
-    if (argmax) {                                                                                 \
-      hipError_t e = launch(nvfp4_mfma<CT, true>, grid, cfg.nw, lds, a, stream);                  \
-      if (e != hipSuccess) return e;                                                              \
-      hipLaunchKernelGGL(argmax_reduce, dim3(1), dim3(256), 0, stream, a.cand,                    \
-                         static_cast<int>(grid.x), M, idx);                                       \
-      return hipGetLastError();                                                                   \
-    }                                                                                             \
-    return launch(nvfp4_mfma<CT, false>, grid, cfg.nw, lds, a, stream);                          \
+#define SKINNY_NVFP4_DISPATCH(CT)                                                   \
+  if (cfg.ct == CT) {                                                               \
+    if (cfg.engine == 0) return launch(nvfp4_valu_m1<CT>, grid, cfg.nw, 0, a, stream); \
+    if (argmax && cfg.ksplit == 1) return launch(nvfp4_mfma<CT, true>, grid, cfg.nw, lds, a, stream); \
+    return launch(nvfp4_mfma<CT, false>, grid, cfg.nw, lds, a, stream);            \
   }
+
+namespace {
+
+hipError_t launch_gemm(const Nvfp4Args& a, const LaunchCfg& cfg, bool argmax, hipStream_t stream) {
+  const dim3 grid((a.nt + cfg.ct - 1) / cfg.ct, cfg.ksplit);
+  const size_t lds = nvfp4_mfma_lds_bytes(a.M, a.S, cfg.nw);
+  SKINNY_NVFP4_DISPATCH(1)
+  SKINNY_NVFP4_DISPATCH(2)
+  SKINNY_NVFP4_DISPATCH(4)
+  SKINNY_NVFP4_DISPATCH(8)
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+#undef SKINNY_NVFP4_DISPATCH
 
 hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y, int M, int K, int N,
                         const LaunchCfg& cfg, int32_t* idx, void* workspace, hipStream_t stream) {
   const Geometry geo = nvfp4_geometry(K, N);
-  const WorkspaceLayout wl = nvfp4_workspace_layout(cfg, M, K, N, idx != nullptr);
+  const bool argmax = idx != nullptr;
+  const WorkspaceLayout wl = nvfp4_workspace_layout(cfg, M, K, N, argmax);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   Nvfp4Args a;
   a.units = blob + kHeaderBytes;
@@ -454,16 +394,16 @@ hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y, int
   a.ksplit = cfg.ksplit;
   a.S = cfg.nw / cfg.ct;
   a.part = wl.part_bytes ? reinterpret_cast<float*>(ws + wl.part_off) : nullptr;
-  a.tile_cnt = wl.tile_cnt_bytes ? reinterpret_cast<uint32_t*>(ws + wl.tile_cnt_off) : nullptr;
-  a.cand = idx ? reinterpret_cast<unsigned long long*>(ws + wl.keys_off) : nullptr;
-  const bool argmax = idx != nullptr;
-  const dim3 grid((geo.nt + cfg.ct - 1) / cfg.ct, cfg.ksplit);
-  const size_t lds = nvfp4_mfma_lds_bytes(M, a.S, cfg.nw);
-  SKINNY_NVFP4_DISPATCH(1)
-  SKINNY_NVFP4_DISPATCH(2)
-  SKINNY_NVFP4_DISPATCH(4)
-  SKINNY_NVFP4_DISPATCH(8)
-  return hipErrorInvalidValue;
+  a.cand = argmax ? reinterpret_cast<unsigned long long*>(ws + wl.keys_off) : nullptr;
+  hipError_t e = launch_gemm(a, cfg, argmax, stream);
+  if (e != hipSuccess) return e;
+  int groups = (geo.nt + cfg.ct - 1) / cfg.ct;
+  if (cfg.ksplit > 1) {
+    e = launch_finalize(a.part, cfg.ksplit, M, N, a.gptr, y, a.cand, stream);
+    if (e != hipSuccess) return e;
+    groups = finalize_groups(N);
+  }
+  return argmax ? launch_argmax_reduce(a.cand, groups, M, idx, stream) : hipSuccess;
 }
 
 }  // namespace skinny

@@ -1,0 +1,108 @@
+// Second-pass kernels of the skinny GEMM: the K-split reduction and the
+// lm_head argmax over workgroup candidates.
+//
+// When K is split over several workgroups, each one stores its fp32 partial
+// sums with plain stores, part[split][m][n], and exits.  finalize_splits then
+// adds the splits in split order (so results never depend on timing),
+// applies the per-tensor scale and rounds to fp16.  For the lm_head it also
+// takes, per row and per block of 256 columns, the largest logit as one
+// ordered 64-bit key (logit bits above the inverted column, so a larger key is
+// a larger logit or the same logit at a lower column); argmax_reduce then
+// takes the largest key per row over all blocks.  The argmax is taken on the
+// fp32 logits before fp16 rounding (author's post, section "This is a server,
+// not a GEMM screenshot": the drafter proposes greedy, local-argmax tokens).
+#include <hip/hip_runtime.h>
+
+#include "common.cuh"
+#include "internal.h"
+
+namespace skinny {
+namespace {
+
+constexpr int kFinalizeThreads = 256;
+
+// Block (x, m): columns 256x .. 256x+255 of row m.  Each thread adds its
+// column's partials in split order.
+template <bool ARGMAX>
+__global__ __launch_bounds__(kFinalizeThreads) void finalize_splits(const float* part, int ksplit, int M, int N,
+                                                                    const float* gptr, _Float16* y,
+                                                                    unsigned long long* cand) {
+  __shared__ unsigned long long best[kFinalizeThreads / 64];
+  const int n = blockIdx.x * kFinalizeThreads + threadIdx.x;
+  const int m = blockIdx.y;
+  unsigned long long key = 0ull;
+  if (n < N) {
+    const float* p = part + static_cast<size_t>(m) * N + n;
+    const size_t stride = static_cast<size_t>(M) * N;
+    // Batches of eight splits: the loads of a batch are all issued before the
+    // first add, so a call with ksplit <= 8 waits for memory only once.
+    float s = 0.0f;
+    for (int k0 = 0; k0 < ksplit; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = k0 + i < ksplit ? p[(k0 + i) * stride] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (k0 + i < ksplit) s += v[i];
+    }
+    const float v = (gptr ? *gptr : 1.0f) * s;
+    if (y) y[static_cast<size_t>(m) * N + n] = static_cast<_Float16>(v);
+    key = argmax_key(v, n);
+  }
+  if (ARGMAX) {
+    key = wave_max_key(key);
+    if ((threadIdx.x & 63) == 0) best[threadIdx.x >> 6] = key;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long k = 0ull;
+      for (int w = 0; w < kFinalizeThreads / 64; ++w) k = best[w] > k ? best[w] : k;
+      cand[static_cast<size_t>(blockIdx.x) * M + m] = k;
+    }
+  }
+}
+
+// idx[m] = column of the largest candidate key of row m.
+__global__ __launch_bounds__(256) void argmax_reduce(const unsigned long long* cand, int groups, int M,
+                                                     int32_t* idx) {
+  __shared__ unsigned long long red[256];
+  for (int m = 0; m < M; ++m) {
+    unsigned long long k = 0ull;
+    for (int g = threadIdx.x; g < groups; g += blockDim.x) {
+      const unsigned long long v = cand[static_cast<size_t>(g) * M + m];
+      k = v > k ? v : k;
+    }
+    red[threadIdx.x] = k;
+    __syncthreads();
+    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
+      if (threadIdx.x < static_cast<unsigned>(off))
+        red[threadIdx.x] = red[threadIdx.x + off] > red[threadIdx.x] ? red[threadIdx.x + off] : red[threadIdx.x];
+      __syncthreads();
+    }
+    // No candidate at all (every logit NaN) leaves the all-ones index -1.
+    if (threadIdx.x == 0) idx[m] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(red[0] & 0xFFFFFFFFull));
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+int finalize_groups(int N) { return (N + kFinalizeThreads - 1) / kFinalizeThreads; }
+
+hipError_t launch_finalize(const float* part, int ksplit, int M, int N, const float* gptr, uint16_t* y,
+                           unsigned long long* cand, hipStream_t stream) {
+  _Float16* yh = reinterpret_cast<_Float16*>(y);
+  const dim3 grid(finalize_groups(N), M), block(kFinalizeThreads);
+  if (cand)
+    hipLaunchKernelGGL(finalize_splits<true>, grid, block, 0, stream, part, ksplit, M, N, gptr, yh, cand);
+  else
+    hipLaunchKernelGGL(finalize_splits<false>, grid, block, 0, stream, part, ksplit, M, N, gptr, yh, cand);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_reduce(const unsigned long long* cand, int groups, int M, int32_t* idx,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(argmax_reduce, dim3(1), dim3(256), 0, stream, cand, groups, M, idx);
+  return hipGetLastError();
+}
+
+}  // namespace skinny

@@ -28,7 +28,7 @@ import sys
 import numpy as np
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-KERNEL_SOURCES = ("common.cuh", "internal.h", "nvfp4_gemm.hip", "fp8_gemm.hip")
+KERNEL_SOURCES = ("common.cuh", "internal.h", "nvfp4_gemm.hip", "fp8_gemm.hip", "reduce.hip")
 
 
 def sources_sha256():
@@ -40,8 +40,24 @@ def sources_sha256():
     return h.hexdigest()
 
 
+def _demangle(name):
+    """Readable name of a mangled kernel symbol of this package (name and template
+    arguments only; the system demangler may not know the _Float16 mangling)."""
+    import re
+    m = re.match(r"_ZN6skinny12_GLOBAL__N_1(\d+)", name)
+    if not m:
+        return name
+    rest = name[m.end():]
+    ident, rest = rest[:int(m.group(1))], rest[int(m.group(1)):]
+    args = []
+    if rest.startswith("I"):
+        for kind, val in re.findall(r"L([bi])(\d+)E", rest[:rest.index("EE") + 1] if "EE" in rest else rest):
+            args.append(("true" if val == "1" else "false") if kind == "b" else val)
+    return f"skinny::{ident}" + (f"<{', '.join(args)}>" if args else "") + "()"
+
+
 def _short(name):
-    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    name = _demangle(name).replace("(anonymous namespace)::", "").replace("void ", "")
     return name.split("(")[0][:48]
 
 

@@ -73,7 +73,10 @@ enum {
  *            On success *out_bytes is set to the blob size.
  *
  * The blob starts with a 256-byte header (magic "SKN4", version, K, N, g)
- * followed by the code tiles and the scale groups.  The caller copies the
+ * followed by 9 KiB units, one per 16 output columns x 1024 K (K padded with
+ * zero codes to a multiple of 1024): eight 1 KiB code chunks, then the
+ * unit's 1 KiB of scales, ordered so that each lane of a wavefront loads
+ * 16 contiguous bytes of every chunk.  The caller copies the
  * blob as-is into a device buffer it owns and passes that to nvfp4_gemm or
  * lm_head_gemm_argmax.  Returns SKINNY_ESIZE if out is non-NULL and
  * *out_bytes is smaller than the blob.
@@ -88,10 +91,10 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float g,
  *   x         : device, fp16 [M][K] row-major.
  *   y         : device, fp16 [M][N] row-major (written, never read).
  *   M         : 1..8.
- *   workspace : device buffer of at least skinny_workspace_bytes(0, M, K, N)
- *               bytes, zero-filled before its first use; every call leaves
- *               its counters zero again.  May be NULL when that size is 0.
- *               Calls that share one workspace must not overlap in time.
+ *   workspace : device scratch buffer of at least
+ *               skinny_workspace_bytes(0, M, K, N) bytes (any contents; the
+ *               call writes every byte it reads).  May be NULL when that size
+ *               is 0.  Calls that share one workspace must not overlap in time.
  *   stream    : HIP stream the kernel is enqueued on (0 = null stream).
  * ------------------------------------------------------------------------- */
 int nvfp4_gemm(const void* w_packed, const uint16_t* x, uint16_t* y,
@@ -123,9 +126,9 @@ int fp8_gemm(const uint8_t* w, const float* block_scales, const uint16_t* x,
  *               g * sum_k x[m][k] * e2m1 * e4m3 is the row maximum.  The
  *               comparison uses the fp32 logits before any fp16 rounding.
  *   logits    : device fp16 [M][N] or NULL (then no logits are written).
- *   workspace : at least skinny_workspace_bytes(2, M, K, N) bytes,
- *               zero-filled before first use, left zero-filled by each call.
- *               Calls that share one workspace must not overlap in time.
+ *   workspace : scratch of at least skinny_workspace_bytes(2, M, K, N) bytes
+ *               (any contents).  Calls that share one workspace must not
+ *               overlap in time.
  * ------------------------------------------------------------------------- */
 int lm_head_gemm_argmax(const void* w_packed, const uint16_t* x, int32_t* idx,
                         uint16_t* logits, int M, int K, int N, void* workspace,
@@ -157,10 +160,14 @@ int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales);
  *   engine : 0 = VALU dot2 engine (nvfp4_gemm with M == 1 only),
  *            1 = MFMA 16x16x32 f16 engine (all calls, M = 1..8)
  *   ct     : 16-column tiles per workgroup: 1, 2, 4 or 8
- *   nw     : wavefronts per workgroup, which split its work: 1..8
- *   ksplit : workgroups that split K (1 = none); partial sums then go
- *            through the workspace, whose size skinny_workspace_bytes_config
- *            gives for the same choice
+ *   nw     : wavefronts per workgroup, ct * S with S = 1..16/ct: the
+ *            workgroup covers ct tiles x S consecutive K spans (1024 K for
+ *            NVFP4, 512 K for FP8), one span of one tile per wavefront
+ *   ksplit : workgroups that share a tile group along K; with P spans in K
+ *            it must satisfy ksplit * S >= P and (ksplit - 1) * S < P.
+ *            With ksplit > 1 each workgroup stores fp32 partial sums in
+ *            the workspace (size from skinny_workspace_bytes_config for the
+ *            same choice) and a second kernel adds them in split order
  * A combination that is not built (or whose LDS need exceeds the CU)
  * returns SKINNY_EINVAL.
  * ------------------------------------------------------------------------- */

@@ -36,9 +36,9 @@ def _log(msg):
 
 
 def _ws(op, M, K, N):
-    """Zero-filled workspace for the library's default kernel choice (None if none is needed)."""
+    """Junk-filled workspace for the library's default kernel choice (None if none is needed)."""
     n = sk.workspace_bytes(op, M, K, N)
-    return torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None
+    return torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
 
 
 @pytest.mark.parametrize("name", ["up", "gate_up", "down"])
@@ -56,7 +56,7 @@ def test_nvfp4_full_shape_sampled(name):
         y2 = torch.empty_like(y)
         sk.nvfp4_gemm(blob, x, y2, workspace=ws)
         torch.cuda.synchronize()
-        # the second call reuses the workspace: its arrival counters must be back at zero
+        # the second call reuses the workspace left behind by the first
         assert torch.equal(y, y2), "not deterministic"
         got = y.float().cpu().numpy()[:, cols]
         ref = oracle.nvfp4_gemm(case["x"][:M], case["codes"], case["scales"], case["g"], cols=cols)

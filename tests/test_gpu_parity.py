@@ -42,8 +42,9 @@ def cfgs(engine, K, unit_k=1024, splits=(1, 2, 3), cts=(1, 2, 4, 8)):
 
 
 def ws_for(op, M, K, N, config):
+    """Workspace for a call, filled with junk: the library must not rely on its contents."""
     n = sk.workspace_bytes(op, M, K, N, config)
-    return torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None
+    return torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
 
 
 def dev(a):
