@@ -17,7 +17,7 @@ from ._lib import lib
 
 OK, EINVAL, ESHAPE, EALIGN, ESIZE, EHIP, EFORMAT = range(7)
 OP_NVFP4, OP_FP8, OP_LM_HEAD = 0, 1, 2
-ENGINE_VALU, ENGINE_MFMA = 0, 1
+ENGINE_VALU, ENGINE_MFMA, ENGINE_STREAM = 0, 1, 2
 
 
 class SkinnyError(RuntimeError):
@@ -61,6 +61,11 @@ def workspace_bytes(op, M, K, N, config=None):
     if config is None:
         return int(lib().skinny_workspace_bytes(op, M, K, N))
     return int(lib().skinny_workspace_bytes_config(op, M, K, N, *config))
+
+
+def config_supported(op, M, K, N, config):
+    """True if the explicit kernel choice (engine, ct, nw, ksplit) is supported for this op and shape."""
+    return bool(lib().skinny_config_supported(op, M, K, N, *config))
 
 
 def _workspace(workspace, need, where):

@@ -22,6 +22,7 @@ def _declare(lib):
         "lm_head_gemm_argmax_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P,
                                                c_int, c_int, c_int, c_int]),
         "skinny_workspace_bytes_config": (c_size_t, [c_int] * 8),
+        "skinny_config_supported": (c_int, [c_int] * 8),
         "nvfp4_quantize": (c_int, [P, c_int, c_int, P, P, ctypes.POINTER(c_float)]),
         "fp8_quantize": (c_int, [P, c_int, c_int, P, P]),
         "skinny_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
@@ -46,4 +47,5 @@ def lib():
 
 EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp4_quantize",
             "fp8_quantize", "skinny_workspace_bytes", "skinny_strerror", "nvfp4_gemm_config",
-            "fp8_gemm_config", "lm_head_gemm_argmax_config", "skinny_workspace_bytes_config")
+            "fp8_gemm_config", "lm_head_gemm_argmax_config", "skinny_workspace_bytes_config",
+            "skinny_config_supported")

@@ -95,16 +95,17 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 // Kernel choice made by the library when the caller does not pick one; each
 // rule is the fastest kernel choice measured on the decode shapes.
 //
-// Up to four rows: one tile per workgroup and as many K spans (units) per
-// workgroup as the 16-wavefront limit allows; K beyond that is split over
-// workgroups, evened out so that every split gets the same spans.  This is
-// the VALU engine for a plain M = 1 GEMV and the MFMA engine otherwise.
+// NVFP4 GEMV (M = 1, no argmax): VALU engine, one tile per workgroup and as
+// many K spans (units) per workgroup as the 16-wavefront limit allows; K
+// beyond that is split over workgroups, evened out so that every split gets
+// the same spans.
 //
-// Five to eight rows (MFMA): four tiles per workgroup (fewer when N has fewer
-// tiles) and the fewest K spans per workgroup that keep the K split at most
-// nine ways.  The x slice a workgroup stages in LDS grows with M and with its
-// spans; short workgroups keep it small, so that more of them fit on a CU,
-// and the split reduction stays a single short pass.
+// Other NVFP4 calls: the streaming MFMA engine whenever all of x fits in LDS
+// (K up to 9 spans).  Otherwise, and for FP8: up to four rows, whole-K
+// workgroups as above (MFMA); five to eight rows, four tiles per workgroup
+// and the fewest K spans per workgroup that keep the K split at most nine
+// ways (the x slice a workgroup stages in LDS grows with M and with its
+// spans; short workgroups keep it small, so that more of them fit on a CU).
 LaunchCfg pick_whole_k_cfg(int engine, int ku) {
   int s = std::min(ku, kMaxWaves);
   const int ksplit = (ku + s - 1) / s;
@@ -121,10 +122,32 @@ LaunchCfg pick_short_cfg(int ku, int nt) {
   return LaunchCfg{1, ct, ct * s, ksplit};
 }
 
+// Streaming engine (all of x in LDS, whole tiles per wavefront, no K split)
+// whenever x fits: two 8-wavefront workgroups per CU when two copies of x
+// fit, else one workgroup of 12 (16 for vocabulary-sized N, whose tiles
+// outnumber the wavefront slots).
+bool pick_stream_cfg(int M, int K, int N, LaunchCfg* out) {
+  const LaunchCfg two{2, 2, 8, 1};
+  if (nvfp4_cfg_supported(two, M, K, false)) {
+    *out = two;
+    return true;
+  }
+  const int nt = (N + kTileCols - 1) / kTileCols;
+  const LaunchCfg one{2, 1, nt >= 4096 ? 16 : 12, 1};
+  if (nvfp4_cfg_supported(one, M, K, false)) {
+    *out = one;
+    return true;
+  }
+  return false;
+}
+
 LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax) {
   const Geometry g = nvfp4_geometry(K, N);
+  if (M == 1 && !argmax) return pick_whole_k_cfg(0, g.ku);
+  LaunchCfg c;
+  if (pick_stream_cfg(M, K, N, &c)) return c;
   if (M > 4) return pick_short_cfg(g.ku, g.nt);
-  return pick_whole_k_cfg(M == 1 && !argmax ? 0 : 1, g.ku);
+  return pick_whole_k_cfg(1, g.ku);
 }
 
 LaunchCfg default_fp8_cfg(int M, int K, int N) {
@@ -153,6 +176,18 @@ int check_workspace(const void* ws, size_t have, size_t need) {
 
 namespace skinny {
 
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 Geometry nvfp4_geometry(int K, int N) {
   Geometry g;
   g.ku = (K + kUnitK - 1) / kUnitK;
@@ -170,7 +205,8 @@ WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N
   WorkspaceLayout w{};
   size_t off = 0;
   if (argmax) {
-    const size_t groups = cfg.ksplit > 1 ? finalize_groups(N) : (g.nt + cfg.ct - 1) / cfg.ct;
+    const size_t groups = cfg.engine == 2 ? kMaxStreamGroups
+                          : cfg.ksplit > 1 ? finalize_groups(N) : (g.nt + cfg.ct - 1) / cfg.ct;
     w.keys_off = off;
     w.keys_bytes = groups * M * 8;
     off = align256(off + w.keys_bytes);
@@ -221,6 +257,17 @@ size_t skinny_workspace_bytes_config(int op, int M, int K, int N, int engine, in
     case 0: return nvfp4_cfg_supported(c, M, K, false) ? nvfp4_workspace_layout(c, M, K, N, false).total : 0;
     case 1: return fp8_cfg_supported(c, M, K) ? fp8_workspace_layout(c, M, K, N).total : 0;
     case 2: return nvfp4_cfg_supported(c, M, K, true) ? nvfp4_workspace_layout(c, M, K, N, true).total : 0;
+    default: return 0;
+  }
+}
+
+int skinny_config_supported(int op, int M, int K, int N, int engine, int ct, int nw, int ksplit) {
+  if (check_shape(M, K, N)) return 0;
+  const LaunchCfg c{engine, ct, nw, ksplit};
+  switch (op) {
+    case 0: return nvfp4_cfg_supported(c, M, K, false) ? 1 : 0;
+    case 1: return fp8_cfg_supported(c, M, K) ? 1 : 0;
+    case 2: return nvfp4_cfg_supported(c, M, K, true) ? 1 : 0;
     default: return 0;
   }
 }

@@ -59,10 +59,10 @@ Geometry nvfp4_geometry(int K, int N);
 
 // Launch parameters picked by the host for one call.
 struct LaunchCfg {
-  int engine;  // 0 = VALU dot2 (M = 1 only), 1 = MFMA 16x16x32 f16
-  int ct;      // column tiles (of 16) per workgroup
-  int nw;      // wavefronts per workgroup (1..16) = ct * K spans per workgroup
-  int ksplit;  // workgroups that split K (1 = no split)
+  int engine;  // 0 = VALU dot2 (M = 1 only), 1 = MFMA 16x16x32 f16, 2 = streaming MFMA
+  int ct;      // engines 0, 1: column tiles (of 16) per workgroup; engine 2: workgroups per CU
+  int nw;      // wavefronts per workgroup (1..16); engines 0, 1: ct * K spans per workgroup
+  int ksplit;  // workgroups that split K (1 = no split; engine 2 never splits)
 };
 constexpr int kMaxWaves = 16;
 constexpr size_t kMaxLdsBytes = 160 * 1024;
@@ -87,6 +87,16 @@ hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x,
 bool nvfp4_cfg_supported(const LaunchCfg& cfg, int M, int K, bool argmax);
 bool fp8_cfg_supported(const LaunchCfg& cfg, int M, int K);
 size_t nvfp4_mfma_lds_bytes(int M, int S, int nw);
+
+// Streaming engine: LDS bytes per workgroup (all of x plus the argmax
+// scratch) and the grid size, at most kMaxStreamGroups workgroups.
+constexpr int kMaxStreamGroups = 1024;
+constexpr int kMaxStreamSpans = 9;
+size_t nvfp4_stream_lds_bytes(int M, int K, int nw);
+int nvfp4_stream_groups(const LaunchCfg& cfg, int N);
+
+// Compute units of the current device (256 if it cannot be queried).
+int device_cu_count();
 
 // Second pass of a K split (reduce.hip): adds part[split][m][n] over the
 // splits in order, scales by *gptr (1 if null) and writes fp16 y (if non-null)

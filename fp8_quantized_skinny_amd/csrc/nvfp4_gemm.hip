@@ -43,6 +43,8 @@
 // the indices.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "common.cuh"
 #include "internal.h"
 
@@ -325,6 +327,158 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming MFMA engine (M = 1..8, K small enough for x to sit in LDS).
+// ---------------------------------------------------------------------------
+// One workgroup per CU slot copies all of x into LDS once; each wavefront then
+// owns whole column tiles (tile t = blockIdx.x + gridDim.x * (wave + nw * i))
+// and walks each tile's K spans in order, with the next unit's nine loads
+// issued before the current unit is contracted (two units in flight per
+// wavefront).  Every tile's sum stays in one wavefront's registers, so there
+// is no K split and no second pass; the price is more VGPRs per wavefront
+// (two units) and an x copy per workgroup instead of per tile group.
+struct Unit {
+  u32x4 c[kChunksPerUnit];
+  u32x4 sv;
+};
+
+__device__ __forceinline__ void load_unit(Unit& u, const uint8_t* p) {
+  u.sv = load16(p + kChunksPerUnit * kChunkBytes);
+#pragma unroll
+  for (int j = 0; j < kChunksPerUnit; ++j) u.c[j] = load16(p + j * kChunkBytes);
+}
+
+// Copies x[m][0..K) for m < M into LDS rows of stride RS halves, zero past K.
+__device__ void stage_x_all(const Nvfp4Args& a, _Float16* xs, int RS, int wave, int nw, int lane) {
+  const int kp = a.ku * kUnitK;
+  if (a.K < kp) {
+    for (int i = threadIdx.x; i < a.M * RS; i += blockDim.x)
+      if (i % RS >= a.K) xs[i] = static_cast<_Float16>(0.0f);
+  }
+  const int blocks_per_row = kp / 512;  // 1 KiB blocks
+  const int nblocks = a.M * blocks_per_row;
+  for (int b = wave; b < nblocks; b += nw) {
+    const int m = b / blocks_per_row, blk = b % blocks_per_row;
+    const int col = blk * 512 + lane * 8;
+    if (col < a.K)
+      __builtin_amdgcn_global_load_lds(a.x + static_cast<size_t>(m) * a.K + col, xs + m * RS + blk * 512, 16, 0, 0);
+  }
+}
+
+// The eight chunks of a unit with one set of A fragments, read from LDS just
+// before use (the streaming kernel spends its registers on the second unit).
+template <int J>
+__device__ __forceinline__ void mfma_unit_lean(const Unit& U, f32x4& acc, const _Float16* xrow) {
+  if constexpr (J < kChunksPerUnit) {
+    f16x8 xa[4];
+    read_x_frag(xa, xrow, J);
+    acc = mfma_chunk<J>(U.c[J], U.sv, xa, acc);
+    mfma_unit_lean<J + 1>(U, acc, xrow);
+  }
+}
+
+// Per-wavefront state of the streaming kernel.
+struct StreamCtx {
+  const Nvfp4Args* a;
+  const _Float16* xbase;  // this lane's LDS x row (row min(c, M-1)), fragment group offset included
+  size_t tile_stride;     // bytes from one of this wavefront's tiles to its next
+  unsigned long long* best;  // LDS [kMaxRows] running argmax keys of this wavefront
+  int t0, step, ntiles, lane;
+  float g;
+};
+
+// Unit J of this wavefront's tile `ti`, whose unit 0 (this lane's 16 bytes)
+// is at `base`.  All buffer choices are compile-time: first the loads of the
+// wavefront's next unit go out into the other buffer, then unit J is
+// contracted.  After the tile's last span the tile is stored and its logits
+// are folded into the wavefront's running argmax keys (kept in LDS, not in
+// registers, which the two units in flight already fill).
+template <int KU, int J, int PAR, bool ARGMAX>
+__device__ __forceinline__ void stream_units(const StreamCtx& c, Unit& A, Unit& B, int ti, const uint8_t* base,
+                                             f32x4& acc) {
+  if constexpr (J < KU) {
+    Unit& cur = PAR ? B : A;
+    Unit& nxt = PAR ? A : B;
+    if constexpr (J + 1 < KU)
+      load_unit(nxt, base + (J + 1) * kUnitBytes);
+    else if (ti + 1 < c.ntiles)
+      load_unit(nxt, base + c.tile_stride);
+    // Keep the scheduler from hoisting work across units: it would start later
+    // units' LDS reads and conversions early and run out of registers.
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_unit_lean<0>(cur, acc, c.xbase + J * kUnitK);
+    __builtin_amdgcn_sched_barrier(0);
+    stream_units<KU, J + 1, 1 - PAR, ARGMAX>(c, A, B, ti, base, acc);
+  } else {
+    const Nvfp4Args& a = *c.a;
+    const int cl = c.lane & 15, grp = c.lane >> 4;
+    const int n = (c.t0 + ti * c.step) * kTileCols + cl;
+    const bool col_ok = c.lane < 32 && n < a.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = grp * 4 + i;
+      const bool ok = col_ok && m < a.M;
+      const float v = c.g * acc[i];
+      if (ok && a.y) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(v);
+      if (ARGMAX) {
+        const unsigned long long k = wave_max_key<16>(ok ? argmax_key(v, n) : 0ull);
+        if (c.lane < 32 && cl == 0) c.best[grp * 4 + i] = k > c.best[grp * 4 + i] ? k : c.best[grp * 4 + i];
+      }
+    }
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+template <int KU, bool ARGMAX>
+__global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_stream(Nvfp4Args a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int RS = KU * kUnitK + 8;
+  _Float16* xs = reinterpret_cast<_Float16*>(lds);
+  unsigned long long* best = reinterpret_cast<unsigned long long*>(lds + ((a.M * RS * 2 + 15) & ~15));  // [nw][8]
+
+  StreamCtx c;
+  c.a = &a;
+  c.lane = lane;
+  c.step = gridDim.x * nw;
+  c.t0 = blockIdx.x + gridDim.x * wave;
+  c.ntiles = c.t0 < a.nt ? (a.nt - 1 - c.t0) / c.step + 1 : 0;
+  c.tile_stride = static_cast<size_t>(c.step) * KU * kUnitBytes;
+  c.g = *a.gptr;
+  c.xbase = xs + min(lane & 15, a.M - 1) * RS + (lane >> 4) * 32;
+  c.best = best + wave * kMaxRows;
+
+  stage_x_all(a, xs, RS, wave, nw, lane);
+  if (ARGMAX && lane < kMaxRows) c.best[lane] = 0ull;
+  Unit A, B;
+  const uint8_t* base = a.units + static_cast<size_t>(c.t0) * KU * kUnitBytes + lane * 16;
+  if (c.ntiles > 0) load_unit(A, base);
+  __syncthreads();
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Tiles in pairs, so that every unit's buffer is fixed at compile time
+  // (the wavefront's unit u lives in A when u is even): with odd KU the
+  // second tile of a pair starts in B.
+  for (int ti = 0; ti < c.ntiles; ti += 2) {
+    stream_units<KU, 0, 0, ARGMAX>(c, A, B, ti, base, acc);
+    base += c.tile_stride;
+    if (ti + 1 < c.ntiles) stream_units<KU, 0, KU % 2, ARGMAX>(c, A, B, ti + 1, base, acc);
+    base += c.tile_stride;
+  }
+
+  if (ARGMAX) {
+    // Largest key per row over the workgroup's wavefronts.
+    __syncthreads();
+    if (threadIdx.x < static_cast<unsigned>(a.M)) {
+      unsigned long long k = 0ull;
+      for (int w = 0; w < nw; ++w) k = best[w * kMaxRows + threadIdx.x] > k ? best[w * kMaxRows + threadIdx.x] : k;
+      a.cand[static_cast<size_t>(blockIdx.x) * a.M + threadIdx.x] = k;
+    }
+  }
+}
+
 template <typename Kern>
 hipError_t launch(Kern k, dim3 grid, int nw, size_t lds, const Nvfp4Args& a, hipStream_t stream) {
   hipLaunchKernelGGL(k, grid, dim3(nw * 64), lds, stream, a);
@@ -332,6 +486,19 @@ hipError_t launch(Kern k, dim3 grid, int nw, size_t lds, const Nvfp4Args& a, hip
 }
 
 }  // namespace
+
+size_t nvfp4_stream_lds_bytes(int M, int K, int nw) {
+  const int ku = (K + kUnitK - 1) / kUnitK;
+  return ((static_cast<size_t>(M) * (ku * kUnitK + 8) * 2 + 15) & ~static_cast<size_t>(15)) +
+         static_cast<size_t>(nw) * kMaxRows * 8;
+}
+
+int nvfp4_stream_groups(const LaunchCfg& c, int N) {
+  const int nt = (N + kTileCols - 1) / kTileCols;
+  const int per_wg = c.nw;
+  const int want = (nt + per_wg - 1) / per_wg;
+  return std::max(1, std::min({want, device_cu_count() * c.ct, kMaxStreamGroups}));
+}
 
 size_t nvfp4_mfma_lds_bytes(int M, int S, int nw) {
   return ((static_cast<size_t>(M) * (S * kUnitK + 8) * 2 + 15) & ~static_cast<size_t>(15)) +
@@ -342,6 +509,9 @@ size_t nvfp4_mfma_lds_bytes(int M, int S, int nw) {
 // tiles; the ksplit workgroups of a tile group must cover all K spans and
 // each must get at least one.
 bool nvfp4_cfg_supported(const LaunchCfg& c, int M, int K, bool argmax) {
+  if (c.engine == 2)  // streaming: ct = workgroups per CU (1 or 2), no K split, K <= 9 spans
+    return (c.ct == 1 || c.ct == 2) && c.nw >= 1 && c.nw <= kMaxWaves && c.ksplit == 1 &&
+           (K + kUnitK - 1) / kUnitK <= kMaxStreamSpans && nvfp4_stream_lds_bytes(M, K, c.nw) * c.ct <= kMaxLdsBytes;
   const bool ct_ok = c.ct == 1 || c.ct == 2 || c.ct == 4 || c.ct == 8;
   if (!ct_ok || c.nw < 1 || c.nw > kMaxWaves || c.nw % c.ct != 0 || c.ksplit < 1) return false;
   const int ku = (K + kUnitK - 1) / kUnitK;
@@ -362,6 +532,27 @@ bool nvfp4_cfg_supported(const LaunchCfg& c, int M, int K, bool argmax) {
 namespace {
 
 hipError_t launch_gemm(const Nvfp4Args& a, const LaunchCfg& cfg, bool argmax, hipStream_t stream) {
+  if (cfg.engine == 2) {
+    const dim3 grid(nvfp4_stream_groups(cfg, a.N));
+    const size_t lds = nvfp4_stream_lds_bytes(a.M, a.K, cfg.nw);
+    switch (a.ku) {
+#define SKINNY_STREAM_KU(KU) \
+  case KU:                   \
+    return argmax ? launch(nvfp4_stream<KU, true>, grid, cfg.nw, lds, a, stream) : launch(nvfp4_stream<KU, false>, grid, cfg.nw, lds, a, stream);
+      SKINNY_STREAM_KU(1)
+      SKINNY_STREAM_KU(2)
+      SKINNY_STREAM_KU(3)
+      SKINNY_STREAM_KU(4)
+      SKINNY_STREAM_KU(5)
+      SKINNY_STREAM_KU(6)
+      SKINNY_STREAM_KU(7)
+      SKINNY_STREAM_KU(8)
+      SKINNY_STREAM_KU(9)
+#undef SKINNY_STREAM_KU
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
   const dim3 grid((a.nt + cfg.ct - 1) / cfg.ct, cfg.ksplit);
   const size_t lds = nvfp4_mfma_lds_bytes(a.M, a.S, cfg.nw);
   SKINNY_NVFP4_DISPATCH(1)
@@ -397,7 +588,7 @@ hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y, int
   a.cand = argmax ? reinterpret_cast<unsigned long long*>(ws + wl.keys_off) : nullptr;
   hipError_t e = launch_gemm(a, cfg, argmax, stream);
   if (e != hipSuccess) return e;
-  int groups = (geo.nt + cfg.ct - 1) / cfg.ct;
+  int groups = cfg.engine == 2 ? nvfp4_stream_groups(cfg, N) : (geo.nt + cfg.ct - 1) / cfg.ct;
   if (cfg.ksplit > 1) {
     e = launch_finalize(a.part, cfg.ksplit, M, N, a.gptr, y, a.cand, stream);
     if (e != hipSuccess) return e;

@@ -21,33 +21,41 @@ namespace {
 
 constexpr int kFinalizeThreads = 256;
 
-// Block (x, m): columns 256x .. 256x+255 of row m.  Each thread adds its
-// column's partials in split order.
-template <bool ARGMAX>
+// Block (x, m): columns 1024x .. 1024x+1023 of row m, four consecutive
+// columns per thread (one 16-byte load per split).  Each thread adds its
+// columns' partials in split order.  N must be a multiple of 4 (the caller
+// uses the one-column variant otherwise).
+template <bool ARGMAX, int COLS>
 __global__ __launch_bounds__(kFinalizeThreads) void finalize_splits(const float* part, int ksplit, int M, int N,
                                                                     const float* gptr, _Float16* y,
                                                                     unsigned long long* cand) {
+  typedef float vecf __attribute__((ext_vector_type(COLS)));
   __shared__ unsigned long long best[kFinalizeThreads / 64];
-  const int n = blockIdx.x * kFinalizeThreads + threadIdx.x;
+  const int n0 = (blockIdx.x * kFinalizeThreads + threadIdx.x) * COLS;
   const int m = blockIdx.y;
   unsigned long long key = 0ull;
-  if (n < N) {
-    const float* p = part + static_cast<size_t>(m) * N + n;
+  if (n0 < N) {
+    const float* p = part + static_cast<size_t>(m) * N + n0;
     const size_t stride = static_cast<size_t>(M) * N;
     // Batches of eight splits: the loads of a batch are all issued before the
     // first add, so a call with ksplit <= 8 waits for memory only once.
-    float s = 0.0f;
+    vecf s = vecf(0.0f);
     for (int k0 = 0; k0 < ksplit; k0 += 8) {
-      float v[8];
+      vecf v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = k0 + i < ksplit ? p[(k0 + i) * stride] : 0.0f;
+      for (int i = 0; i < 8; ++i) v[i] = k0 + i < ksplit ? *reinterpret_cast<const vecf*>(p + (k0 + i) * stride) : vecf(0.0f);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (k0 + i < ksplit) s += v[i];
     }
-    const float v = (gptr ? *gptr : 1.0f) * s;
-    if (y) y[static_cast<size_t>(m) * N + n] = static_cast<_Float16>(v);
-    key = argmax_key(v, n);
+    const float g = gptr ? *gptr : 1.0f;
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) {
+      const float v = g * s[c];
+      if (y) y[static_cast<size_t>(m) * N + n0 + c] = static_cast<_Float16>(v);
+      const unsigned long long k = argmax_key(v, n0 + c);
+      key = k > key ? k : key;
+    }
   }
   if (ARGMAX) {
     key = wave_max_key(key);
@@ -86,16 +94,27 @@ __global__ __launch_bounds__(256) void argmax_reduce(const unsigned long long* c
 
 }  // namespace
 
-int finalize_groups(int N) { return (N + kFinalizeThreads - 1) / kFinalizeThreads; }
+// Four columns per thread when N allows it, else one.
+int finalize_cols(int N) { return N % 4 == 0 ? 4 : 1; }
+
+int finalize_groups(int N) {
+  const int per_block = kFinalizeThreads * finalize_cols(N);
+  return (N + per_block - 1) / per_block;
+}
 
 hipError_t launch_finalize(const float* part, int ksplit, int M, int N, const float* gptr, uint16_t* y,
                            unsigned long long* cand, hipStream_t stream) {
   _Float16* yh = reinterpret_cast<_Float16*>(y);
   const dim3 grid(finalize_groups(N), M), block(kFinalizeThreads);
-  if (cand)
-    hipLaunchKernelGGL(finalize_splits<true>, grid, block, 0, stream, part, ksplit, M, N, gptr, yh, cand);
+  const bool wide = finalize_cols(N) == 4;
+  if (cand && wide)
+    hipLaunchKernelGGL((finalize_splits<true, 4>), grid, block, 0, stream, part, ksplit, M, N, gptr, yh, cand);
+  else if (cand)
+    hipLaunchKernelGGL((finalize_splits<true, 1>), grid, block, 0, stream, part, ksplit, M, N, gptr, yh, cand);
+  else if (wide)
+    hipLaunchKernelGGL((finalize_splits<false, 4>), grid, block, 0, stream, part, ksplit, M, N, gptr, yh, cand);
   else
-    hipLaunchKernelGGL(finalize_splits<false>, grid, block, 0, stream, part, ksplit, M, N, gptr, yh, cand);
+    hipLaunchKernelGGL((finalize_splits<false, 1>), grid, block, 0, stream, part, ksplit, M, N, gptr, yh, cand);
   return hipGetLastError();
 }
 

@@ -158,13 +158,21 @@ int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales);
  * The three GEMM calls with an explicit kernel choice instead of the
  * library's pick (same arguments and results, used to compare kernels):
  *   engine : 0 = VALU dot2 engine (nvfp4_gemm with M == 1 only),
- *            1 = MFMA 16x16x32 f16 engine (all calls, M = 1..8)
- *   ct     : 16-column tiles per workgroup: 1, 2, 4 or 8
- *   nw     : wavefronts per workgroup, ct * S with S = 1..16/ct: the
- *            workgroup covers ct tiles x S consecutive K spans (1024 K for
- *            NVFP4, 512 K for FP8), one span of one tile per wavefront
+ *            1 = MFMA 16x16x32 f16 engine (all calls, M = 1..8),
+ *            2 = streaming MFMA engine (nvfp4_gemm and lm_head_gemm_argmax,
+ *                K <= 9216): each workgroup keeps all of x in LDS and each
+ *                wavefront walks whole column tiles along K, so K is never
+ *                split
+ *   ct     : engines 0, 1: 16-column tiles per workgroup: 1, 2, 4 or 8;
+ *            engine 2: workgroups per CU, 1 or 2 (the grid is that many per
+ *            CU of the current device, at most 1024)
+ *   nw     : wavefronts per workgroup.  Engines 0, 1: ct * S with
+ *            S = 1..16/ct: the workgroup covers ct tiles x S consecutive K
+ *            spans (1024 K for NVFP4, 512 K for FP8), one span of one tile
+ *            per wavefront.  Engine 2: 1..16
  *   ksplit : workgroups that share a tile group along K; with P spans in K
- *            it must satisfy ksplit * S >= P and (ksplit - 1) * S < P.
+ *            it must satisfy ksplit * S >= P and (ksplit - 1) * S < P
+ *            (engine 2: always 1).
  *            With ksplit > 1 each workgroup stores fp32 partial sums in
  *            the workspace (size from skinny_workspace_bytes_config for the
  *            same choice) and a second kernel adds them in split order
@@ -184,6 +192,11 @@ int lm_head_gemm_argmax_config(const void* w_packed, const uint16_t* x,
                                int N, void* workspace, size_t workspace_bytes,
                                hipStream_t stream, int engine, int ct, int nw,
                                int ksplit);
+
+/* 1 if the explicit kernel choice is supported for this op and shape (op as
+ * below), else 0. */
+int skinny_config_supported(int op, int M, int K, int N, int engine, int ct,
+                            int nw, int ksplit);
 
 /* Workspace bytes of a call made with an explicit kernel choice (op as
  * below); 0 for an unsupported choice or when none is needed. */

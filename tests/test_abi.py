@@ -65,7 +65,16 @@ def test_explicit_config_rejections():
     cfg = lambda *c: L.nvfp4_gemm_config(A, A, A, c[0], 256, 512, None, 0, None, *c[1:])
     # VALU engine is M = 1 only; unknown engine / tile counts / wave counts / splits are rejected.
     assert cfg(2, 0, 1, 4, 1) == sk.EINVAL
-    assert cfg(1, 2, 1, 4, 1) == sk.EINVAL
+    assert cfg(1, 3, 1, 4, 1) == sk.EINVAL
+    # streaming engine: no K split, 1 or 2 workgroups per CU, at most 9 K spans, NVFP4 calls only
+    assert cfg(1, 2, 1, 4, 2) == sk.EINVAL
+    assert cfg(1, 2, 3, 4, 1) == sk.EINVAL
+    assert L.nvfp4_gemm_config(A, A, A, 1, 10240, 512, None, 0, None, 2, 1, 16, 1) == sk.EINVAL
+    assert L.fp8_gemm_config(A, A, A, A, 1, 256, 512, None, 0, None, 2, 1, 4, 1) == sk.EINVAL
+    assert sk.config_supported(sk.OP_NVFP4, 8, 9216, 512, (2, 1, 16, 1))
+    assert not sk.config_supported(sk.OP_NVFP4, 8, 9216, 512, (2, 2, 16, 1))      # 2 x 147 KB of LDS
+    assert sk.config_supported(sk.OP_LM_HEAD, 8, 5120, 151936, (2, 1, 16, 1))
+    assert not sk.config_supported(sk.OP_FP8, 1, 5120, 7168, (2, 1, 16, 1))
     assert cfg(1, 1, 3, 4, 1) == sk.EINVAL
     assert cfg(1, 1, 1, 17, 1) == sk.EINVAL         # at most 16 wavefronts
     assert cfg(1, 1, 2, 3, 1) == sk.EINVAL          # nw must be a multiple of ct

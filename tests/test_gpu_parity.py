@@ -41,6 +41,14 @@ def cfgs(engine, K, unit_k=1024, splits=(1, 2, 3), cts=(1, 2, 4, 8)):
     return sorted(set(out))
 
 
+STREAM = [(2, 1, 16, 1), (2, 1, 4, 1), (2, 2, 8, 1), (2, 1, 1, 1)]
+
+
+def stream_cfgs(op, M, K, N):
+    """Streaming-engine choices (x resident in LDS, whole tiles per wavefront) supported here."""
+    return [c for c in STREAM if sk.config_supported(op, M, K, N, c)]
+
+
 def ws_for(op, M, K, N, config):
     """Workspace for a call, filled with junk: the library must not rely on its contents."""
     n = sk.workspace_bytes(op, M, K, N, config)
@@ -108,7 +116,7 @@ def test_nvfp4_one_hot_reproduces_dequantized_weights_exactly(K, N):
     deq = oracle.nvfp4_dequant_unscaled(case["codes"], case["scales"], K)       # [K, N]
     assert np.array_equal(deq.astype(np.float16).astype(np.float64), deq)
     eye = torch.eye(K, dtype=torch.float16, device="cuda")
-    for cfg in cfgs(1, K) + cfgs(0, K):
+    for cfg in cfgs(1, K) + cfgs(0, K) + stream_cfgs(sk.OP_NVFP4, 8, K, N):
         rows = 1 if cfg[0] == 0 else 8
         out = np.empty((K, N))
         ws = ws_for(sk.OP_NVFP4, rows, K, N, cfg)
@@ -143,7 +151,8 @@ def test_fp8_one_hot_reproduces_codes_exactly():
 def test_nvfp4_parity_all_configs(small_nvfp4, shape):
     case = small_nvfp4[shape]
     ref = ref_nvfp4(case)
-    choices = cfgs(1, case["K"]) + (cfgs(0, case["K"]) if case["M"] == 1 else [])
+    choices = (cfgs(1, case["K"]) + (cfgs(0, case["K"]) if case["M"] == 1 else [])
+               + stream_cfgs(sk.OP_NVFP4, case["M"], case["K"], case["N"]))
     for cfg in choices:
         _check(run_nvfp4(case, config=cfg), ref, f"{shape} {cfg}")
     _check(run_nvfp4(case, guard=8), ref, f"{shape} default")
@@ -155,6 +164,7 @@ def test_nvfp4_every_m():
         ref = ref_nvfp4(case, M)
         _check(run_nvfp4(case, M=M), ref, f"M={M} default")
         _check(run_nvfp4(case, M=M, config=(1, 2, 2, 2)), ref, f"M={M} mfma split")
+        _check(run_nvfp4(case, M=M, config=(2, 1, 16, 1)), ref, f"M={M} streaming")
 
 
 SMALL_FP8 = [(1, 256, 256), (2, 272, 100), (4, 400, 300), (8, 1040, 1000), (3, 16, 129)]
@@ -176,6 +186,8 @@ def test_deterministic_repeats(small_nvfp4):
     assert np.array_equal(a, b)
     c1 = small_nvfp4[(1, 272, 100)]
     assert np.array_equal(run_nvfp4(c1), run_nvfp4(c1))
+    s1 = run_nvfp4(case, config=(2, 1, 16, 1))
+    assert np.array_equal(s1, run_nvfp4(case, config=(2, 1, 16, 1)))
 
 
 # ------------------------------------------------------------------ argmax
@@ -195,7 +207,7 @@ def test_lm_head_argmax_and_logits(shape):
     case = workload.nvfp4_case(*shape, seed=sum(shape))
     ref = ref_nvfp4(case)
     want, margin = oracle.argmax_rows(ref)
-    for cfg in cfgs(1, K):
+    for cfg in cfgs(1, K) + stream_cfgs(sk.OP_LM_HEAD, M, K, N):
         idx, lg = run_lm_head(case, M, config=cfg, logits=True)
         assert np.array_equal(idx, want), f"{shape} {cfg}: {idx} vs {want} (margins {margin})"
         _check(lg, ref, f"{shape} {cfg} logits")
@@ -216,7 +228,7 @@ def test_lm_head_ties_go_to_lowest_column():
     case2 = dict(case, codes=codes, scales=scales, blob=sk.nvfp4_pack(codes, scales, case["g"], K, N))
     ref2 = ref_nvfp4(case2)
     want, _ = oracle.argmax_rows(ref2)
-    for cfg in cfgs(1, K):
+    for cfg in cfgs(1, K) + stream_cfgs(sk.OP_LM_HEAD, M, K, N):
         idx, _ = run_lm_head(case2, M, config=cfg)
         assert np.array_equal(idx, want), f"{cfg}: {idx} vs {want}"
 
