@@ -54,6 +54,22 @@ __device__ __forceinline__ float sum_over_rows(float v) {
   return v;
 }
 
+// Workgroup barrier after direct-to-LDS copies (global_load_lds) that each
+// wavefront issued before `pending` newer loads of its own.  The vector-memory
+// counter completes in order, so waiting until at most PENDING loads are
+// outstanding finishes this wavefront's copies without waiting for its newer
+// loads; __syncthreads() would wait for all of them (a full fence), which
+// holds the whole workgroup until its slowest weight load has arrived.
+template <int PENDING>
+__device__ __forceinline__ void lds_copy_barrier(bool pending) {
+  if (pending)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PENDING) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

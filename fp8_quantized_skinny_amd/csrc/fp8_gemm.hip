@@ -108,7 +108,7 @@ __device__ __forceinline__ void fp8_steps(const u32x4 (&w)[kFp8UnitChunks][2], c
 }
 
 template <int CT>
-__global__ __launch_bounds__(kMaxWaves * 64) void fp8_mfma(Fp8Args a) {
+__global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(8))) void fp8_mfma(Fp8Args a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const Fp8Plan P(a, CT);
   _Float16* xs = reinterpret_cast<_Float16*>(lds);
@@ -120,29 +120,31 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_mfma(Fp8Args a) {
   u32x4 w[kFp8UnitChunks][2];
   float sc[kFp8UnitChunks];
   if (P.active) {
+    const int u = P.s0 + P.s;
+    // Scales of the tile's 128-column block for this unit's four K blocks,
+    // loaded before the weights so that reading them waits for nothing else.
+    // A K block past the end contributes nothing (its x is zero in LDS), so
+    // the last block's scale stands in for it.
+    const float* srow = a.scales + static_cast<size_t>(min(tt * kTileCols, a.N - 1) / 128) * a.kb;
+#pragma unroll
+    for (int j = 0; j < kFp8UnitChunks; ++j) sc[j] = srow[min(u * kFp8UnitChunks + j, a.kb - 1)];
+    // Codes: pieces past K load from the row start instead (x is zero there,
+    // so they add exact zeros); no select on loaded data, which would make
+    // every load wait for the previous one.
     const int n = min(tt * kTileCols + cl, a.N - 1);
     const uint8_t* row = a.w + static_cast<size_t>(n) * a.K;
-    const int u = P.s0 + P.s;
     const int k0 = u * kFp8UnitK + grp * 16;
 #pragma unroll
     for (int j = 0; j < kFp8UnitChunks; ++j) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int k = k0 + j * kChunkK + 64 * h;
-        const bool ok = k + 16 <= a.K;
-        const u32x4 v = load16(row + (ok ? k : 0));
-        w[j][h] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        w[j][h] = load16(row + (k + 16 <= a.K ? k : 0));
       }
     }
-    // Scales of the tile's 128-column block for this unit's four K blocks (wave-uniform).
-    const float* srow = a.scales + static_cast<size_t>(min(tt * kTileCols, a.N - 1) / 128) * a.kb;
-#pragma unroll
-    for (int j = 0; j < kFp8UnitChunks; ++j) {
-      const int kb = u * kFp8UnitChunks + j;
-      sc[j] = kb < a.kb ? srow[kb] : 0.0f;
-    }
   }
-  __syncthreads();
+  // x is in LDS once every wavefront's copies are done; the weights keep arriving.
+  lds_copy_barrier<2 * kFp8UnitChunks>(P.active);
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (P.active) {

@@ -263,7 +263,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) c[j] = load16(p + j * kChunkBytes);
   }
-  __syncthreads();
+  // x is in LDS once every wavefront's copies are done; the weights keep arriving.
+  lds_copy_barrier<kChunksPerUnit + 1>(P.active);
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (P.active) {
