@@ -124,8 +124,8 @@ LaunchCfg pick_short_cfg(int ku, int nt) {
 
 // Streaming engine (all of x in LDS, whole tiles per wavefront, no K split)
 // whenever x fits: two 8-wavefront workgroups per CU when two copies of x
-// fit, else one workgroup of 12 (16 for vocabulary-sized N, whose tiles
-// outnumber the wavefront slots).
+// fit, else one workgroup of 11 wavefronts (16 for vocabulary-sized N, whose
+// tiles outnumber the wavefront slots).
 bool pick_stream_cfg(int M, int K, int N, LaunchCfg* out) {
   const LaunchCfg two{2, 2, 8, 1};
   if (nvfp4_cfg_supported(two, M, K, false)) {
@@ -133,7 +133,7 @@ bool pick_stream_cfg(int M, int K, int N, LaunchCfg* out) {
     return true;
   }
   const int nt = (N + kTileCols - 1) / kTileCols;
-  const LaunchCfg one{2, 1, nt >= 4096 ? 16 : 12, 1};
+  const LaunchCfg one{2, 1, nt >= 4096 ? 16 : 11, 1};
   if (nvfp4_cfg_supported(one, M, K, false)) {
     *out = one;
     return true;

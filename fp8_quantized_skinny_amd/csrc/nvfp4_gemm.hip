@@ -456,7 +456,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_stream(Nvfp4Args a) {
   Unit A, B;
   const uint8_t* base = a.units + static_cast<size_t>(c.t0) * KU * kUnitBytes + lane * 16;
   if (c.ntiles > 0) load_unit(A, base);
-  __syncthreads();
+  // x is in LDS once every wavefront's copies are done; the first unit keeps arriving.
+  lds_copy_barrier<kChunksPerUnit + 1>(c.ntiles > 0);
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   // Tiles in pairs, so that every unit's buffer is fixed at compile time
