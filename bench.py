@@ -14,8 +14,10 @@ gate+up 5120 x 34816 and down 17408 x 5120), timed the same way.
 Each step reads a different one of R byte-identical copies of the weights
 (R copies exceed 600 MB) so that the 256 MB Infinity Cache cannot serve them.
 Timing: W eager warm-up steps, then the K steps are captured once into a HIP
-graph; the timed region is one replay of that graph, bracketed by device
-synchronisation, with a HIP event pair recorded on the replay stream.  The
+graph, which is replayed untimed for about 0.1 s (GPU clocks settle only
+after tens of milliseconds of work); the timed region is one more replay,
+bracketed by device synchronisation, with a HIP event pair recorded on the
+replay stream.  The
 kernels of a replay run back to back, so the per-launch kernel duration is the
 event time divided by K.  The CPU oracle is timed beside it on the host, on a
 bounded sample of the headline workload.
@@ -166,8 +168,14 @@ def measure(name, M, cfg, steps, warmup, keep_case=False):
         with torch.cuda.graph(g, stream=cap):
             for i in range(steps):
                 step(i, torch.cuda.current_stream().cuda_stream)
-    g.replay()
-    torch.cuda.synchronize()
+    # Untimed replays until about 0.1 s of GPU work has run: clocks and power
+    # state settle only after tens of milliseconds of back-to-back kernels.
+    t_warm = time.perf_counter()
+    for _ in range(50):
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_warm > 0.1:
+            break
 
     # Timed region: one replay of the K-step graph on `stream`.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -69,26 +69,34 @@ __global__ __launch_bounds__(kFinalizeThreads) void finalize_splits(const float*
   }
 }
 
-// idx[m] = column of the largest candidate key of row m.
+// idx[m] = column of the largest candidate key of row m.  Every thread
+// issues the loads of all its rows before reducing any of them, so the kernel
+// waits for memory about once instead of once per row.
 __global__ __launch_bounds__(256) void argmax_reduce(const unsigned long long* cand, int groups, int M,
                                                      int32_t* idx) {
-  __shared__ unsigned long long red[256];
-  for (int m = 0; m < M; ++m) {
-    unsigned long long k = 0ull;
-    for (int g = threadIdx.x; g < groups; g += blockDim.x) {
-      const unsigned long long v = cand[static_cast<size_t>(g) * M + m];
-      k = v > k ? v : k;
-    }
-    red[threadIdx.x] = k;
-    __syncthreads();
-    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
-      if (threadIdx.x < static_cast<unsigned>(off))
-        red[threadIdx.x] = red[threadIdx.x + off] > red[threadIdx.x] ? red[threadIdx.x + off] : red[threadIdx.x];
-      __syncthreads();
-    }
+  __shared__ unsigned long long red[4][kMaxRows];
+  unsigned long long k[kMaxRows];
+#pragma unroll
+  for (int m = 0; m < kMaxRows; ++m) k[m] = 0ull;
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) {
+    unsigned long long v[kMaxRows];
+#pragma unroll
+    for (int m = 0; m < kMaxRows; ++m) v[m] = m < M ? cand[static_cast<size_t>(g) * M + m] : 0ull;
+#pragma unroll
+    for (int m = 0; m < kMaxRows; ++m) k[m] = v[m] > k[m] ? v[m] : k[m];
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 0; m < kMaxRows; ++m) {
+    const unsigned long long w = wave_max_key(k[m]);
+    if (lane == 0) red[wave][m] = w;
+  }
+  __syncthreads();
+  if (threadIdx.x < static_cast<unsigned>(M)) {
+    unsigned long long best = 0ull;
+    for (int w = 0; w < 4; ++w) best = red[w][threadIdx.x] > best ? red[w][threadIdx.x] : best;
     // No candidate at all (every logit NaN) leaves the all-ones index -1.
-    if (threadIdx.x == 0) idx[m] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(red[0] & 0xFFFFFFFFull));
-    __syncthreads();
+    idx[threadIdx.x] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFull));
   }
 }
 
