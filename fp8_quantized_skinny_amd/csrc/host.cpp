@@ -315,7 +315,7 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float gscale, int K,
   const size_t row_codes = K / 2, row_scales = K / 16;
   for (int t = 0; t < geo.nt; ++t) {
     for (int u = 0; u < geo.ku; ++u) {
-      uint8_t* unit = blob + kHeaderBytes + (static_cast<size_t>(t) * geo.ku + u) * kUnitBytes;
+      uint8_t* unit = blob + kHeaderBytes + (static_cast<size_t>(u) * geo.nt + t) * kUnitBytes;
       uint8_t* svec = unit + kChunksPerUnit * kChunkBytes;
       for (int lane = 0; lane < 64; ++lane) {
         const int grp = lane >> 4, c = lane & 15;

@@ -12,7 +12,8 @@ namespace skinny {
 // Packed NVFP4 blob.
 //
 //   [0, 256)     header (Nvfp4Header, zero padded)
-//   [256, ...)   units: NT x G units of 9216 bytes, tile-major
+//   [256, ...)   units: G x NT units of 9216 bytes, span-major: unit (t, g)
+//                at 256 + (g * NT + t) * 9216
 //
 // A unit covers one column tile t (columns 16t .. 16t+15) and one K span g
 // (K 1024g .. 1024g+1023): eight 1 KiB code chunks followed by one 1 KiB
@@ -25,11 +26,16 @@ namespace skinny {
 // Scale vector: lane l owns bytes [16l, 16l+16); byte 2j + h is the E4M3
 // scale of that lane's codes in chunk j, half h (16 K each).
 //
+// Span-major order puts the units of one K span of consecutive tiles next to
+// each other, so wavefronts that walk their tiles span by span in step (the
+// streaming engine) read one contiguous region at a time; the one-unit-per-
+// wavefront kernels read consecutive tiles of every span, which is as dense.
+//
 // K is padded to a multiple of 1024 and N to a multiple of 16 with zero codes
 // and zero scales, so padded weights are exactly 0.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kBlobMagic = 0x344E4B53u;  // "SKN4" little-endian
-constexpr uint32_t kBlobVersion = 2;
+constexpr uint32_t kBlobVersion = 3;
 constexpr size_t kHeaderBytes = 256;
 constexpr int kTileCols = 16;
 constexpr int kChunkK = 128;

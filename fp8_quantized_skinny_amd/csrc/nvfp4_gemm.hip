@@ -83,7 +83,7 @@ struct Plan {
   // results are never stored.
   __device__ const uint8_t* unit_ptr(const Nvfp4Args& a) const {
     const int tt = min(tile0 + t, a.nt - 1);
-    return a.units + (static_cast<size_t>(tt) * a.ku + s0 + s) * kUnitBytes + lane * 16;
+    return a.units + (static_cast<size_t>(s0 + s) * a.nt + tt) * kUnitBytes + lane * 16;
   }
 };
 
@@ -382,6 +382,7 @@ __device__ __forceinline__ void mfma_unit_lean(const Unit& U, f32x4& acc, const 
 struct StreamCtx {
   const Nvfp4Args* a;
   const _Float16* xbase;  // this lane's LDS x row (row min(c, M-1)), fragment group offset included
+  size_t span_stride;     // bytes from one K span of a tile to its next (span-major units)
   size_t tile_stride;     // bytes from one of this wavefront's tiles to its next
   unsigned long long* best;  // LDS [kMaxRows] running argmax keys of this wavefront
   int t0, step, ntiles, lane;
@@ -401,7 +402,7 @@ __device__ __forceinline__ void stream_units(const StreamCtx& c, Unit& A, Unit& 
     Unit& cur = PAR ? B : A;
     Unit& nxt = PAR ? A : B;
     if constexpr (J + 1 < KU)
-      load_unit(nxt, base + (J + 1) * kUnitBytes);
+      load_unit(nxt, base + (J + 1) * c.span_stride);
     else if (ti + 1 < c.ntiles)
       load_unit(nxt, base + c.tile_stride);
     // Keep the scheduler from hoisting work across units: it would start later
@@ -446,7 +447,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_stream(Nvfp4Args a) {
   c.step = gridDim.x * nw;
   c.t0 = blockIdx.x + gridDim.x * wave;
   c.ntiles = c.t0 < a.nt ? (a.nt - 1 - c.t0) / c.step + 1 : 0;
-  c.tile_stride = static_cast<size_t>(c.step) * KU * kUnitBytes;
+  c.span_stride = static_cast<size_t>(a.nt) * kUnitBytes;
+  c.tile_stride = static_cast<size_t>(c.step) * kUnitBytes;
   c.g = *a.gptr;
   c.xbase = xs + min(lane & 15, a.M - 1) * RS + (lane >> 4) * 32;
   c.best = best + wave * kMaxRows;
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_stream(Nvfp4Args a) {
   stage_x_all(a, xs, RS, wave, nw, lane);
   if (ARGMAX && lane < kMaxRows) c.best[lane] = 0ull;
   Unit A, B;
-  const uint8_t* base = a.units + static_cast<size_t>(c.t0) * KU * kUnitBytes + lane * 16;
+  const uint8_t* base = a.units + static_cast<size_t>(c.t0) * kUnitBytes + lane * 16;
   if (c.ntiles > 0) load_unit(A, base);
   // x is in LDS once every wavefront's copies are done; the first unit keeps arriving.
   lds_copy_barrier<kChunksPerUnit + 1>(c.ntiles > 0);

@@ -74,9 +74,9 @@ enum {
  *
  * The blob starts with a 256-byte header (magic "SKN4", version, K, N, g)
  * followed by 9 KiB units, one per 16 output columns x 1024 K (K padded with
- * zero codes to a multiple of 1024): eight 1 KiB code chunks, then the
- * unit's 1 KiB of scales, ordered so that each lane of a wavefront loads
- * 16 contiguous bytes of every chunk.  The caller copies the
+ * zero codes to a multiple of 1024), all tiles of the first K span, then of
+ * the next: eight 1 KiB code chunks, then the unit's 1 KiB of scales, ordered
+ * so that each lane of a wavefront loads 16 contiguous bytes of every chunk.  The caller copies the
  * blob as-is into a device buffer it owns and passes that to nvfp4_gemm or
  * lm_head_gemm_argmax.  Returns SKINNY_ESIZE if out is non-NULL and
  * *out_bytes is smaller than the blob.

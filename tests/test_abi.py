@@ -161,7 +161,7 @@ def test_pack_size_and_header():
     blob = sk.nvfp4_pack(codes, scales, 0.125, 272, 100)
     h = blob[:64]
     assert bytes(h[:4]) == b"SKN4"
-    assert list(h[4:28].view(np.uint32)) == [2, 272, 100, 1, 7, 9216]
+    assert list(h[4:28].view(np.uint32)) == [3, 272, 100, 1, 7, 9216]
     assert h[28:32].view(np.float32)[0] == np.float32(0.125)
     assert list(h[32:48].view(np.uint64)) == [256, 7 * 9216]
 
@@ -190,7 +190,7 @@ def test_pack_places_every_byte_once(K, N):
     scales = rng.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8)   # no NaN codes
     blob = sk.nvfp4_pack(codes, scales, 1.0, K, N)
     ku, nt = _geom(K, N)
-    units = blob[256:].reshape(nt, ku, 9, 4, 16, 16)     # tile, span, chunk(8)+scales, grp, col, byte
+    units = blob[256:].reshape(ku, nt, 9, 4, 16, 16).transpose(1, 0, 2, 3, 4, 5)   # span-major -> [tile, span, ...]
     seen_c = np.zeros(codes.shape, np.int64)
     seen_s = np.zeros(scales.shape, np.int64)
     for n in range(N):
