@@ -106,20 +106,29 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 // and the fewest K spans per workgroup that keep the K split at most nine
 // ways (the x slice a workgroup stages in LDS grows with M and with its
 // spans; short workgroups keep it small, so that more of them fit on a CU).
-LaunchCfg pick_whole_k_cfg(int engine, int ku) {
-  int s = std::min(ku, kMaxWaves);
-  const int ksplit = (ku + s - 1) / s;
-  s = (ku + ksplit - 1) / ksplit;
-  return LaunchCfg{engine, 1, s, ksplit};
+// The largest S (K spans per workgroup) from `s_max` down for which the
+// choice is supported (its LDS copy of x fits), with the K split evened out.
+template <typename Fits>
+LaunchCfg fit_spans(int engine, int ct, int ku, int s_max, Fits fits) {
+  for (int s0 = std::max(1, s_max); s0 >= 1; --s0) {
+    const int ksplit = (ku + s0 - 1) / s0;
+    const int s = (ku + ksplit - 1) / ksplit;
+    const LaunchCfg c{engine, ct, ct * s, ksplit};
+    if (fits(c)) return c;
+  }
+  return LaunchCfg{engine, ct, ct, ku};
 }
 
-LaunchCfg pick_short_cfg(int ku, int nt) {
+template <typename Fits>
+LaunchCfg pick_whole_k_cfg(int engine, int ku, Fits fits) {
+  return fit_spans(engine, 1, ku, std::min(ku, kMaxWaves), fits);
+}
+
+template <typename Fits>
+LaunchCfg pick_short_cfg(int ku, int nt, Fits fits) {
   constexpr int kMaxSplit = 9;
   const int ct = nt >= 4 ? 4 : (nt >= 2 ? 2 : 1);
-  int s = std::min((ku + kMaxSplit - 1) / kMaxSplit, kMaxWaves / ct);
-  const int ksplit = (ku + s - 1) / s;
-  s = (ku + ksplit - 1) / ksplit;
-  return LaunchCfg{1, ct, ct * s, ksplit};
+  return fit_spans(1, ct, ku, std::min((ku + kMaxSplit - 1) / kMaxSplit, kMaxWaves / ct), fits);
 }
 
 // Streaming engine (all of x in LDS, whole tiles per wavefront, no K split)
@@ -143,17 +152,19 @@ bool pick_stream_cfg(int M, int K, int N, LaunchCfg* out) {
 
 LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax) {
   const Geometry g = nvfp4_geometry(K, N);
-  if (M == 1 && !argmax) return pick_whole_k_cfg(0, g.ku);
+  auto fits = [&](const LaunchCfg& c) { return nvfp4_cfg_supported(c, M, K, argmax); };
+  if (M == 1 && !argmax) return pick_whole_k_cfg(0, g.ku, fits);
   LaunchCfg c;
   if (pick_stream_cfg(M, K, N, &c)) return c;
-  if (M > 4) return pick_short_cfg(g.ku, g.nt);
-  return pick_whole_k_cfg(1, g.ku);
+  if (M > 4) return pick_short_cfg(g.ku, g.nt, fits);
+  return pick_whole_k_cfg(1, g.ku, fits);
 }
 
 LaunchCfg default_fp8_cfg(int M, int K, int N) {
   const int ku = (K + 511) / 512;
-  if (M > 4) return pick_short_cfg(ku, (N + 15) / 16);
-  return pick_whole_k_cfg(1, ku);
+  auto fits = [&](const LaunchCfg& c) { return fp8_cfg_supported(c, M, K); };
+  if (M > 4) return pick_short_cfg(ku, (N + 15) / 16, fits);
+  return pick_whole_k_cfg(1, ku, fits);
 }
 
 int nvfp4_common_checks(const void* w_packed, const uint16_t* x, const void* out, int M, int K, int N) {

@@ -264,3 +264,18 @@ def test_host_quantizer_special_inputs():
     a1, b1 = sk.fp8_quantize(w)
     a2, b2 = oracle.fp8_quantize(w)
     assert np.array_equal(a1, a2) and np.array_equal(b1, b2)
+
+
+def test_default_kernel_choice_is_always_supported():
+    """For every op and a spread of shapes, the library's own pick passes its checks.
+
+    With fake device pointers a call that passes every host check fails only at
+    the launch (no GPU here: SKINNY_EHIP); an unsupported pick would be EINVAL."""
+    L = lib()
+    big = 1 << 40
+    for M in range(1, 9):
+        for K in (16, 256, 1040, 5120, 9216, 10240, 17408, 1 << 20):
+            for N in (1, 16, 17, 40, 5120, 151936):
+                assert L.nvfp4_gemm(A, A, A, M, K, N, A, big, None) == sk.EHIP, (M, K, N)
+                assert L.fp8_gemm(A, A, A, A, M, K, N, A, big, None) == sk.EHIP, (M, K, N)
+                assert L.lm_head_gemm_argmax(A, A, A, None, M, K, N, A, big, None) == sk.EHIP, (M, K, N)
