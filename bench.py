@@ -7,7 +7,10 @@ scales) per step divided by the time per step, with every input already
 resident in HBM.  The headline workload is the NVFP4 GEMV at M = 1,
 K = 5120, N = 17408 (an MLP up-projection at decode): one step is one
 nvfp4_gemm call.  The same line also carries the two NVFP4 M = 8 shapes (fused
-gate+up 5120 x 34816 and down 17408 x 5120), timed the same way.
+gate+up 5120 x 34816 and down 17408 x 5120), timed the same way, and for each
+shape the measured read ceiling: the library's read probe (skinny_read_probe,
+one 9 KiB block per wavefront like one packed unit) over the same rotating
+copies, plus the probe over a 2 GiB buffer.
 
     python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head] [--M m]
 
@@ -112,7 +115,74 @@ def recorded_traffic(name, M):
     return None
 
 
-def measure(name, M, cfg, steps, warmup, keep_case=False):
+def time_graph(step, steps, stream):
+    """Capture `steps` launches of step(i, stream_handle) in a HIP graph, replay it untimed for
+    about 0.1 s (clocks and power state settle only after tens of milliseconds of back-to-back
+    kernels), then time one replay with HIP events on `stream`; returns ms for that replay."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(steps):
+                step(i, torch.cuda.current_stream().cuda_stream)
+    t_warm = time.perf_counter()
+    for _ in range(50):
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_warm > 0.1:
+            break
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    del g
+    return ms
+
+
+def read_ceiling(copies, nbytes, steps, large=True):
+    """Measured HBM read ceiling: the library's read probe (one 9 KiB block per
+    wavefront, nine 16-byte loads per lane) over the same rotating copies as the
+    GEMM, and over a 2 GiB buffer."""
+    import torch
+    import fp8_quantized_skinny_amd as sk
+    from fp8_quantized_skinny_amd._lib import lib
+    L = lib()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    probe_bytes = (nbytes // 9216) * 9216
+
+    def step_same(i, s):
+        st = L.skinny_read_probe(copies[i % len(copies)].data_ptr(), probe_bytes, sink.data_ptr(), s)
+        if st != 0:
+            raise RuntimeError(f"read probe failed: {sk.strerror(st)}")
+    ms = time_graph(step_same, steps, stream)
+    same = probe_bytes * steps / (ms * 1e-3) / 1e9
+    out = {"same_size_GBs": round(same, 1),
+           "probe": "skinny_read_probe: one 9 KiB block per wavefront, nine 16-byte loads per lane; "
+                    "same rotation of weight copies as the GEMM, HIP-graph replay"}
+    log(f"read probe: {same:.1f} GB/s at {nbytes / 1e6:.1f} MB")
+    if not large:
+        return out
+    big = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    big_bytes = (big.numel() // 9216) * 9216
+
+    def step_big(i, s):
+        st = L.skinny_read_probe(big.data_ptr(), big_bytes, sink.data_ptr(), s)
+        if st != 0:
+            raise RuntimeError(f"read probe failed: {sk.strerror(st)}")
+    ms_big = time_graph(step_big, 20, stream)
+    large_gbs = big_bytes * 20 / (ms_big * 1e-3) / 1e9
+    del big
+    log(f"read probe: {large_gbs:.1f} GB/s at 2 GiB")
+    out["2GiB_GBs"] = round(large_gbs, 1)
+    return out
+
+
+def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_probe=False):
     """Time `steps` launches of one workload; returns (result dict, case or None)."""
     import numpy as np
     import torch
@@ -162,38 +232,18 @@ def measure(name, M, cfg, steps, warmup, keep_case=False):
         step(i, stream.cuda_stream)
     torch.cuda.synchronize()
 
-    g = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(g, stream=cap):
-            for i in range(steps):
-                step(i, torch.cuda.current_stream().cuda_stream)
-    # Untimed replays until about 0.1 s of GPU work has run: clocks and power
-    # state settle only after tens of milliseconds of back-to-back kernels.
-    t_warm = time.perf_counter()
-    for _ in range(50):
-        g.replay()
-        torch.cuda.synchronize()
-        if time.perf_counter() - t_warm > 0.1:
-            break
-
-    # Timed region: one replay of the K-step graph on `stream`.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
-    log(f"{name} M={M}: graph replay {gpu_ms:.3f} ms GPU, {wall * 1e3:.3f} ms wall for {steps} steps")
+    # Timed region: one replay of the K-step graph on `stream`, after untimed replays.
+    gpu_ms = time_graph(step, steps, stream)
+    log(f"{name} M={M}: graph replay {gpu_ms:.3f} ms GPU for {steps} steps")
     us = gpu_ms * 1e3 / steps
     gbs = wbytes / (us * 1e-6) / 1e9
     res = {"workload": describe(case, name), "M": M, "K": K, "N": N, "weight_bytes": wbytes, "weight_copies": R,
            "kernel_choice": list(cfg) if cfg else "default", "us_per_step": round(us, 3),
            "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-    del g, copies
+    if ceiling:
+        res["read_ceiling"] = read_ceiling(copies, wbytes, steps, large=large_probe)
+        res["frac_of_read_ceiling"] = round(gbs / res["read_ceiling"]["same_size_GBs"], 4)
+    del copies
     torch.cuda.synchronize()
     return res, (case if keep_case else None)
 
@@ -216,11 +266,12 @@ def main():
         return
     cfg = tuple(int(v) for v in args.config.split(",")) if args.config else None
     head, case = measure(args.workload, args.M, cfg, args.steps, args.warmup,
-                         keep_case=not args.no_cpu_baseline)
+                         keep_case=not args.no_cpu_baseline, ceiling=not args.headline_only,
+                         large_probe=True)
     companions = []
     if not args.headline_only and args.workload == "up" and cfg is None:
         for name in ("gate_up", "down"):
-            r, _ = measure(name, 8, None, args.steps, args.warmup)
+            r, _ = measure(name, 8, None, args.steps, args.warmup, ceiling=True)
             companions.append(r)
     value = head["GB/s"]
     out = {

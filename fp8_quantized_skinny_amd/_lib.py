@@ -23,6 +23,7 @@ def _declare(lib):
                                                c_int, c_int, c_int, c_int]),
         "skinny_workspace_bytes_config": (c_size_t, [c_int] * 8),
         "skinny_config_supported": (c_int, [c_int] * 8),
+        "skinny_read_probe": (c_int, [P, c_size_t, P, P]),
         "nvfp4_quantize": (c_int, [P, c_int, c_int, P, P, ctypes.POINTER(c_float)]),
         "fp8_quantize": (c_int, [P, c_int, c_int, P, P]),
         "skinny_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
@@ -48,4 +49,4 @@ def lib():
 EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp4_quantize",
             "fp8_quantize", "skinny_workspace_bytes", "skinny_strerror", "nvfp4_gemm_config",
             "fp8_gemm_config", "lm_head_gemm_argmax_config", "skinny_workspace_bytes_config",
-            "skinny_config_supported")
+            "skinny_config_supported", "skinny_read_probe")

@@ -283,6 +283,13 @@ int skinny_config_supported(int op, int M, int K, int N, int engine, int ct, int
   }
 }
 
+int skinny_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink) return SKINNY_EINVAL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return SKINNY_EALIGN;
+  if (bytes < 9216 || bytes / 9216 > (static_cast<size_t>(1) << 31) * 4) return SKINNY_ESIZE;
+  return launch_status(launch_read_probe(buf, bytes, sink, stream));
+}
+
 size_t skinny_workspace_bytes(int op, int M, int K, int N) {
   if (check_shape(M, K, N)) return 0;
   switch (op) {

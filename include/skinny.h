@@ -207,6 +207,20 @@ size_t skinny_workspace_bytes_config(int op, int M, int K, int N, int engine,
  * 2 = lm_head_gemm_argmax.  Returns 0 for an unsupported op or shape. */
 size_t skinny_workspace_bytes(int op, int M, int K, int N);
 
+/* ---------------------------------------------------------------------------
+ * skinny_read_probe -- measurement helper, not part of the GEMM path.
+ *
+ * Reads floor(bytes / 9216) blocks of 9216 bytes of the device buffer `buf`,
+ * each by one wavefront with nine 16-byte loads per lane (the access shape of
+ * one NVFP4 unit), and writes nothing else but possibly one word to `sink`
+ * (device, 4 bytes).  Timing it gives the HBM read ceiling that the GEMM
+ * kernels are rated against (the post, section "What I actually built",
+ * rates its kernels against a measured read-only ceiling).  Asynchronous on
+ * `stream`.  SKINNY_ESIZE if bytes < 9216.
+ * ------------------------------------------------------------------------- */
+int skinny_read_probe(const void* buf, size_t bytes, uint32_t* sink,
+                      hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* skinny_strerror(int status);
 
