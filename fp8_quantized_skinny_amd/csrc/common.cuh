@@ -54,20 +54,37 @@ __device__ __forceinline__ float sum_over_rows(float v) {
   return v;
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits until at most `vm` vector
+// memory and `lgkm` LDS/scalar operations are outstanding.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
+}
+
 // Workgroup barrier after direct-to-LDS copies (global_load_lds) that each
 // wavefront issued before `pending` newer loads of its own.  The vector-memory
 // counter completes in order, so waiting until at most PENDING loads are
 // outstanding finishes this wavefront's copies without waiting for its newer
 // loads; __syncthreads() would wait for all of them (a full fence), which
-// holds the whole workgroup until its slowest weight load has arrived.
+// holds the whole workgroup until its slowest weight load has arrived.  The
+// wait is the compiler's own s_waitcnt, not inline asm: the compiler then
+// knows the copies have landed, whereas after an opaque wait it treats them
+// as outstanding and, at its next wait on a newer load, waits for every load
+// in flight.  The empty asm keeps LDS reads from moving above the barrier.
 template <int PENDING>
 __device__ __forceinline__ void lds_copy_barrier(bool pending) {
   if (pending)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PENDING) : "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(PENDING, 0));
   else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Raw buffer resource over the `halves` fp16 values at p (gfx9 descriptor
+// word 3 for untyped dword access).  Loads at byte offsets at or past the end
+// return zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const _Float16* p, int halves) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(p), static_cast<short>(0), halves * 2, 0x00020000);
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {

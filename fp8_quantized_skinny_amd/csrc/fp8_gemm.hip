@@ -119,7 +119,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
   const int tt = min(P.tile0 + P.t, a.nt - 1);
   u32x4 w[kFp8UnitChunks][2];
   float sc[kFp8UnitChunks];
-  if (P.active) {
+  // Every wavefront loads, an idle one (past the last K span) clamped
+  // addresses it never uses: with no load under a branch the compiler waits
+  // for each chunk alone instead of the whole unit.
+  {
     const int u = P.s0 + P.s;
     // Scales of the tile's 128-column block for this unit's four K blocks,
     // loaded before the weights so that reading them waits for nothing else.
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
     }
   }
   // x is in LDS once every wavefront's copies are done; the weights keep arriving.
-  lds_copy_barrier<2 * kFp8UnitChunks>(P.active);
+  lds_copy_barrier<2 * kFp8UnitChunks>(true);
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (P.active) {

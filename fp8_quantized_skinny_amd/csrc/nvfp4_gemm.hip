@@ -148,11 +148,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu_m1(Nvfp4Args a) {
     u32x4 c[kChunksPerUnit];
     uint32_t xv[kChunksPerUnit];
     const int kx = (P.s0 + P.s) * kUnitK + 2 * P.lane;
+    // x through a buffer resource of exactly K halves: pairs past K read as
+    // zero in hardware, with no select on loaded data (a select would make
+    // the first chunk wait for every load before it).
+    const __amdgpu_buffer_rsrc_t xr = x_rsrc(a.x, a.K);
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
       c[j] = load16(p + j * kChunkBytes);
-      const int k = kx + j * kChunkK;
-      xv[j] = k < a.K ? *reinterpret_cast<const uint32_t*>(a.x + k) : 0u;
+      xv[j] = __builtin_amdgcn_raw_buffer_load_b32(xr, (kx + j * kChunkK) * 2, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
@@ -255,16 +258,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
   f32x4* red = reinterpret_cast<f32x4*>(lds + ((a.M * xs_stride(P.S) * 2 + 15) & ~15));  // [nw][32]
 
   // x first (the vector-memory counter completes in order), then the unit.
+  // Every wavefront loads a unit, an idle one (past the last K span) the
+  // blob's unit 0, a cache hit it never uses: with no load under a branch
+  // the compiler waits for each chunk alone instead of the whole unit.
   stage_x(a, P, xs);
-  u32x4 c[kChunksPerUnit], sv = u32x4{0u, 0u, 0u, 0u};
-  if (P.active) {
-    const uint8_t* p = P.unit_ptr(a);
+  u32x4 c[kChunksPerUnit], sv;
+  {
+    const uint8_t* p = P.active ? P.unit_ptr(a) : a.units + P.lane * 16;
     sv = load16(p + kChunksPerUnit * kChunkBytes);
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) c[j] = load16(p + j * kChunkBytes);
   }
   // x is in LDS once every wavefront's copies are done; the weights keep arriving.
-  lds_copy_barrier<kChunksPerUnit + 1>(P.active);
+  lds_copy_barrier<kChunksPerUnit + 1>(true);
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (P.active) {
@@ -385,6 +391,7 @@ struct StreamCtx {
   size_t span_stride;     // bytes from one K span of a tile to its next (span-major units)
   size_t tile_stride;     // bytes from one of this wavefront's tiles to its next
   unsigned long long* best;  // LDS [kMaxRows] running argmax keys of this wavefront
+  const uint8_t* spare;      // unit 0 of the blob (this lane's 16 bytes): read in place of a unit past the last tile
   int t0, step, ntiles, lane;
   float g;
 };
@@ -392,7 +399,12 @@ struct StreamCtx {
 // Unit J of this wavefront's tile `ti`, whose unit 0 (this lane's 16 bytes)
 // is at `base`.  All buffer choices are compile-time: first the loads of the
 // wavefront's next unit go out into the other buffer, then unit J is
-// contracted.  After the tile's last span the tile is stored and its logits
+// contracted.  The next unit is always loaded: after the wavefront's last
+// tile it is the blob's unit 0, a cache hit that is never used.  With no
+// load under a branch the compiler knows, at every chunk, exactly how many
+// loads are still in flight, and waits for the current unit only; a
+// conditional prefetch made it wait for the prefetch too, at every tile
+// boundary.  After the tile's last span the tile is stored and its logits
 // are folded into the wavefront's running argmax keys (kept in LDS, not in
 // registers, which the two units in flight already fill).
 template <int KU, int J, int PAR, bool ARGMAX>
@@ -403,8 +415,8 @@ __device__ __forceinline__ void stream_units(const StreamCtx& c, Unit& A, Unit& 
     Unit& nxt = PAR ? A : B;
     if constexpr (J + 1 < KU)
       load_unit(nxt, base + (J + 1) * c.span_stride);
-    else if (ti + 1 < c.ntiles)
-      load_unit(nxt, base + c.tile_stride);
+    else
+      load_unit(nxt, ti + 1 < c.ntiles ? base + c.tile_stride : c.spare);
     // Keep the scheduler from hoisting work across units: it would start later
     // units' LDS reads and conversions early and run out of registers.
     __builtin_amdgcn_sched_barrier(0);
@@ -452,25 +464,28 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_stream(Nvfp4Args a) {
   c.g = *a.gptr;
   c.xbase = xs + min(lane & 15, a.M - 1) * RS + (lane >> 4) * 32;
   c.best = best + wave * kMaxRows;
+  c.spare = a.units + lane * 16;
 
   stage_x_all(a, xs, RS, wave, nw, lane);
   if (ARGMAX && lane < kMaxRows) c.best[lane] = 0ull;
   Unit A, B;
   const uint8_t* base = a.units + static_cast<size_t>(c.t0) * kUnitBytes + lane * 16;
-  if (c.ntiles > 0) load_unit(A, base);
+  load_unit(A, c.ntiles > 0 ? base : c.spare);
   // x is in LDS once every wavefront's copies are done; the first unit keeps arriving.
-  lds_copy_barrier<kChunksPerUnit + 1>(c.ntiles > 0);
+  lds_copy_barrier<kChunksPerUnit + 1>(true);
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   // Tiles in pairs, so that every unit's buffer is fixed at compile time
   // (the wavefront's unit u lives in A when u is even): with odd KU the
-  // second tile of a pair starts in B.
-  for (int ti = 0; ti < c.ntiles; ti += 2) {
+  // second tile of a pair starts in B.  An odd last tile follows the loop.
+  int ti = 0;
+  for (; ti + 1 < c.ntiles; ti += 2) {
     stream_units<KU, 0, 0, ARGMAX>(c, A, B, ti, base, acc);
     base += c.tile_stride;
-    if (ti + 1 < c.ntiles) stream_units<KU, 0, KU % 2, ARGMAX>(c, A, B, ti + 1, base, acc);
+    stream_units<KU, 0, KU % 2, ARGMAX>(c, A, B, ti + 1, base, acc);
     base += c.tile_stride;
   }
+  if (ti < c.ntiles) stream_units<KU, 0, 0, ARGMAX>(c, A, B, ti, base, acc);
 
   if (ARGMAX) {
     // Largest key per row over the workgroup's wavefronts.
