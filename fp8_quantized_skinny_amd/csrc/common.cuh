@@ -80,13 +80,6 @@ __device__ __forceinline__ void lds_copy_barrier(bool pending) {
   asm volatile("" ::: "memory");
 }
 
-// Raw buffer resource over the `halves` fp16 values at p (gfx9 descriptor
-// word 3 for untyped dword access).  Loads at byte offsets at or past the end
-// return zero without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const _Float16* p, int halves) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(p), static_cast<short>(0), halves * 2, 0x00020000);
-}
-
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

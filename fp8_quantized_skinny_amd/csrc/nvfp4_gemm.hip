@@ -148,14 +148,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu_m1(Nvfp4Args a) {
     u32x4 c[kChunksPerUnit];
     uint32_t xv[kChunksPerUnit];
     const int kx = (P.s0 + P.s) * kUnitK + 2 * P.lane;
-    // x through a buffer resource of exactly K halves: pairs past K read as
-    // zero in hardware, with no select on loaded data (a select would make
-    // the first chunk wait for every load before it).
-    const __amdgpu_buffer_rsrc_t xr = x_rsrc(a.x, a.K);
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
       c[j] = load16(p + j * kChunkBytes);
-      xv[j] = __builtin_amdgcn_raw_buffer_load_b32(xr, (kx + j * kChunkK) * 2, 0, 0);
+      const int k = kx + j * kChunkK;
+      xv[j] = k < a.K ? *reinterpret_cast<const uint32_t*>(a.x + k) : 0u;
     }
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
