@@ -6,7 +6,8 @@ library shares no code with it.  Everything here is plain NumPy in float64:
 
   formats   E2M1 / E4M3FN decoders and encoders from their bit layouts
   quantize  the NVFP4 and 128x128-block FP8 quantization rules
-  gemm      y = x . dequant(W) in float64, per-row argmax, error metrics
+  gemm      y = x . dequant(W) in float64, per-row argmax, error metrics,
+            and the SwiGLU of a gate/up pair of projections
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) against
 tables, library routines, brute force and closed-form cases.
@@ -15,4 +16,4 @@ tables, library routines, brute force and closed-form cases.
 from .formats import e2m1_decode, e4m3_decode, e2m1_encode, e4m3_encode, E2M1_MAX, E4M3_MAX
 from .quantize import nvfp4_quantize, fp8_quantize
 from .gemm import (nvfp4_unpack_codes, nvfp4_dequant_unscaled, nvfp4_gemm, fp8_dequant, fp8_gemm,
-                   argmax_rows, compare)
+                   silu, nvfp4_swiglu, argmax_rows, compare)

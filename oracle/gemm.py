@@ -90,6 +90,32 @@ def fp8_gemm(x, codes, scales, cols=None, chunk=1024):
     return y
 
 
+def silu(z):
+    """SiLU (sigmoid-weighted linear unit), z * sigmoid(z), in float64.
+
+    The activation of the gated MLP that follows a fused gate+up projection
+    (SwiGLU: Shazeer, "GLU Variants Improve Transformer", 2020, with the
+    SiLU of Elfwing, Uchibe and Doya, 2018).  Written as z / (1 + exp(-z));
+    exp overflows to inf for z below about -709, which gives the correct
+    limit -0."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def nvfp4_swiglu(x, gate, up, cols=None, chunk=1024):
+    """h = silu(x @ Wg~) * (x @ Wu~) in float64.
+
+    gate, up: (codes [F][K/2], scales [F][K/16], g) -- two NVFP4 weights of
+    the same shape, each with its own per-tensor scale.  The GEMMs are the
+    plain definitions above; the activation acts on the exact (float64)
+    projections, since the kernels apply it to their fp32 sums before any
+    rounding to fp16."""
+    yg = nvfp4_gemm(x, gate[0], gate[1], gate[2], cols=cols, chunk=chunk)
+    yu = nvfp4_gemm(x, up[0], up[1], up[2], cols=cols, chunk=chunk)
+    return silu(yg) * yu
+
+
 def argmax_rows(y):
     """Per-row index of the maximum, ties to the lowest index; plus the normalised margin.
 

@@ -146,3 +146,56 @@ def test_compare_metrics():
     m = oracle.compare(ref + np.array([[0.0, 0.1], [0.0, 0.0]]), ref)
     assert abs(m["rel_frob"] - 0.1 / np.sqrt(26)) < 1e-15
     assert abs(m["row_max"] - 0.1 / np.sqrt(12.5)) < 1e-15
+
+
+def test_silu_closed_forms():
+    """SiLU pinned by values and identities that do not use its formula:
+    sigmoid(ln 3) = 3/4, silu(z) - silu(-z) = z, silu(z) + silu(-z) =
+    z * tanh(z / 2), and the limits z (large z) and -0 (very negative z)."""
+    ln3 = np.log(3.0)
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(ln3) - 0.75 * ln3) <= 1e-15
+    assert abs(oracle.silu(-ln3) + 0.25 * ln3) <= 1e-15
+    z = np.linspace(-30.0, 30.0, 601)
+    s, t = oracle.silu(z), oracle.silu(-z)
+    assert np.allclose(s - t, z, rtol=0, atol=1e-13)
+    assert np.allclose(s + t, z * np.tanh(z / 2), rtol=0, atol=1e-13)
+    assert oracle.silu(40.0) == 40.0
+    big_neg = oracle.silu(-800.0)
+    assert big_neg == 0.0 and np.signbit(big_neg)
+
+
+def test_nvfp4_swiglu_brute_force():
+    """h = silu(gate) * up against exact rational gate and up sums with the
+    activation taken in Python's math library, on tiny shapes."""
+    import math
+    for M, K, F, seed in [(1, 32, 3, 3), (4, 48, 5, 4), (8, 64, 2, 5)]:
+        w, x = synth.draw(M, K, 2 * F, seed=seed)
+        gate = oracle.nvfp4_quantize(w[:, :F])
+        up = oracle.nvfp4_quantize(w[:, F:])
+        h = oracle.nvfp4_swiglu(x, gate, up)
+        assert h.shape == (M, F)
+        for m in range(M):
+            for f in range(F):
+                val = []
+                for codes, scales, g in (gate, up):
+                    tot = Fraction(0)
+                    for k in range(K):
+                        byte = int(codes[f, k // 2])
+                        c = byte & 15 if k % 2 == 0 else byte >> 4
+                        tot += Fraction(float(x[m, k])) * _frac_e2m1(c) * _frac_e4m3(int(scales[f, k // 16]))
+                    val.append(float(tot * Fraction(float(g))))
+                a, b = val
+                want = a / (1.0 + math.exp(-a)) * b
+                assert abs(want - h[m, f]) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_nvfp4_swiglu_zero_halves():
+    """A zero gate gives silu(0) * up = 0; a zero up gives 0 whatever the gate."""
+    M, K, F = 3, 64, 4
+    w, x = synth.draw(M, K, 2 * F, seed=6)
+    gate = oracle.nvfp4_quantize(w[:, :F])
+    up = oracle.nvfp4_quantize(w[:, F:])
+    zero = oracle.nvfp4_quantize(np.zeros((K, F), np.float32))
+    assert np.all(oracle.nvfp4_swiglu(x, zero, up) == 0.0)
+    assert np.all(oracle.nvfp4_swiglu(x, gate, zero) == 0.0)
