@@ -7,12 +7,13 @@ scales) per step divided by the time per step, with every input already
 resident in HBM.  The headline workload is the NVFP4 GEMV at M = 1,
 K = 5120, N = 17408 (an MLP up-projection at decode): one step is one
 nvfp4_gemm call.  The same line also carries the two NVFP4 M = 8 shapes (fused
-gate+up 5120 x 34816 and down 17408 x 5120), timed the same way, and for each
+gate+up 5120 x 34816 and down 17408 x 5120) and the gate+up shape with the
+fused SwiGLU epilogue (nvfp4_gemm_swiglu, h[8, 17408]), timed the same way, and for each
 shape the measured read ceiling: the library's read probe (skinny_read_probe,
 one 9 KiB block per wavefront like one packed unit) over the same rotating
 copies, plus the probe over a 2 GiB buffer.
 
-    python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head] [--M m]
+    python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head|gate_up_swiglu] [--M m]
 
 Each step reads a different one of R byte-identical copies of the weights
 (R copies exceed 600 MB) so that the 256 MB Infinity Cache cannot serve them.
@@ -63,6 +64,8 @@ def log(msg):
 
 
 def describe(case, name):
+    if case["fmt"] == "swiglu":
+        return f"NVFP4 W4A16 {name} M={case['M']} K={case['K']} F={case['F']} (gate and up, h = silu(gate) * up)"
     fmt = "NVFP4 W4A16" if case["fmt"] == "nvfp4" else "FP8 E4M3 W8A16"
     extra = " + fused argmax" if name == "lm_head" else ""
     return f"{fmt} {name} M={case['M']} K={case['K']} N={case['N']}{extra}"
@@ -193,7 +196,8 @@ def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_p
     fmt, ms, K, N = synth.WORKLOADS[name]
     M = M or max(ms)
     t = time.perf_counter()
-    case = workload.nvfp4_case(M, K, N) if fmt == "nvfp4" else workload.fp8_case(M, K, N)
+    case = (workload.nvfp4_case(M, K, N) if fmt == "nvfp4" else
+            workload.swiglu_case(M, K, N) if fmt == "swiglu" else workload.fp8_case(M, K, N))
     log(f"prepared {describe(case, name)} in {time.perf_counter() - t:.1f} s")
     wbytes = case["weight_bytes"]
     R = max(2, math.ceil(MIN_ROTATION_BYTES / wbytes))
@@ -202,13 +206,14 @@ def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_p
     x = dev(case["x"])
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     idx = torch.empty((M,), dtype=torch.int32, device="cuda")
-    if fmt == "nvfp4":
+    if fmt in ("nvfp4", "swiglu"):
         copies = [dev(case["blob"]) for _ in range(R)]
         scales = None
     else:
         copies = [dev(case["codes"]) for _ in range(R)]
         scales = dev(case["scales"])
-    op = sk.OP_LM_HEAD if name == "lm_head" else (sk.OP_NVFP4 if fmt == "nvfp4" else sk.OP_FP8)
+    op = (sk.OP_LM_HEAD if name == "lm_head" else sk.OP_SWIGLU if fmt == "swiglu" else
+          sk.OP_NVFP4 if fmt == "nvfp4" else sk.OP_FP8)
     ws = torch.zeros(max(sk.workspace_bytes(op, M, K, N, cfg), 256), dtype=torch.uint8, device="cuda")
     wsp, wsn = ws.data_ptr(), ws.numel()
     xp, yp = x.data_ptr(), y.data_ptr()
@@ -221,6 +226,9 @@ def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_p
         elif op == sk.OP_NVFP4:
             st = (L.nvfp4_gemm_config(w, xp, yp, M, K, N, wsp, wsn, s, *cfg) if cfg
                   else L.nvfp4_gemm(w, xp, yp, M, K, N, wsp, wsn, s))
+        elif op == sk.OP_SWIGLU:   # N is F here; y holds h[M, F]
+            st = (L.nvfp4_gemm_swiglu_config(w, xp, yp, M, K, N, wsp, wsn, s, *cfg) if cfg
+                  else L.nvfp4_gemm_swiglu(w, xp, yp, M, K, N, wsp, wsn, s))
         else:
             st = (L.fp8_gemm_config(w, scales.data_ptr(), xp, yp, M, K, N, wsp, wsn, s, *cfg) if cfg
                   else L.fp8_gemm(w, scales.data_ptr(), xp, yp, M, K, N, wsp, wsn, s))
@@ -270,8 +278,8 @@ def main():
                          large_probe=True)
     companions = []
     if not args.headline_only and args.workload == "up" and cfg is None:
-        for name in ("gate_up", "down"):
-            r, _ = measure(name, 8, None, args.steps, args.warmup, ceiling=True)
+        for name in ("gate_up", "down", "gate_up_swiglu"):
+            r, _ = measure(name, 8, None, args.steps, args.warmup, ceiling=name != "gate_up_swiglu")
             companions.append(r)
     value = head["GB/s"]
     out = {

@@ -16,7 +16,7 @@ import numpy as np
 from ._lib import lib
 
 OK, EINVAL, ESHAPE, EALIGN, ESIZE, EHIP, EFORMAT = range(7)
-OP_NVFP4, OP_FP8, OP_LM_HEAD = 0, 1, 2
+OP_NVFP4, OP_FP8, OP_LM_HEAD, OP_SWIGLU = 0, 1, 2, 3
 ENGINE_VALU, ENGINE_MFMA, ENGINE_STREAM = 0, 1, 2
 
 
@@ -119,6 +119,31 @@ def nvfp4_pack(codes, scales, g, K, N):
     return out
 
 
+def nvfp4_pack_swiglu(gate, up, K, F):
+    """Pack a gate/up pair for nvfp4_gemm_swiglu.  gate, up: (codes [F][K/2], scales [F][K/16], g)
+    canonical NVFP4 arrays (host) with their own per-tensor scales.  Returns the host uint8 blob of
+    N = 16 * ceil(F / 8) columns, gate and up interleaved by eight (see nvfp4_pack_swiglu in skinny.h)."""
+    arrs = []
+    for codes, scales, g in (gate, up):
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        if codes.size < F * (K // 2) or scales.size < F * (K // 16):
+            raise ValueError("codes/scales smaller than F x K/2 / F x K/16")
+        arrs.append((codes, scales, float(g)))
+    (gc, gs, gg), (uc, us, ug) = arrs
+    size = ctypes.c_size_t(0)
+    args = (_host_ptr(gc), _host_ptr(gs), gg, _host_ptr(uc), _host_ptr(us), ug, K, F)
+    _check(lib().nvfp4_pack_swiglu(*args, None, ctypes.byref(size)), "nvfp4_pack_swiglu")
+    out = np.zeros(size.value, np.uint8)
+    _check(lib().nvfp4_pack_swiglu(*args, _host_ptr(out), ctypes.byref(size)), "nvfp4_pack_swiglu")
+    return out
+
+
+def swiglu_packed_cols(F):
+    """Columns of the packed blob of a SwiGLU pair of F columns each."""
+    return 16 * (-(-F // 8))
+
+
 def packed_bytes(K, N):
     size = ctypes.c_size_t(0)
     dummy = np.zeros(1, np.uint8)
@@ -157,6 +182,28 @@ def nvfp4_gemm(w_packed, x, y, K=None, N=None, workspace=None, stream=None, conf
         st = lib().nvfp4_gemm_config(wp, xp, yp, M, K, N, ws, wsb, _stream(stream), *config)
     _check(st, "nvfp4_gemm")
     return y
+
+
+def nvfp4_gemm_swiglu(w_packed, x, h, workspace=None, stream=None, config=None):
+    """h[M, F] fp16 = silu(x . Wg~) * (x . Wu~); w_packed: CUDA uint8 blob from nvfp4_pack_swiglu.
+
+    config: optional (engine, ct, nw, ksplit) for the packed blob's 16 * ceil(F / 8) columns.
+    workspace: CUDA uint8 tensor of at least workspace_bytes(OP_SWIGLU, M, K, F, config) bytes."""
+    import torch
+    M, K = x.shape
+    F = h.shape[-1]
+    _shape_checks(x, M, K, h, F, "h")
+    if w_packed.numel() < packed_bytes(K, swiglu_packed_cols(F)):
+        raise ValueError("w_packed is smaller than the SwiGLU blob for this K, F")
+    wp = _dev(w_packed, torch.uint8, "w_packed")
+    xp, hp = _dev(x, torch.float16, "x"), _dev(h, torch.float16, "h")
+    ws, wsb = _workspace(workspace, workspace_bytes(OP_SWIGLU, M, K, F, config), "nvfp4_gemm_swiglu")
+    if config is None:
+        st = lib().nvfp4_gemm_swiglu(wp, xp, hp, M, K, F, ws, wsb, _stream(stream))
+    else:
+        st = lib().nvfp4_gemm_swiglu_config(wp, xp, hp, M, K, F, ws, wsb, _stream(stream), *config)
+    _check(st, "nvfp4_gemm_swiglu")
+    return h
 
 
 def fp8_gemm(w, block_scales, x, y, workspace=None, stream=None, config=None):

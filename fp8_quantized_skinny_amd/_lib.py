@@ -16,6 +16,10 @@ def _declare(lib):
         "nvfp4_pack": (c_int, [P, P, c_float, c_int, c_int, P, ctypes.POINTER(c_size_t)]),
         "nvfp4_gemm": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
         "nvfp4_gemm_config": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int, c_int]),
+        "nvfp4_pack_swiglu": (c_int, [P, P, c_float, P, P, c_float, c_int, c_int, P, ctypes.POINTER(c_size_t)]),
+        "nvfp4_gemm_swiglu": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
+        "nvfp4_gemm_swiglu_config": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P,
+                                             c_int, c_int, c_int, c_int]),
         "fp8_gemm": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
         "fp8_gemm_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int, c_int]),
         "lm_head_gemm_argmax": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
@@ -49,4 +53,5 @@ def lib():
 EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp4_quantize",
             "fp8_quantize", "skinny_workspace_bytes", "skinny_strerror", "nvfp4_gemm_config",
             "fp8_gemm_config", "lm_head_gemm_argmax_config", "skinny_workspace_bytes_config",
-            "skinny_config_supported", "skinny_read_probe")
+            "skinny_config_supported", "skinny_read_probe", "nvfp4_pack_swiglu", "nvfp4_gemm_swiglu",
+            "nvfp4_gemm_swiglu_config")

@@ -80,6 +80,11 @@ __device__ __forceinline__ void lds_copy_barrier(bool pending) {
   asm volatile("" ::: "memory");
 }
 
+// SiLU in fp32, v * sigmoid(v), the activation of a SwiGLU MLP (Shazeer,
+// "GLU Variants Improve Transformer").  exp(-v) overflows to inf for
+// v < -88, which gives the right limit -0.
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

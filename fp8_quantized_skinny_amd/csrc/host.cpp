@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 #include <thread>
 #include <vector>
@@ -167,6 +168,12 @@ LaunchCfg default_fp8_cfg(int M, int K, int N) {
   return pick_whole_k_cfg(1, ku, fits);
 }
 
+// A SwiGLU pair of F columns each packs to swiglu_packed_cols(F) <= kMaxN columns.
+int swiglu_shape(int M, int K, int F) {
+  if (F < 1 || F > kMaxN / 2) return SKINNY_ESHAPE;
+  return check_shape(M, K, F);
+}
+
 int nvfp4_common_checks(const void* w_packed, const uint16_t* x, const void* out, int M, int K, int N) {
   if (!w_packed || !x || !out) return SKINNY_EINVAL;
   int s = check_shape(M, K, N);
@@ -268,6 +275,10 @@ size_t skinny_workspace_bytes_config(int op, int M, int K, int N, int engine, in
     case 0: return nvfp4_cfg_supported(c, M, K, false) ? nvfp4_workspace_layout(c, M, K, N, false).total : 0;
     case 1: return fp8_cfg_supported(c, M, K) ? fp8_workspace_layout(c, M, K, N).total : 0;
     case 2: return nvfp4_cfg_supported(c, M, K, true) ? nvfp4_workspace_layout(c, M, K, N, true).total : 0;
+    case 3:
+      return swiglu_shape(M, K, N) == SKINNY_OK && nvfp4_cfg_supported(c, M, K, false)
+                 ? nvfp4_workspace_layout(c, M, K, swiglu_packed_cols(N), false).total
+                 : 0;
     default: return 0;
   }
 }
@@ -279,6 +290,7 @@ int skinny_config_supported(int op, int M, int K, int N, int engine, int ct, int
     case 0: return nvfp4_cfg_supported(c, M, K, false) ? 1 : 0;
     case 1: return fp8_cfg_supported(c, M, K) ? 1 : 0;
     case 2: return nvfp4_cfg_supported(c, M, K, true) ? 1 : 0;
+    case 3: return swiglu_shape(M, K, N) == SKINNY_OK && nvfp4_cfg_supported(c, M, K, false) ? 1 : 0;
     default: return 0;
   }
 }
@@ -296,26 +308,33 @@ size_t skinny_workspace_bytes(int op, int M, int K, int N) {
     case 0: return nvfp4_workspace_layout(default_nvfp4_cfg(M, K, N, false), M, K, N, false).total;
     case 1: return fp8_workspace_layout(default_fp8_cfg(M, K, N), M, K, N).total;
     case 2: return nvfp4_workspace_layout(default_nvfp4_cfg(M, K, N, true), M, K, N, true).total;
+    case 3: {
+      if (swiglu_shape(M, K, N)) return 0;
+      const int Np = swiglu_packed_cols(N);
+      return nvfp4_workspace_layout(default_nvfp4_cfg(M, K, Np, false), M, K, Np, false).total;
+    }
     default: return 0;
   }
 }
 
-int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float gscale, int K, int N,
-               void* out, size_t* out_bytes) {
-  if (!codes || !scales || !out_bytes) return SKINNY_EINVAL;
-  if (K < 16 || K % 16 != 0 || K > kMaxK || N < 1 || N > kMaxN) return SKINNY_ESHAPE;
-  if (!std::isfinite(gscale) || gscale < 0.0f) return SKINNY_EINVAL;
-  const Geometry geo = nvfp4_geometry(K, N);
-  if (!out) {
-    *out_bytes = geo.total_bytes;
-    return SKINNY_OK;
-  }
-  if (*out_bytes < geo.total_bytes) return SKINNY_ESIZE;
-  const size_t nscale = static_cast<size_t>(N) * (K / 16);
-  for (size_t i = 0; i < nscale; ++i)
-    if ((scales[i] & 0x7F) == 0x7F) return SKINNY_EFORMAT;
+}  // extern "C"
 
-  uint8_t* blob = static_cast<uint8_t*>(out);
+namespace {
+
+static_assert(offsetof(Nvfp4Header, g) == kGOffset && offsetof(Nvfp4Header, g2) == kG2Offset,
+              "header field offsets");
+
+bool has_nan_scale(const uint8_t* scales, size_t n) {
+  for (size_t i = 0; i < n; ++i)
+    if ((scales[i] & 0x7F) == 0x7F) return true;
+  return false;
+}
+
+// Writes the header and the span-major units of canonical codes [N][K/2] and
+// scales [N][K/16] into blob (geo.total_bytes, zeroed here first).
+void write_blob(const uint8_t* codes, const uint8_t* scales, int K, int N, float g, float g2, uint32_t kind,
+                int F, uint8_t* blob) {
+  const Geometry geo = nvfp4_geometry(K, N);
   std::memset(blob, 0, geo.total_bytes);
   Nvfp4Header h{};
   h.magic = kBlobMagic;
@@ -325,9 +344,12 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float gscale, int K,
   h.ku = geo.ku;
   h.nt = geo.nt;
   h.unit_bytes = kUnitBytes;
-  h.g = gscale;
+  h.g = g;
   h.units_off = kHeaderBytes;
   h.units_bytes = geo.units_bytes;
+  h.g2 = g2;
+  h.kind = kind;
+  h.F = static_cast<uint32_t>(F);
   std::memcpy(blob, &h, sizeof(h));
 
   const size_t row_codes = K / 2, row_scales = K / 16;
@@ -351,6 +373,59 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float gscale, int K,
       }
     }
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float gscale, int K, int N,
+               void* out, size_t* out_bytes) {
+  if (!codes || !scales || !out_bytes) return SKINNY_EINVAL;
+  if (K < 16 || K % 16 != 0 || K > kMaxK || N < 1 || N > kMaxN) return SKINNY_ESHAPE;
+  if (!std::isfinite(gscale) || gscale < 0.0f) return SKINNY_EINVAL;
+  const Geometry geo = nvfp4_geometry(K, N);
+  if (!out) {
+    *out_bytes = geo.total_bytes;
+    return SKINNY_OK;
+  }
+  if (*out_bytes < geo.total_bytes) return SKINNY_ESIZE;
+  if (has_nan_scale(scales, static_cast<size_t>(N) * (K / 16))) return SKINNY_EFORMAT;
+  write_blob(codes, scales, K, N, gscale, gscale, kKindPlain, 0, static_cast<uint8_t*>(out));
+  *out_bytes = geo.total_bytes;
+  return SKINNY_OK;
+}
+
+int nvfp4_pack_swiglu(const uint8_t* gate_codes, const uint8_t* gate_scales, float gate_g,
+                      const uint8_t* up_codes, const uint8_t* up_scales, float up_g, int K, int F,
+                      void* out, size_t* out_bytes) {
+  if (!gate_codes || !gate_scales || !up_codes || !up_scales || !out_bytes) return SKINNY_EINVAL;
+  if (K < 16 || K % 16 != 0 || K > kMaxK || F < 1 || F > kMaxN / 2) return SKINNY_ESHAPE;
+  if (!std::isfinite(gate_g) || gate_g < 0.0f || !std::isfinite(up_g) || up_g < 0.0f) return SKINNY_EINVAL;
+  const int N = swiglu_packed_cols(F);
+  const Geometry geo = nvfp4_geometry(K, N);
+  if (!out) {
+    *out_bytes = geo.total_bytes;
+    return SKINNY_OK;
+  }
+  if (*out_bytes < geo.total_bytes) return SKINNY_ESIZE;
+  const size_t row_codes = K / 2, row_scales = K / 16;
+  if (has_nan_scale(gate_scales, static_cast<size_t>(F) * row_scales) ||
+      has_nan_scale(up_scales, static_cast<size_t>(F) * row_scales))
+    return SKINNY_EFORMAT;
+  // Canonical arrays of the interleaved N columns: packed column 16t + c is
+  // gate column 8t + c (c < 8) or up column 8t + c - 8, zero past F.
+  std::vector<uint8_t> codes(static_cast<size_t>(N) * row_codes, 0), scales(static_cast<size_t>(N) * row_scales, 0);
+  for (int n = 0; n < N; ++n) {
+    const int c = n % kTileCols, f = (n / kTileCols) * 8 + (c & 7);
+    if (f >= F) continue;
+    const uint8_t* sc = c < 8 ? gate_codes : up_codes;
+    const uint8_t* ss = c < 8 ? gate_scales : up_scales;
+    std::memcpy(codes.data() + static_cast<size_t>(n) * row_codes, sc + static_cast<size_t>(f) * row_codes, row_codes);
+    std::memcpy(scales.data() + static_cast<size_t>(n) * row_scales, ss + static_cast<size_t>(f) * row_scales,
+                row_scales);
+  }
+  write_blob(codes.data(), scales.data(), K, N, gate_g, up_g, kKindSwiglu, F, static_cast<uint8_t*>(out));
   *out_bytes = geo.total_bytes;
   return SKINNY_OK;
 }
@@ -490,6 +565,32 @@ int fp8_gemm(const uint8_t* w, const float* block_scales, const uint16_t* x, uin
   const LaunchCfg c = default_fp8_cfg(M, K, N);
   return fp8_gemm_config(w, block_scales, x, y, M, K, N, workspace, workspace_bytes, stream,
                          c.engine, c.ct, c.nw, c.ksplit);
+}
+
+int nvfp4_gemm_swiglu_config(const void* w_packed, const uint16_t* x, uint16_t* h, int M, int K, int F,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream, int engine, int ct,
+                             int nw, int ksplit) {
+  int s = swiglu_shape(M, K, F);
+  if (s) return s;
+  s = nvfp4_common_checks(w_packed, x, h, M, K, F);
+  if (s) return s;
+  if (!aligned(h, 16)) return SKINNY_EALIGN;
+  const int N = swiglu_packed_cols(F);
+  const LaunchCfg cfg{engine, ct, nw, ksplit};
+  if (!nvfp4_cfg_supported(cfg, M, K, false)) return SKINNY_EINVAL;
+  s = check_workspace(workspace, workspace_bytes, nvfp4_workspace_layout(cfg, M, K, N, false).total);
+  if (s) return s;
+  return launch_status(launch_nvfp4(static_cast<const uint8_t*>(w_packed), x, h, M, K, N, cfg, nullptr,
+                                    workspace, stream, F));
+}
+
+int nvfp4_gemm_swiglu(const void* w_packed, const uint16_t* x, uint16_t* h, int M, int K, int F,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int s = swiglu_shape(M, K, F);
+  if (s) return s;
+  const LaunchCfg c = default_nvfp4_cfg(M, K, swiglu_packed_cols(F), false);
+  return nvfp4_gemm_swiglu_config(w_packed, x, h, M, K, F, workspace, workspace_bytes, stream, c.engine, c.ct,
+                                  c.nw, c.ksplit);
 }
 
 int lm_head_gemm_argmax_config(const void* w_packed, const uint16_t* x, int32_t* idx,

@@ -33,9 +33,16 @@ namespace skinny {
 //
 // K is padded to a multiple of 1024 and N to a multiple of 16 with zero codes
 // and zero scales, so padded weights are exactly 0.
+//
+// A SwiGLU pair blob (kind 1) holds two weights of F columns each, gate and
+// up, interleaved by eight: tile t has gate columns 8t .. 8t+7 as its columns
+// 0..7 and up columns 8t .. 8t+7 as its columns 8..15 (zero past F), so
+// N = 16 * ceil(F / 8) and every gate column meets its up column in the same
+// wavefront, eight lanes apart.  g is the gate's per-tensor scale, g2 the
+// up's.  A plain blob (kind 0) has g2 = g.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kBlobMagic = 0x344E4B53u;  // "SKN4" little-endian
-constexpr uint32_t kBlobVersion = 3;
+constexpr uint32_t kBlobVersion = 4;
 constexpr size_t kHeaderBytes = 256;
 constexpr int kTileCols = 16;
 constexpr int kChunkK = 128;
@@ -53,9 +60,16 @@ struct Nvfp4Header {
   uint32_t unit_bytes;
   float g;      // per-tensor scale; byte offset 28
   uint64_t units_off, units_bytes;
+  float g2;       // up scale of a SwiGLU pair (= g otherwise); byte offset 48
+  uint32_t kind;  // 0 plain, 1 SwiGLU pair
+  uint32_t F;     // SwiGLU pair: columns of each of gate and up (0 otherwise)
 };
 static_assert(sizeof(Nvfp4Header) <= kHeaderBytes, "header too large");
 constexpr size_t kGOffset = 28;
+constexpr size_t kG2Offset = 48;
+constexpr uint32_t kKindPlain = 0, kKindSwiglu = 1;
+// Columns of the packed blob of a SwiGLU pair of F columns each.
+constexpr int swiglu_packed_cols(int F) { return 16 * ((F + 7) / 8); }
 
 struct Geometry {
   int ku, nt;
@@ -84,9 +98,11 @@ WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N
 WorkspaceLayout fp8_workspace_layout(const LaunchCfg& cfg, int M, int K, int N);
 
 // Kernel launchers (defined in the .hip files).  Arguments are validated.
+// swiglu_F > 0: the blob is a SwiGLU pair of swiglu_F columns each (N is its
+// packed column count) and y is h[M][swiglu_F] = silu(gate) * up.
 hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y,
                         int M, int K, int N, const LaunchCfg& cfg,
-                        int32_t* idx, void* workspace, hipStream_t stream);
+                        int32_t* idx, void* workspace, hipStream_t stream, int swiglu_F = 0);
 hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x,
                       uint16_t* y, int M, int K, int N, const LaunchCfg& cfg,
                       void* workspace, hipStream_t stream);
@@ -117,6 +133,11 @@ hipError_t launch_finalize(const float* part, int ksplit, int M, int N, const fl
                            unsigned long long* cand, hipStream_t stream);
 hipError_t launch_argmax_reduce(const unsigned long long* cand, int groups, int M, int32_t* idx,
                                 hipStream_t stream);
+// Second pass of a K split of a SwiGLU pair: h[m][f] = silu(g * gate) * (g2 *
+// up), both sums taken over the splits in order from part[split][m][n] of
+// the packed columns (n = 16 * (f / 8) + f % 8 and n + 8).
+hipError_t launch_finalize_swiglu(const float* part, int ksplit, int M, int N, int F, const float* gptr,
+                                  const float* g2ptr, uint16_t* h, hipStream_t stream);
 
 // Largest row count (the target token plus seven drafts).
 constexpr int kMaxRows = 8;

@@ -60,7 +60,21 @@ struct Nvfp4Args {
   int ku, nt, ksplit, S;     // S: K spans per workgroup
   float* part;               // [ksplit][M][N] fp32 partial sums (ksplit > 1)
   unsigned long long* cand;  // [gridDim.x][M] argmax candidates (lm_head, ksplit == 1)
+  const float* g2ptr;        // SwiGLU pair: the up projection's scale
+  int F;                     // SwiGLU pair: output columns (y is h[M][F])
 };
+
+// What a kernel does with its finished fp32 tile sums.
+enum : int { kEpiPlain = 0, kEpiArgmax = 1, kEpiSwiglu = 2 };
+
+// SwiGLU of a pair-interleaved tile: the lane of gate column c < 8 takes its
+// up sum from lane c + 8 (same row group) and returns silu(g * gate) * (g2 *
+// up); lanes c >= 8 get a value that is never stored.  Every lane of the
+// 16-lane row must execute this.
+__device__ __forceinline__ float swiglu_pair(float sum, float g, float g2) {
+  const float up = __shfl_xor(sum, 8);
+  return silu(g * sum) * (g2 * up);
+}
 
 // This wavefront's unit and its workgroup's geometry (wave-uniform values).
 struct Plan {
@@ -136,7 +150,7 @@ SKINNY_BLOCK_DOT(block_dot_lo, 0, 1, 2, 3, 4, 5, 6, 7)
 SKINNY_BLOCK_DOT(block_dot_hi, 8, 9, 10, 11, 12, 13, 14, 15)
 #undef SKINNY_BLOCK_DOT
 
-template <int CT>
+template <int CT, bool SWIGLU>
 __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu_m1(Nvfp4Args a) {
   __shared__ float red[kMaxWaves][16];
   const Plan P(a, CT);
@@ -174,7 +188,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu_m1(Nvfp4Args a) {
     float tot = 0.0f;
     for (int s = 0; s < P.sw; ++s) tot += red[P.wave * P.S + s][P.lane];
     const int n = (P.tile0 + P.wave) * kTileCols + P.lane;
-    if (n < a.N) {
+    if (SWIGLU && a.ksplit == 1) {  // lanes 0..15 of the wavefront are all here
+      const float h = swiglu_pair(tot, *a.gptr, *a.g2ptr);
+      const int f = (P.tile0 + P.wave) * 8 + P.lane;
+      if (P.lane < 8 && f < a.F) a.y[f] = static_cast<_Float16>(h);
+    } else if (n < a.N) {
       if (a.ksplit > 1)
         a.part[static_cast<size_t>(blockIdx.y) * a.N + n] = tot;
       else
@@ -247,7 +265,7 @@ __device__ __forceinline__ void mfma_steps(const u32x4 (&c)[kChunksPerUnit], con
   }
 }
 
-template <int CT, bool ARGMAX>
+template <int CT, int EPI>
 __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const Plan P(a, CT);
@@ -300,6 +318,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
   }
 
   const float g = *a.gptr;
+  if (EPI == kEpiSwiglu) {  // lanes 0..31 of the wavefront are all in `fin` or none
+    if (fin) {
+      const float g2 = *a.g2ptr;
+      const int f = (P.tile0 + P.wave) * 8 + cl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = grp * 4 + i;
+        const float h = swiglu_pair(tot[i], g, g2);
+        if (cl < 8 && m < a.M && f < a.F) a.y[static_cast<size_t>(m) * a.F + f] = static_cast<_Float16>(h);
+      }
+    }
+    return;
+  }
   unsigned long long key[4] = {0ull, 0ull, 0ull, 0ull};
   if (fin && n < a.N) {
 #pragma unroll
@@ -312,7 +343,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
       }
     }
   }
-  if (ARGMAX) {
+  if (EPI == kEpiArgmax) {
     // Largest key over the 16 columns of each row group, then over the
     // workgroup's tiles: one candidate per row.
     __shared__ unsigned long long best[kMaxWaves][kMaxRows];
@@ -390,7 +421,7 @@ struct StreamCtx {
   unsigned long long* best;  // LDS [kMaxRows] running argmax keys of this wavefront
   const uint8_t* spare;      // unit 0 of the blob (this lane's 16 bytes): read in place of a unit past the last tile
   int t0, step, ntiles, lane;
-  float g;
+  float g, g2;
 };
 
 // Unit J of this wavefront's tile `ti`, whose unit 0 (this lane's 16 bytes)
@@ -404,7 +435,7 @@ struct StreamCtx {
 // boundary.  After the tile's last span the tile is stored and its logits
 // are folded into the wavefront's running argmax keys (kept in LDS, not in
 // registers, which the two units in flight already fill).
-template <int KU, int J, int PAR, bool ARGMAX>
+template <int KU, int J, int PAR, int EPI>
 __device__ __forceinline__ void stream_units(const StreamCtx& c, Unit& A, Unit& B, int ti, const uint8_t* base,
                                              f32x4& acc) {
   if constexpr (J < KU) {
@@ -419,10 +450,21 @@ __device__ __forceinline__ void stream_units(const StreamCtx& c, Unit& A, Unit& 
     __builtin_amdgcn_sched_barrier(0);
     mfma_unit_lean<0>(cur, acc, c.xbase + J * kUnitK);
     __builtin_amdgcn_sched_barrier(0);
-    stream_units<KU, J + 1, 1 - PAR, ARGMAX>(c, A, B, ti, base, acc);
+    stream_units<KU, J + 1, 1 - PAR, EPI>(c, A, B, ti, base, acc);
   } else {
     const Nvfp4Args& a = *c.a;
     const int cl = c.lane & 15, grp = c.lane >> 4;
+    if (EPI == kEpiSwiglu) {  // every lane is here: pair up gate and up columns
+      const int f = (c.t0 + ti * c.step) * 8 + cl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = grp * 4 + i;
+        const float h = swiglu_pair(acc[i], c.g, c.g2);
+        if (c.lane < 32 && cl < 8 && m < a.M && f < a.F) a.y[static_cast<size_t>(m) * a.F + f] = static_cast<_Float16>(h);
+      }
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      return;
+    }
     const int n = (c.t0 + ti * c.step) * kTileCols + cl;
     const bool col_ok = c.lane < 32 && n < a.N;
 #pragma unroll
@@ -431,7 +473,7 @@ __device__ __forceinline__ void stream_units(const StreamCtx& c, Unit& A, Unit& 
       const bool ok = col_ok && m < a.M;
       const float v = c.g * acc[i];
       if (ok && a.y) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(v);
-      if (ARGMAX) {
+      if (EPI == kEpiArgmax) {
         const unsigned long long k = wave_max_key<16>(ok ? argmax_key(v, n) : 0ull);
         if (c.lane < 32 && cl == 0) c.best[grp * 4 + i] = k > c.best[grp * 4 + i] ? k : c.best[grp * 4 + i];
       }
@@ -440,7 +482,7 @@ __device__ __forceinline__ void stream_units(const StreamCtx& c, Unit& A, Unit& 
   }
 }
 
-template <int KU, bool ARGMAX>
+template <int KU, int EPI>
 __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_stream(Nvfp4Args a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int lane = threadIdx.x & 63;
@@ -459,12 +501,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_stream(Nvfp4Args a) {
   c.span_stride = static_cast<size_t>(a.nt) * kUnitBytes;
   c.tile_stride = static_cast<size_t>(c.step) * kUnitBytes;
   c.g = *a.gptr;
+  c.g2 = EPI == kEpiSwiglu ? *a.g2ptr : 0.0f;
   c.xbase = xs + min(lane & 15, a.M - 1) * RS + (lane >> 4) * 32;
   c.best = best + wave * kMaxRows;
   c.spare = a.units + lane * 16;
 
   stage_x_all(a, xs, RS, wave, nw, lane);
-  if (ARGMAX && lane < kMaxRows) c.best[lane] = 0ull;
+  if (EPI == kEpiArgmax && lane < kMaxRows) c.best[lane] = 0ull;
   Unit A, B;
   const uint8_t* base = a.units + static_cast<size_t>(c.t0) * kUnitBytes + lane * 16;
   load_unit(A, c.ntiles > 0 ? base : c.spare);
@@ -477,14 +520,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_stream(Nvfp4Args a) {
   // second tile of a pair starts in B.  An odd last tile follows the loop.
   int ti = 0;
   for (; ti + 1 < c.ntiles; ti += 2) {
-    stream_units<KU, 0, 0, ARGMAX>(c, A, B, ti, base, acc);
+    stream_units<KU, 0, 0, EPI>(c, A, B, ti, base, acc);
     base += c.tile_stride;
-    stream_units<KU, 0, KU % 2, ARGMAX>(c, A, B, ti + 1, base, acc);
+    stream_units<KU, 0, KU % 2, EPI>(c, A, B, ti + 1, base, acc);
     base += c.tile_stride;
   }
-  if (ti < c.ntiles) stream_units<KU, 0, 0, ARGMAX>(c, A, B, ti, base, acc);
+  if (ti < c.ntiles) stream_units<KU, 0, 0, EPI>(c, A, B, ti, base, acc);
 
-  if (ARGMAX) {
+  if (EPI == kEpiArgmax) {
     // Largest key per row over the workgroup's wavefronts.
     __syncthreads();
     if (threadIdx.x < static_cast<unsigned>(a.M)) {
@@ -538,23 +581,30 @@ bool nvfp4_cfg_supported(const LaunchCfg& c, int M, int K, bool argmax) {
   return nvfp4_mfma_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
 }
 
-#define SKINNY_NVFP4_DISPATCH(CT)                                                   \
-  if (cfg.ct == CT) {                                                               \
-    if (cfg.engine == 0) return launch(nvfp4_valu_m1<CT>, grid, cfg.nw, 0, a, stream); \
-    if (argmax && cfg.ksplit == 1) return launch(nvfp4_mfma<CT, true>, grid, cfg.nw, lds, a, stream); \
-    return launch(nvfp4_mfma<CT, false>, grid, cfg.nw, lds, a, stream);            \
+#define SKINNY_NVFP4_DISPATCH(CT)                                                                       \
+  if (cfg.ct == CT) {                                                                                   \
+    if (cfg.engine == 0)                                                                                \
+      return epi == kEpiSwiglu ? launch(nvfp4_valu_m1<CT, true>, grid, cfg.nw, 0, a, stream)            \
+                               : launch(nvfp4_valu_m1<CT, false>, grid, cfg.nw, 0, a, stream);          \
+    if (epi == kEpiArgmax && cfg.ksplit == 1)                                                           \
+      return launch(nvfp4_mfma<CT, kEpiArgmax>, grid, cfg.nw, lds, a, stream);                          \
+    if (epi == kEpiSwiglu && cfg.ksplit == 1)                                                           \
+      return launch(nvfp4_mfma<CT, kEpiSwiglu>, grid, cfg.nw, lds, a, stream);                          \
+    return launch(nvfp4_mfma<CT, kEpiPlain>, grid, cfg.nw, lds, a, stream);                             \
   }
 
 namespace {
 
-hipError_t launch_gemm(const Nvfp4Args& a, const LaunchCfg& cfg, bool argmax, hipStream_t stream) {
+hipError_t launch_gemm(const Nvfp4Args& a, const LaunchCfg& cfg, int epi, hipStream_t stream) {
   if (cfg.engine == 2) {
     const dim3 grid(nvfp4_stream_groups(cfg, a.N));
     const size_t lds = nvfp4_stream_lds_bytes(a.M, a.K, cfg.nw);
     switch (a.ku) {
 #define SKINNY_STREAM_KU(KU) \
   case KU:                   \
-    return argmax ? launch(nvfp4_stream<KU, true>, grid, cfg.nw, lds, a, stream) : launch(nvfp4_stream<KU, false>, grid, cfg.nw, lds, a, stream);
+    return epi == kEpiArgmax   ? launch(nvfp4_stream<KU, kEpiArgmax>, grid, cfg.nw, lds, a, stream) \
+           : epi == kEpiSwiglu ? launch(nvfp4_stream<KU, kEpiSwiglu>, grid, cfg.nw, lds, a, stream) \
+                               : launch(nvfp4_stream<KU, kEpiPlain>, grid, cfg.nw, lds, a, stream);
       SKINNY_STREAM_KU(1)
       SKINNY_STREAM_KU(2)
       SKINNY_STREAM_KU(3)
@@ -583,7 +633,7 @@ hipError_t launch_gemm(const Nvfp4Args& a, const LaunchCfg& cfg, bool argmax, hi
 #undef SKINNY_NVFP4_DISPATCH
 
 hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y, int M, int K, int N,
-                        const LaunchCfg& cfg, int32_t* idx, void* workspace, hipStream_t stream) {
+                        const LaunchCfg& cfg, int32_t* idx, void* workspace, hipStream_t stream, int swiglu_F) {
   const Geometry geo = nvfp4_geometry(K, N);
   const bool argmax = idx != nullptr;
   const WorkspaceLayout wl = nvfp4_workspace_layout(cfg, M, K, N, argmax);
@@ -602,9 +652,14 @@ hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y, int
   a.S = cfg.nw / cfg.ct;
   a.part = wl.part_bytes ? reinterpret_cast<float*>(ws + wl.part_off) : nullptr;
   a.cand = argmax ? reinterpret_cast<unsigned long long*>(ws + wl.keys_off) : nullptr;
-  hipError_t e = launch_gemm(a, cfg, argmax, stream);
+  a.g2ptr = reinterpret_cast<const float*>(blob + kG2Offset);
+  a.F = swiglu_F;
+  const bool swiglu = swiglu_F > 0;
+  hipError_t e = launch_gemm(a, cfg, argmax ? kEpiArgmax : swiglu ? kEpiSwiglu : kEpiPlain, stream);
   if (e != hipSuccess) return e;
   int groups = cfg.engine == 2 ? nvfp4_stream_groups(cfg, N) : (geo.nt + cfg.ct - 1) / cfg.ct;
+  if (cfg.ksplit > 1 && swiglu)
+    return launch_finalize_swiglu(a.part, cfg.ksplit, M, N, swiglu_F, a.gptr, a.g2ptr, y, stream);
   if (cfg.ksplit > 1) {
     e = launch_finalize(a.part, cfg.ksplit, M, N, a.gptr, y, a.cand, stream);
     if (e != hipSuccess) return e;

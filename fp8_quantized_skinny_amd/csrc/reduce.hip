@@ -1,5 +1,6 @@
-// Second-pass kernels of the skinny GEMM: the K-split reduction and the
-// lm_head argmax over workgroup candidates.
+// Second-pass kernels of the skinny GEMM: the K-split reduction (plain, or
+// the SwiGLU of a gate/up pair) and the lm_head argmax over workgroup
+// candidates.
 //
 // When K is split over several workgroups, each one stores its fp32 partial
 // sums with plain stores, part[split][m][n], and exits.  finalize_splits then
@@ -100,6 +101,26 @@ __global__ __launch_bounds__(256) void argmax_reduce(const unsigned long long* c
   }
 }
 
+// SwiGLU pair of a K split: thread f of block (x, m) adds the split partials
+// of gate column 16 * (f / 8) + f % 8 and of its up column eight further on,
+// each in split order, and writes h[m][f] = silu(g * gate) * (g2 * up).
+__global__ __launch_bounds__(kFinalizeThreads) void finalize_swiglu(const float* part, int ksplit, int M, int N,
+                                                                    int F, const float* gptr, const float* g2ptr,
+                                                                    _Float16* h) {
+  const int f = blockIdx.x * kFinalizeThreads + threadIdx.x;
+  const int m = blockIdx.y;
+  if (f >= F) return;
+  const int n = (f / 8) * kTileCols + f % 8;
+  const float* p = part + static_cast<size_t>(m) * N + n;
+  const size_t stride = static_cast<size_t>(M) * N;
+  float gate = 0.0f, up = 0.0f;
+  for (int s = 0; s < ksplit; ++s) {
+    gate += p[s * stride];
+    up += p[s * stride + 8];
+  }
+  h[static_cast<size_t>(m) * F + f] = static_cast<_Float16>(silu(*gptr * gate) * (*g2ptr * up));
+}
+
 }  // namespace
 
 // Four columns per thread when N allows it, else one.
@@ -123,6 +144,14 @@ hipError_t launch_finalize(const float* part, int ksplit, int M, int N, const fl
     hipLaunchKernelGGL((finalize_splits<false, 4>), grid, block, 0, stream, part, ksplit, M, N, gptr, yh, cand);
   else
     hipLaunchKernelGGL((finalize_splits<false, 1>), grid, block, 0, stream, part, ksplit, M, N, gptr, yh, cand);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_swiglu(const float* part, int ksplit, int M, int N, int F, const float* gptr,
+                                  const float* g2ptr, uint16_t* h, hipStream_t stream) {
+  const dim3 grid((F + kFinalizeThreads - 1) / kFinalizeThreads, M), block(kFinalizeThreads);
+  hipLaunchKernelGGL(finalize_swiglu, grid, block, 0, stream, part, ksplit, M, N, F, gptr, g2ptr,
+                     reinterpret_cast<_Float16*>(h));
   return hipGetLastError();
 }
 

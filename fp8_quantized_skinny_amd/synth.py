@@ -29,6 +29,8 @@ WORKLOADS = {
     "qkv":     ("fp8", (1, 2, 4), 5120, 7168),
     "o_proj":  ("fp8", (1, 2, 4), 6144, 5120),
     "lm_head": ("nvfp4", (1, 8), 5120, 151936),
+    # the gate+up shape as a SwiGLU pair: two 5120 x 17408 projections, output h[M, 17408]
+    "gate_up_swiglu": ("swiglu", (8,), 5120, 17408),
 }
 
 

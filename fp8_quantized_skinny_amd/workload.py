@@ -7,7 +7,7 @@ result is host arrays; callers move them to the device.
 
 import numpy as np
 
-from . import nvfp4_quantize, fp8_quantize, nvfp4_pack, synth
+from . import nvfp4_quantize, fp8_quantize, nvfp4_pack, nvfp4_pack_swiglu, synth
 
 
 def nvfp4_case(M, K, N, seed=0):
@@ -20,6 +20,22 @@ def nvfp4_case(M, K, N, seed=0):
     blob = nvfp4_pack(codes, scales, g, K, N)
     return {"fmt": "nvfp4", "M": M, "K": K, "N": N, "codes": codes, "scales": scales, "g": g,
             "blob": blob, "x": x, "weight_bytes": codes.nbytes + scales.nbytes + 4}
+
+
+def swiglu_case(M, K, F, seed=0):
+    """dict for a SwiGLU pair: the fused gate+up weight [K, 2F] is drawn as for
+    nvfp4_case(M, K, 2F, seed); its first F columns are the gate projection and
+    the last F the up projection, each quantized with its own per-tensor scale."""
+    rng = np.random.default_rng(seed)
+    w = synth.draw_weights(rng, K, 2 * F)
+    x = synth.draw_activations(rng, M, K)
+    gate = nvfp4_quantize(np.ascontiguousarray(w[:, :F]))
+    up = nvfp4_quantize(np.ascontiguousarray(w[:, F:]))
+    del w
+    blob = nvfp4_pack_swiglu(gate, up, K, F)
+    nbytes = sum(a.nbytes for a in gate[:2] + up[:2]) + 8
+    return {"fmt": "swiglu", "M": M, "K": K, "F": F, "gate": gate, "up": up, "blob": blob, "x": x,
+            "weight_bytes": nbytes}
 
 
 def fp8_case(M, K, N, seed=0):

@@ -72,8 +72,8 @@ enum {
  *   out    : host buffer of *out_bytes bytes, or NULL to query the size.
  *            On success *out_bytes is set to the blob size.
  *
- * The blob starts with a 256-byte header (magic "SKN4", version, K, N, g)
- * followed by 9 KiB units, one per 16 output columns x 1024 K (K padded with
+ * The blob starts with a 256-byte header (magic "SKN4", version 4, K, N, g at
+ * byte 28, g again at byte 48, kind 0 at byte 52) followed by 9 KiB units, one per 16 output columns x 1024 K (K padded with
  * zero codes to a multiple of 1024), all tiles of the first K span, then of
  * the next: eight 1 KiB code chunks, then the unit's 1 KiB of scales, ordered
  * so that each lane of a wavefront loads 16 contiguous bytes of every chunk.  The caller copies the
@@ -83,6 +83,35 @@ enum {
  * ------------------------------------------------------------------------- */
 int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float g,
                int K, int N, void* out, size_t* out_bytes);
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_pack_swiglu -- pack the gate and up projections of a gated MLP into
+ * one blob for nvfp4_gemm_swiglu.
+ *
+ * The decode shapes fuse the MLP's gate and up projections into one GEMM
+ * over the same x (the fused gate+up shape the post's skinny GEMM serves);
+ * the next step of the MLP is h = silu(gate) * up (SwiGLU: Shazeer, "GLU
+ * Variants Improve Transformer", 2020).  Packing the pair interleaved lets
+ * the GEMM finish that step in registers and write h instead of both
+ * projections.
+ *
+ *   gate_codes, gate_scales, gate_g : canonical NVFP4 arrays of the gate
+ *            projection, F output columns (layouts and checks as nvfp4_pack).
+ *   up_codes, up_scales, up_g       : the same for the up projection.  The
+ *            two scales may differ (one per projection) or be equal (one
+ *            scale for the fused tensor).
+ *   F      : columns of each projection, 1 .. 2^23.
+ *   out, out_bytes : as nvfp4_pack.
+ *
+ * The blob is an NVFP4 blob of N = 16 * ceil(F / 8) columns: tile t holds
+ * gate columns 8t .. 8t+7 as its columns 0..7 and up columns 8t .. 8t+7 as
+ * its columns 8..15 (zero weights past F).  Its header has g = gate_g at
+ * byte 28, g2 = up_g at byte 48, kind 1 at byte 52 and F at byte 56.
+ * ------------------------------------------------------------------------- */
+int nvfp4_pack_swiglu(const uint8_t* gate_codes, const uint8_t* gate_scales,
+                      float gate_g, const uint8_t* up_codes,
+                      const uint8_t* up_scales, float up_g, int K, int F,
+                      void* out, size_t* out_bytes);
 
 /* ---------------------------------------------------------------------------
  * nvfp4_gemm -- y = x . (e2m1(q) * e4m3(s) * g), fp32 accumulate, fp16 out.
@@ -100,6 +129,25 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, float g,
 int nvfp4_gemm(const void* w_packed, const uint16_t* x, uint16_t* y,
                int M, int K, int N, void* workspace, size_t workspace_bytes,
                hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_gemm_swiglu -- h = silu(x . Wg~) * (x . Wu~), fp16 out.
+ *
+ *   w_packed  : device, blob from nvfp4_pack_swiglu for exactly this K and F
+ *               (the header is in device memory and is not checked; a plain
+ *               blob gives meaningless results).
+ *   x, M      : as for nvfp4_gemm.
+ *   h         : device, fp16 [M][F] row-major (written, never read).
+ *   workspace : scratch of at least skinny_workspace_bytes(3, M, K, F) bytes
+ *               (any contents; calls sharing one must not overlap in time).
+ *
+ * Both projections are accumulated in fp32 and scaled by their own g; the
+ * activation is applied to those fp32 values in fp32, and only h is rounded
+ * to fp16.  The weights are read once, as for nvfp4_gemm.
+ * ------------------------------------------------------------------------- */
+int nvfp4_gemm_swiglu(const void* w_packed, const uint16_t* x, uint16_t* h,
+                      int M, int K, int F, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * fp8_gemm -- y = x . (e4m3(c) * S), fp32 accumulate, fp16 out.
@@ -155,7 +203,7 @@ int nvfp4_quantize(const float* w, int K, int N, uint8_t* codes,
 int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales);
 
 /* ---------------------------------------------------------------------------
- * The three GEMM calls with an explicit kernel choice instead of the
+ * The GEMM calls with an explicit kernel choice instead of the
  * library's pick (same arguments and results, used to compare kernels):
  *   engine : 0 = VALU dot2 engine (nvfp4_gemm with M == 1 only),
  *            1 = MFMA 16x16x32 f16 engine (all calls, M = 1..8),
@@ -192,6 +240,12 @@ int lm_head_gemm_argmax_config(const void* w_packed, const uint16_t* x,
                                int N, void* workspace, size_t workspace_bytes,
                                hipStream_t stream, int engine, int ct, int nw,
                                int ksplit);
+/* For nvfp4_gemm_swiglu the choice applies to the packed blob's
+ * 16 * ceil(F / 8) columns (engine 0 is available for M == 1). */
+int nvfp4_gemm_swiglu_config(const void* w_packed, const uint16_t* x,
+                             uint16_t* h, int M, int K, int F, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream,
+                             int engine, int ct, int nw, int ksplit);
 
 /* 1 if the explicit kernel choice is supported for this op and shape (op as
  * below), else 0. */
@@ -204,7 +258,8 @@ size_t skinny_workspace_bytes_config(int op, int M, int K, int N, int engine,
                                      int ct, int nw, int ksplit);
 
 /* Workspace bytes a call needs. op: 0 = nvfp4_gemm, 1 = fp8_gemm,
- * 2 = lm_head_gemm_argmax.  Returns 0 for an unsupported op or shape. */
+ * 2 = lm_head_gemm_argmax, 3 = nvfp4_gemm_swiglu (N is then F).  Returns 0
+ * for an unsupported op or shape. */
 size_t skinny_workspace_bytes(int op, int M, int K, int N);
 
 /* ---------------------------------------------------------------------------

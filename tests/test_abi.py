@@ -161,9 +161,73 @@ def test_pack_size_and_header():
     blob = sk.nvfp4_pack(codes, scales, 0.125, 272, 100)
     h = blob[:64]
     assert bytes(h[:4]) == b"SKN4"
-    assert list(h[4:28].view(np.uint32)) == [3, 272, 100, 1, 7, 9216]
+    assert list(h[4:28].view(np.uint32)) == [4, 272, 100, 1, 7, 9216]
     assert h[28:32].view(np.float32)[0] == np.float32(0.125)
     assert list(h[32:48].view(np.uint64)) == [256, 7 * 9216]
+    assert h[48:52].view(np.float32)[0] == np.float32(0.125)          # g2 = g for a plain blob
+    assert list(h[52:60].view(np.uint32)) == [0, 0]                    # kind plain, F unused
+
+
+def _interleave(gate, up, F):
+    """Canonical arrays of the packed SwiGLU columns, built column by column:
+    packed column 16t + c is gate column 8t + c (c < 8) or up column 8t + c - 8."""
+    Np = 16 * -(-F // 8)
+    codes = np.zeros((Np, gate[0].shape[1]), np.uint8)
+    scales = np.zeros((Np, gate[1].shape[1]), np.uint8)
+    for n in range(Np):
+        t, c = divmod(n, 16)
+        f = 8 * t + c % 8
+        if f < F:
+            src = gate if c < 8 else up
+            codes[n], scales[n] = src[0][f], src[1][f]
+    return codes, scales
+
+
+@pytest.mark.parametrize("K,F", [(256, 8), (272, 13), (2064, 3), (1024, 40)])
+def test_pack_swiglu_interleaves_gate_and_up(K, F):
+    rng = np.random.default_rng(K * F)
+    gate = (rng.integers(0, 256, (F, K // 2), dtype=np.uint8), rng.integers(0, 0x7F, (F, K // 16), dtype=np.uint8), 0.5)
+    up = (rng.integers(0, 256, (F, K // 2), dtype=np.uint8), rng.integers(0, 0x7F, (F, K // 16), dtype=np.uint8), 0.25)
+    blob = sk.nvfp4_pack_swiglu(gate, up, K, F)
+    Np = sk.swiglu_packed_cols(F)
+    assert Np == 16 * -(-F // 8) and blob.size == sk.packed_bytes(K, Np)
+    codes, scales = _interleave(gate, up, F)
+    plain = sk.nvfp4_pack(codes, scales, 0.5, K, Np)
+    assert np.array_equal(blob[256:], plain[256:])
+    h = blob[:64]
+    assert bytes(h[:4]) == b"SKN4" and list(h[4:16].view(np.uint32)) == [4, K, Np]
+    assert h[28:32].view(np.float32)[0] == np.float32(0.5)
+    assert h[48:52].view(np.float32)[0] == np.float32(0.25)
+    assert list(h[52:60].view(np.uint32)) == [1, F]
+
+
+def test_swiglu_argument_errors():
+    L = lib()
+    c = np.zeros((4, 128), np.uint8)
+    s = np.zeros((4, 16), np.uint8)
+    size = ctypes.c_size_t(0)
+    P = lambda a: a.ctypes.data if a is not None else None
+    pack = lambda gc=c, gs=s, gg=1.0, uc=c, us=s, ug=1.0, K=256, F=4: L.nvfp4_pack_swiglu(
+        P(gc), P(gs), gg, P(uc), P(us), ug, K, F, None, ctypes.byref(size))
+    assert pack() == sk.OK and size.value == sk.packed_bytes(256, 16)
+    assert pack(uc=None) == sk.EINVAL
+    assert pack(ug=float("nan")) == sk.EINVAL and pack(gg=-1.0) == sk.EINVAL
+    assert pack(F=0) == sk.ESHAPE and pack(K=250) == sk.ESHAPE and pack(F=(1 << 23) + 1) == sk.ESHAPE
+    bad = s.copy()
+    bad[2, 3] = 0xFF
+    out = np.zeros(size.value, np.uint8)
+    assert L.nvfp4_pack_swiglu(P(c), P(s), 1.0, P(c), P(bad), 1.0, 256, 4, P(out), ctypes.byref(size)) == sk.EFORMAT
+    gemm = lambda M=1, K=256, F=100, w=A, x=A, h=A: L.nvfp4_gemm_swiglu(w, x, h, M, K, F, None, 0, None)
+    assert gemm(w=None) == sk.EINVAL and gemm(h=None) == sk.EINVAL
+    assert gemm(M=9) == sk.ESHAPE and gemm(F=0) == sk.ESHAPE and gemm(K=24) == sk.ESHAPE
+    assert gemm(F=(1 << 23) + 1) == sk.ESHAPE
+    assert gemm(h=MIS) == sk.EALIGN and gemm(x=MIS) == sk.EALIGN
+    # lm_head / split workspace rules carry over to the packed column count
+    assert L.nvfp4_gemm_swiglu_config(A, A, A, 8, 256, 100, None, 0, None, 0, 1, 1, 1) == sk.EINVAL  # VALU is M = 1
+    need = sk.workspace_bytes(sk.OP_SWIGLU, 8, 17408, 5120)
+    assert need == sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 10240)
+    assert gemm(M=8, K=17408, F=5120) == sk.EINVAL                     # no workspace for the K split
+    assert sk.workspace_bytes(sk.OP_SWIGLU, 1, 256, 0) == 0
 
 
 def test_pack_errors():

@@ -66,6 +66,32 @@ def test_nvfp4_full_shape_sampled(name):
         assert np.isfinite(y.float().cpu().numpy()).all()
 
 
+def test_swiglu_gate_up_full_shape_sampled():
+    """The fused gate+up shape (K = 5120, 2 x 17408 columns) with the SwiGLU
+    epilogue: h[M, 17408], M = 1 and 8, against the oracle on sampled columns."""
+    fmt, ms, K, N = synth.WORKLOADS["gate_up"]
+    F = N // 2
+    _log("preparing gate_up SwiGLU pair")
+    case = workload.swiglu_case(8, K, F)
+    blob = dev(case["blob"])
+    cols = _cols(F)
+    for M in (1, 8):
+        x = dev(case["x"][:M])
+        ws = _ws(sk.OP_SWIGLU, M, K, F)
+        h = torch.empty((M, F), dtype=torch.float16, device="cuda")
+        sk.nvfp4_gemm_swiglu(blob, x, h, workspace=ws)
+        h2 = torch.empty_like(h)
+        sk.nvfp4_gemm_swiglu(blob, x, h2, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(h, h2), "not deterministic"
+        got = h.float().cpu().numpy()[:, cols]
+        ref = oracle.nvfp4_swiglu(case["x"][:M], case["gate"], case["up"], cols=cols)
+        m = oracle.compare(got, ref)
+        _log(f"gate_up SwiGLU M={M}: {m}")
+        assert m["rel_frob"] <= REL_FROB and m["row_max"] <= ROW_MAX, m
+        assert np.isfinite(h.float().cpu().numpy()).all()
+
+
 @pytest.mark.parametrize("name", ["qkv", "o_proj"])
 def test_fp8_full_shape_sampled(name):
     _log(f"preparing {name}")

@@ -167,6 +167,55 @@ def test_nvfp4_every_m():
         _check(run_nvfp4(case, M=M, config=(2, 1, 16, 1)), ref, f"M={M} streaming")
 
 
+# ------------------------------------------------------------ SwiGLU pair
+SMALL_SWIGLU = [(1, 256, 8), (1, 272, 13), (3, 400, 100), (8, 1040, 500), (8, 2064, 21), (1, 3088, 40), (2, 16, 5)]
+
+
+def run_swiglu(case, M=None, config=None, guard=0):
+    M = case["M"] if M is None else M
+    K, F = case["K"], case["F"]
+    buf = torch.full((M * F + 2 * guard,), float("nan"), dtype=torch.float16, device="cuda")
+    h = buf[guard:guard + M * F].view(M, F)
+    sk.nvfp4_gemm_swiglu(dev(case["blob"]), dev(case["x"][:M]), h, config=config,
+                         workspace=ws_for(sk.OP_SWIGLU, M, K, F, config))
+    torch.cuda.synchronize()
+    if guard:
+        assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + M * F:]).all(), "guard overwritten"
+    return h.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("shape", SMALL_SWIGLU)
+def test_nvfp4_swiglu_parity_all_configs(shape):
+    """h = silu(x.Wg) * (x.Wu) from the interleaved pair, in every engine, against the oracle."""
+    M, K, F = shape
+    case = workload.swiglu_case(M, K, F, seed=sum(shape) + 7)
+    ref = oracle.nvfp4_swiglu(case["x"], case["gate"], case["up"])
+    choices = (cfgs(1, K) + (cfgs(0, K) if M == 1 else [])
+               + stream_cfgs(sk.OP_SWIGLU, M, K, F))
+    assert choices
+    for cfg in choices:
+        _check(run_swiglu(case, config=cfg), ref, f"swiglu {shape} {cfg}")
+    _check(run_swiglu(case, guard=8), ref, f"swiglu {shape} default")
+
+
+def test_nvfp4_swiglu_every_m_and_shared_scale():
+    """Every row count, and a pair quantized with one scale for the fused tensor."""
+    K, F = 1152, 72
+    case = workload.swiglu_case(8, K, F, seed=21)
+    for M in range(1, 9):
+        ref = oracle.nvfp4_swiglu(case["x"][:M], case["gate"], case["up"])
+        _check(run_swiglu(case, M=M), ref, f"swiglu M={M} default")
+        _check(run_swiglu(case, M=M, config=(1, 2, 2, 2)), ref, f"swiglu M={M} mfma split")
+        _check(run_swiglu(case, M=M, config=(2, 1, 16, 1)), ref, f"swiglu M={M} streaming")
+    w, x = workload.synth.draw(4, K, 2 * F, seed=22)
+    codes, scales, g = sk.nvfp4_quantize(w)       # one g for the fused [K, 2F] tensor
+    gate, up = (codes[:F], scales[:F], g), (codes[F:], scales[F:], g)
+    shared = {"M": 4, "K": K, "F": F, "x": x, "blob": sk.nvfp4_pack_swiglu(gate, up, K, F)}
+    ref = oracle.nvfp4_swiglu(x, gate, up)
+    for cfg in (None, (1, 1, 2, 1), (2, 2, 8, 1)):
+        _check(run_swiglu(shared, config=cfg), ref, f"swiglu shared g {cfg}")
+
+
 SMALL_FP8 = [(1, 256, 256), (2, 272, 100), (4, 400, 300), (8, 1040, 1000), (3, 16, 129)]
 
 
