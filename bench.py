@@ -13,7 +13,7 @@ shape the measured read ceiling: the library's read probe (skinny_read_probe,
 one 9 KiB block per wavefront like one packed unit) over the same rotating
 copies, plus the probe over a 2 GiB buffer.
 
-    python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head|gate_up_swiglu] [--M m]
+    python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head|gate_up_swiglu|lm_head_verify] [--M m]
 
 Each step reads a different one of R byte-identical copies of the weights
 (R copies exceed 600 MB) so that the 256 MB Infinity Cache cannot serve them.
@@ -67,7 +67,8 @@ def describe(case, name):
     if case["fmt"] == "swiglu":
         return f"NVFP4 W4A16 {name} M={case['M']} K={case['K']} F={case['F']} (gate and up, h = silu(gate) * up)"
     fmt = "NVFP4 W4A16" if case["fmt"] == "nvfp4" else "FP8 E4M3 W8A16"
-    extra = " + fused argmax" if name == "lm_head" else ""
+    extra = (" + fused argmax" if name == "lm_head" else
+             " + fused argmax and greedy verification of 7 drafts" if name == "lm_head_verify" else "")
     return f"{fmt} {name} M={case['M']} K={case['K']} N={case['N']}{extra}"
 
 
@@ -212,15 +213,23 @@ def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_p
     else:
         copies = [dev(case["codes"]) for _ in range(R)]
         scales = dev(case["scales"])
-    op = (sk.OP_LM_HEAD if name == "lm_head" else sk.OP_SWIGLU if fmt == "swiglu" else
+    verify = name == "lm_head_verify"
+    op = (sk.OP_LM_HEAD if name in ("lm_head", "lm_head_verify") else sk.OP_SWIGLU if fmt == "swiglu" else
           sk.OP_NVFP4 if fmt == "nvfp4" else sk.OP_FP8)
+    drafts = torch.zeros((max(M - 1, 1),), dtype=torch.int32, device="cuda")
+    result = torch.empty((M + 1,), dtype=torch.int32, device="cuda")
     ws = torch.zeros(max(sk.workspace_bytes(op, M, K, N, cfg), 256), dtype=torch.uint8, device="cuda")
     wsp, wsn = ws.data_ptr(), ws.numel()
     xp, yp = x.data_ptr(), y.data_ptr()
 
     def step(i, s):
         w = copies[i % R].data_ptr()
-        if op == sk.OP_LM_HEAD:
+        if verify:
+            st = (L.lm_head_verify_greedy_config(w, xp, drafts.data_ptr(), idx.data_ptr(), result.data_ptr(),
+                                                 M, K, N, wsp, wsn, s, *cfg) if cfg
+                  else L.lm_head_verify_greedy(w, xp, drafts.data_ptr(), idx.data_ptr(), result.data_ptr(),
+                                               M, K, N, wsp, wsn, s))
+        elif op == sk.OP_LM_HEAD:
             st = (L.lm_head_gemm_argmax_config(w, xp, idx.data_ptr(), None, M, K, N, wsp, wsn, s, *cfg) if cfg
                   else L.lm_head_gemm_argmax(w, xp, idx.data_ptr(), None, M, K, N, wsp, wsn, s))
         elif op == sk.OP_NVFP4:

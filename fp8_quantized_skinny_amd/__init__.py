@@ -247,3 +247,30 @@ def lm_head_gemm_argmax(w_packed, x, idx, N, logits=None, workspace=None, stream
         st = lib().lm_head_gemm_argmax_config(wp, xp, ip, lp, M, K, N, ws, wsb, _stream(stream), *config)
     _check(st, "lm_head_gemm_argmax")
     return idx
+
+
+def lm_head_verify_greedy(w_packed, x, drafts, idx, result, N, workspace=None, stream=None, config=None):
+    """Greedy verification of one speculative round on the device.
+
+    x: CUDA fp16 [M, K] (row 0 after the last accepted token, row m after draft m);
+    drafts: CUDA int32 [M - 1] (None if M == 1); idx: CUDA int32 [M] (per-row argmax);
+    result: CUDA int32 [M + 1] -> [L, committed tokens (L + 1), -1 ...].
+    workspace: as lm_head_gemm_argmax (op OP_LM_HEAD)."""
+    import torch
+    M, K = x.shape
+    _shape_checks(x, M, K, None, N, "x")
+    if idx.numel() < M or result.numel() < M + 1 or (M > 1 and (drafts is None or drafts.numel() < M - 1)):
+        raise ValueError("idx must hold M, result M + 1 and drafts M - 1 elements")
+    if w_packed.numel() < packed_bytes(K, N):
+        raise ValueError("w_packed is smaller than the blob for this K, N")
+    ws, wsb = _workspace(workspace, workspace_bytes(OP_LM_HEAD, M, K, N, config), "lm_head_verify_greedy")
+    wp = _dev(w_packed, torch.uint8, "w_packed")
+    xp = _dev(x, torch.float16, "x")
+    dp = None if drafts is None else _dev(drafts, torch.int32, "drafts")
+    ip, rp = _dev(idx, torch.int32, "idx"), _dev(result, torch.int32, "result")
+    if config is None:
+        st = lib().lm_head_verify_greedy(wp, xp, dp, ip, rp, M, K, N, ws, wsb, _stream(stream))
+    else:
+        st = lib().lm_head_verify_greedy_config(wp, xp, dp, ip, rp, M, K, N, ws, wsb, _stream(stream), *config)
+    _check(st, "lm_head_verify_greedy")
+    return result

@@ -23,6 +23,9 @@ def _declare(lib):
         "fp8_gemm": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
         "fp8_gemm_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int, c_int]),
         "lm_head_gemm_argmax": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
+        "lm_head_verify_greedy": (c_int, [P, P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
+        "lm_head_verify_greedy_config": (c_int, [P, P, P, P, P, c_int, c_int, c_int, P, c_size_t, P,
+                                                 c_int, c_int, c_int, c_int]),
         "lm_head_gemm_argmax_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P,
                                                c_int, c_int, c_int, c_int]),
         "skinny_workspace_bytes_config": (c_size_t, [c_int] * 8),
@@ -54,4 +57,4 @@ EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp
             "fp8_quantize", "skinny_workspace_bytes", "skinny_strerror", "nvfp4_gemm_config",
             "fp8_gemm_config", "lm_head_gemm_argmax_config", "skinny_workspace_bytes_config",
             "skinny_config_supported", "skinny_read_probe", "nvfp4_pack_swiglu", "nvfp4_gemm_swiglu",
-            "nvfp4_gemm_swiglu_config")
+            "nvfp4_gemm_swiglu_config", "lm_head_verify_greedy", "lm_head_verify_greedy_config")

@@ -608,6 +608,32 @@ int lm_head_gemm_argmax_config(const void* w_packed, const uint16_t* x, int32_t*
                                     idx, workspace, stream));
 }
 
+int lm_head_verify_greedy_config(const void* w_packed, const uint16_t* x, const int32_t* drafts,
+                                 int32_t* idx, int32_t* result, int M, int K, int N, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream, int engine, int ct, int nw,
+                                 int ksplit) {
+  int s = nvfp4_common_checks(w_packed, x, idx, M, K, N);
+  if (s) return s;
+  if (!result || (M > 1 && !drafts)) return SKINNY_EINVAL;
+  if (!aligned(idx, 4) || !aligned(result, 4) || (drafts && !aligned(drafts, 4))) return SKINNY_EALIGN;
+  const LaunchCfg cfg{engine, ct, nw, ksplit};
+  if (!nvfp4_cfg_supported(cfg, M, K, true)) return SKINNY_EINVAL;
+  s = check_workspace(workspace, workspace_bytes, nvfp4_workspace_layout(cfg, M, K, N, true).total);
+  if (s) return s;
+  return launch_status(launch_nvfp4(static_cast<const uint8_t*>(w_packed), x, nullptr, M, K, N, cfg, idx,
+                                    workspace, stream, 0, drafts, result));
+}
+
+int lm_head_verify_greedy(const void* w_packed, const uint16_t* x, const int32_t* drafts, int32_t* idx,
+                          int32_t* result, int M, int K, int N, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  int s = check_shape(M, K, N);
+  if (s) return s;
+  const LaunchCfg c = default_nvfp4_cfg(M, K, N, true);
+  return lm_head_verify_greedy_config(w_packed, x, drafts, idx, result, M, K, N, workspace, workspace_bytes,
+                                      stream, c.engine, c.ct, c.nw, c.ksplit);
+}
+
 int lm_head_gemm_argmax(const void* w_packed, const uint16_t* x, int32_t* idx, uint16_t* logits,
                         int M, int K, int N, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {

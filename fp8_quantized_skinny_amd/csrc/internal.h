@@ -102,7 +102,8 @@ WorkspaceLayout fp8_workspace_layout(const LaunchCfg& cfg, int M, int K, int N);
 // packed column count) and y is h[M][swiglu_F] = silu(gate) * up.
 hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y,
                         int M, int K, int N, const LaunchCfg& cfg,
-                        int32_t* idx, void* workspace, hipStream_t stream, int swiglu_F = 0);
+                        int32_t* idx, void* workspace, hipStream_t stream, int swiglu_F = 0,
+                        const int32_t* drafts = nullptr, int32_t* verify = nullptr);
 hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x,
                       uint16_t* y, int M, int K, int N, const LaunchCfg& cfg,
                       void* workspace, hipStream_t stream);
@@ -131,8 +132,11 @@ int device_cu_count();
 int finalize_groups(int N);
 hipError_t launch_finalize(const float* part, int ksplit, int M, int N, const float* gptr, uint16_t* y,
                            unsigned long long* cand, hipStream_t stream);
+// With result non-null it also verifies the speculative round whose drafts
+// rows 1 .. M-1 carry (drafts[M-1], greedy acceptance): result[0] = accepted
+// drafts L, result[1 .. L+1] = committed tokens, result[L+2 .. M] = -1.
 hipError_t launch_argmax_reduce(const unsigned long long* cand, int groups, int M, int32_t* idx,
-                                hipStream_t stream);
+                                hipStream_t stream, const int32_t* drafts = nullptr, int32_t* result = nullptr);
 // Second pass of a K split of a SwiGLU pair: h[m][f] = silu(g * gate) * (g2 *
 // up), both sums taken over the splits in order from part[split][m][n] of
 // the packed columns (n = 16 * (f / 8) + f % 8 and n + 8).

@@ -633,7 +633,8 @@ hipError_t launch_gemm(const Nvfp4Args& a, const LaunchCfg& cfg, int epi, hipStr
 #undef SKINNY_NVFP4_DISPATCH
 
 hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y, int M, int K, int N,
-                        const LaunchCfg& cfg, int32_t* idx, void* workspace, hipStream_t stream, int swiglu_F) {
+                        const LaunchCfg& cfg, int32_t* idx, void* workspace, hipStream_t stream, int swiglu_F,
+                        const int32_t* drafts, int32_t* verify) {
   const Geometry geo = nvfp4_geometry(K, N);
   const bool argmax = idx != nullptr;
   const WorkspaceLayout wl = nvfp4_workspace_layout(cfg, M, K, N, argmax);
@@ -665,7 +666,7 @@ hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y, int
     if (e != hipSuccess) return e;
     groups = finalize_groups(N);
   }
-  return argmax ? launch_argmax_reduce(a.cand, groups, M, idx, stream) : hipSuccess;
+  return argmax ? launch_argmax_reduce(a.cand, groups, M, idx, stream, drafts, verify) : hipSuccess;
 }
 
 }  // namespace skinny

@@ -73,9 +73,20 @@ __global__ __launch_bounds__(kFinalizeThreads) void finalize_splits(const float*
 // idx[m] = column of the largest candidate key of row m.  Every thread
 // issues the loads of all its rows before reducing any of them, so the kernel
 // waits for memory about once instead of once per row.
+//
+// With `result` (greedy verification of a speculative round), row m of x is
+// the target model's state after the last accepted token (m = 0) or after
+// draft m (m >= 1), so idx[m] is the target's greedy choice for the token
+// that follows.  Draft m + 1 is accepted while it equals idx[m] for every
+// earlier row; the round commits the L accepted drafts and then idx[L]
+// (greedy speculative decoding: Leviathan, Kalman and Matias, "Fast Inference
+// from Transformers via Speculative Decoding", 2023; the author's post runs
+// rounds of k = 7 drafts, M = 8 rows, with greedy local-argmax proposals).
+// result[0] = L, result[1 .. L+1] = the committed tokens, the rest -1.
 __global__ __launch_bounds__(256) void argmax_reduce(const unsigned long long* cand, int groups, int M,
-                                                     int32_t* idx) {
+                                                     int32_t* idx, const int32_t* drafts, int32_t* result) {
   __shared__ unsigned long long red[4][kMaxRows];
+  __shared__ int32_t top[kMaxRows];
   unsigned long long k[kMaxRows];
 #pragma unroll
   for (int m = 0; m < kMaxRows; ++m) k[m] = 0ull;
@@ -97,7 +108,18 @@ __global__ __launch_bounds__(256) void argmax_reduce(const unsigned long long* c
     unsigned long long best = 0ull;
     for (int w = 0; w < 4; ++w) best = red[w][threadIdx.x] > best ? red[w][threadIdx.x] : best;
     // No candidate at all (every logit NaN) leaves the all-ones index -1.
-    idx[threadIdx.x] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFull));
+    const int32_t i = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFull));
+    idx[threadIdx.x] = i;
+    top[threadIdx.x] = i;
+  }
+  if (result) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int L = 0;
+      while (L < M - 1 && drafts[L] == top[L]) ++L;
+      result[0] = L;
+      for (int j = 0; j < M; ++j) result[1 + j] = j < L ? drafts[j] : j == L ? top[L] : -1;
+    }
   }
 }
 
@@ -156,8 +178,8 @@ hipError_t launch_finalize_swiglu(const float* part, int ksplit, int M, int N, i
 }
 
 hipError_t launch_argmax_reduce(const unsigned long long* cand, int groups, int M, int32_t* idx,
-                                hipStream_t stream) {
-  hipLaunchKernelGGL(argmax_reduce, dim3(1), dim3(256), 0, stream, cand, groups, M, idx);
+                                hipStream_t stream, const int32_t* drafts, int32_t* result) {
+  hipLaunchKernelGGL(argmax_reduce, dim3(1), dim3(256), 0, stream, cand, groups, M, idx, drafts, result);
   return hipGetLastError();
 }
 

@@ -31,6 +31,8 @@ WORKLOADS = {
     "lm_head": ("nvfp4", (1, 8), 5120, 151936),
     # the gate+up shape as a SwiGLU pair: two 5120 x 17408 projections, output h[M, 17408]
     "gate_up_swiglu": ("swiglu", (8,), 5120, 17408),
+    # the lm_head shape verifying one speculative round (k = 7 drafts, M = 8 rows)
+    "lm_head_verify": ("nvfp4", (8,), 5120, 151936),
 }
 
 

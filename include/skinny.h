@@ -183,6 +183,33 @@ int lm_head_gemm_argmax(const void* w_packed, const uint16_t* x, int32_t* idx,
                         size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * lm_head_verify_greedy -- lm_head_gemm_argmax plus the greedy verification
+ * of one speculative-decoding round, on the device.
+ *
+ * A round feeds the target model the last accepted token and k = M - 1 draft
+ * tokens d_1 .. d_k; row m of x is its hidden state after token m (row 0:
+ * after the last accepted token), so idx[m] is the target's greedy next
+ * token there.  Draft d_{j+1} is accepted while it equals idx[j] for every
+ * earlier row; with L drafts accepted the round commits d_1 .. d_L and then
+ * idx[L], L + 1 tokens (greedy speculative decoding, Leviathan, Kalman and
+ * Matias, "Fast Inference from Transformers via Speculative Decoding", 2023;
+ * the author's post runs k = 7 native-MTP drafts per round and reports the
+ * tokens committed per round, and has the drafter propose greedy tokens).
+ *
+ *   w_packed, x, M, K, N, workspace : as for lm_head_gemm_argmax (op 2 for
+ *               the workspace size).
+ *   drafts    : device, int32 [M - 1]: d_1 .. d_{M-1} (may be NULL if M == 1).
+ *   idx       : device, int32 [M]: the per-row argmax, as lm_head_gemm_argmax.
+ *   result    : device, int32 [M + 1]: result[0] = L (0 .. M-1), result[1 ..
+ *               L+1] = the committed tokens, result[L+2 .. M] = -1.
+ * The verification runs inside the argmax reduction kernel: no extra launch.
+ * ------------------------------------------------------------------------- */
+int lm_head_verify_greedy(const void* w_packed, const uint16_t* x,
+                          const int32_t* drafts, int32_t* idx, int32_t* result,
+                          int M, int K, int N, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Host quantizers (offline weight preparation, not part of the GEMM).  They
  * stand in for the pages' offline FP16 -> NVFP4 conversion script (ai-manual
  * article, section "NVFP4 model conversion") and produce the canonical
@@ -240,6 +267,12 @@ int lm_head_gemm_argmax_config(const void* w_packed, const uint16_t* x,
                                int N, void* workspace, size_t workspace_bytes,
                                hipStream_t stream, int engine, int ct, int nw,
                                int ksplit);
+int lm_head_verify_greedy_config(const void* w_packed, const uint16_t* x,
+                                 const int32_t* drafts, int32_t* idx,
+                                 int32_t* result, int M, int K, int N,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, int engine, int ct, int nw,
+                                 int ksplit);
 /* For nvfp4_gemm_swiglu the choice applies to the packed blob's
  * 16 * ceil(F / 8) columns (engine 0 is available for M == 1). */
 int nvfp4_gemm_swiglu_config(const void* w_packed, const uint16_t* x,

@@ -8,6 +8,7 @@ library shares no code with it.  Everything here is plain NumPy in float64:
   quantize  the NVFP4 and 128x128-block FP8 quantization rules
   gemm      y = x . dequant(W) in float64, per-row argmax, error metrics,
             and the SwiGLU of a gate/up pair of projections
+  speculative  greedy verification of a speculative-decoding round
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) against
 tables, library routines, brute force and closed-form cases.
@@ -15,5 +16,6 @@ tables, library routines, brute force and closed-form cases.
 
 from .formats import e2m1_decode, e4m3_decode, e2m1_encode, e4m3_encode, E2M1_MAX, E4M3_MAX
 from .quantize import nvfp4_quantize, fp8_quantize
+from .speculative import verify_greedy
 from .gemm import (nvfp4_unpack_codes, nvfp4_dequant_unscaled, nvfp4_gemm, fp8_dequant, fp8_gemm,
                    silu, nvfp4_swiglu, argmax_rows, compare)

@@ -92,6 +92,17 @@ def test_explicit_config_rejections():
     assert big(MIS, need) == sk.EALIGN
 
 
+def test_verify_argument_errors():
+    L = lib()
+    v = lambda M=8, d=A, i=A, r=A, x=A, w=A: L.lm_head_verify_greedy(w, x, d, i, r, M, 256, 512, None, 0, None)
+    assert v(d=None) == sk.EINVAL and v(r=None) == sk.EINVAL and v(i=None) == sk.EINVAL
+    assert v(M=9) == sk.ESHAPE
+    assert v(d=A + 2) == sk.EALIGN and v(r=A + 2) == sk.EALIGN
+    # M = 1 needs no drafts: the call gets past that check and stops at the missing workspace
+    assert sk.workspace_bytes(sk.OP_LM_HEAD, 1, 256, 512) > 0
+    assert v(M=1, d=None) == sk.EINVAL and v(M=1, d=None, r=A + 2) == sk.EALIGN
+
+
 def test_fp8_gemm_argument_errors():
     L = lib()
     f = lambda **k: L.fp8_gemm(k.get("w", A), k.get("s", A), k.get("x", A), k.get("y", A), k.get("M", 1),

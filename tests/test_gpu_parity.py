@@ -296,3 +296,41 @@ def test_lm_head_zero_weights_and_shared_workspace():
         want, _ = oracle.argmax_rows(ref_nvfp4(case, Mi))
         idx, _ = run_lm_head(case, Mi, ws=ws)
         assert np.array_equal(idx, want), Mi
+
+
+# ------------------------------------------------------ speculative verify
+def run_verify(case, M, drafts, config=None):
+    K, N = case["K"], case["N"]
+    idx = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    res = torch.full((M + 1,), -9, dtype=torch.int32, device="cuda")
+    d = dev(np.asarray(drafts, np.int32)) if M > 1 else None
+    sk.lm_head_verify_greedy(dev(case["blob"]), dev(case["x"][:M]), d, idx, res, N,
+                             workspace=ws_for(sk.OP_LM_HEAD, M, K, N, config), config=config)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), res.cpu().numpy()
+
+
+def test_lm_head_verify_greedy_rounds():
+    """Rounds of k = 7 drafts that are accepted in full, cut at every position,
+    or rejected at once, plus M = 1: the device's accepted length and committed
+    tokens equal the oracle's verification of the oracle's argmax, bit for bit."""
+    M, K, N = 8, 2048, 3000
+    case = workload.nvfp4_case(M, K, N, seed=23)
+    want_idx, margin = oracle.argmax_rows(ref_nvfp4(case))
+    rng = np.random.default_rng(5)
+    rounds = [list(want_idx[:M - 1])]
+    for cut in range(M - 1):                      # first wrong draft at position `cut`
+        d = list(want_idx[:M - 1])
+        d[cut] = (d[cut] + 1 + int(rng.integers(N - 1))) % N
+        rounds.append(d)
+    choices = [None, (1, 2, 2, 2), (2, 1, 16, 1), (1, 1, 1, 2), (1, 4, 8, 1)]
+    assert all(c is None or sk.config_supported(sk.OP_LM_HEAD, M, K, N, c) for c in choices)
+    for cfg in choices:
+        for drafts in rounds:
+            idx, res = run_verify(case, M, drafts, config=cfg)
+            assert np.array_equal(idx, want_idx), (cfg, idx, want_idx, margin)
+            L, committed = oracle.verify_greedy(want_idx, drafts)
+            want_res = [L] + committed + [-1] * (M - 1 - L)
+            assert list(res) == want_res, (cfg, drafts, list(res), want_res)
+    idx, res = run_verify(case, 1, [])
+    assert list(res) == [0, int(want_idx[0])]
