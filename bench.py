@@ -147,6 +147,17 @@ def time_graph(step, steps, stream):
     return ms
 
 
+def probe_size(nbytes, buffers):
+    """Bytes the read probe reads from each buffer: the weight bytes rounded down
+    to whole 9216-byte blocks, never more than the smallest buffer holds (FP8
+    weight bytes count the block scales, which live outside the code buffers)."""
+    cap = min(b.numel() * b.element_size() for b in buffers)
+    size = (min(int(nbytes), cap) // 9216) * 9216
+    if size < 9216 or size > cap:
+        raise ValueError(f"read probe of {size} bytes does not fit buffers of {cap} bytes")
+    return size
+
+
 def read_ceiling(copies, nbytes, steps, large=True):
     """Measured HBM read ceiling: the library's read probe (one 9 KiB block per
     wavefront, nine 16-byte loads per lane) over the same rotating copies as the
@@ -157,7 +168,7 @@ def read_ceiling(copies, nbytes, steps, large=True):
     L = lib()
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    probe_bytes = (nbytes // 9216) * 9216
+    probe_bytes = probe_size(nbytes, copies)
 
     def step_same(i, s):
         st = L.skinny_read_probe(copies[i % len(copies)].data_ptr(), probe_bytes, sink.data_ptr(), s)
@@ -172,7 +183,7 @@ def read_ceiling(copies, nbytes, steps, large=True):
     if not large:
         return out
     big = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
-    big_bytes = (big.numel() // 9216) * 9216
+    big_bytes = probe_size(big.numel(), [big])
 
     def step_big(i, s):
         st = L.skinny_read_probe(big.data_ptr(), big_bytes, sink.data_ptr(), s)

@@ -89,6 +89,19 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Zeroes halves [from, to) of rows 0..M-1 of an LDS copy of x (row stride RS
+// halves) with 16-byte stores: the part of the copy past K, which the
+// direct-to-LDS loads leave untouched.  from, to and RS are multiples of 8.
+__device__ __forceinline__ void zero_x_tail(_Float16* xs, int M, int RS, int from, int to) {
+  from = from < 0 ? 0 : from;
+  const int per_row = (to - from) >> 3;
+  if (per_row <= 0) return;
+  for (int c = threadIdx.x; c < M * per_row; c += blockDim.x) {
+    const int m = c / per_row, j = c - m * per_row;
+    *reinterpret_cast<u32x4*>(xs + m * RS + from + 8 * j) = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 // Ordered argmax key of logit v at column n: the top 32 bits order like the
 // fp32 value (+0 and -0 made equal), the low 32 bits are the inverted column,
 // so the larger key is the larger logit or, on a tie, the lower column.

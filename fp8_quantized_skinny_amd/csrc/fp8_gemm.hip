@@ -65,10 +65,7 @@ __device__ void fp8_stage_x(const Fp8Args& a, const Fp8Plan& P, _Float16* xs) {
   const int RS = fp8_xs_stride(P.S);
   const int kbase = P.s0 * kFp8UnitK;
   const int kvalid = a.K - kbase;
-  if (kvalid < P.S * kFp8UnitK) {
-    for (int i = threadIdx.x; i < a.M * RS; i += blockDim.x)
-      if (i % RS >= kvalid) xs[i] = static_cast<_Float16>(0.0f);
-  }
+  if (kvalid < P.S * kFp8UnitK) zero_x_tail(xs, a.M, RS, kvalid, P.S * kFp8UnitK);
   const int nblocks = a.M * P.S;  // 1 KiB blocks = 512 halves = one unit of K
   for (int b = P.wave; b < nblocks; b += P.nw) {
     const int m = b / P.S, blk = b % P.S;

@@ -93,20 +93,26 @@ int launch_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_EH
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-// Kernel choice made by the library when the caller does not pick one; each
-// rule is the fastest kernel choice measured on the decode shapes.
+// Kernel choice made by the library when the caller does not pick one.  The
+// rules follow timings of every choice on the decode shapes and on one rank's
+// share of them under 4-way tensor parallelism, at M = 1, 4 and 8:
 //
-// NVFP4 GEMV (M = 1, no argmax): VALU engine, one tile per workgroup and as
-// many K spans (units) per workgroup as the 16-wavefront limit allows; K
-// beyond that is split over workgroups, evened out so that every split gets
-// the same spans.
+// NVFP4 GEMV (M = 1, no argmax): VALU engine, whole K per workgroup (K beyond
+// 16 spans split over workgroups, evened out), two tiles per workgroup when
+// there are few tiles (N <= 6144), else one.
 //
-// Other NVFP4 calls: the streaming MFMA engine whenever all of x fits in LDS
-// (K up to 9 spans).  Otherwise, and for FP8: up to four rows, whole-K
-// workgroups as above (MFMA); five to eight rows, four tiles per workgroup
-// and the fewest K spans per workgroup that keep the K split at most nine
-// ways (the x slice a workgroup stages in LDS grows with M and with its
-// spans; short workgroups keep it small, so that more of them fit on a CU).
+// Other NVFP4 calls: the streaming engine when there are enough column tiles
+// to keep the CUs busy with whole tiles (N >= 8192) and all of x fits in LDS
+// (K <= 9216): one workgroup per CU of about N / 3200 wavefronts (4 to 12),
+// which gives each wavefront about one tile on the MLP shapes and a few on a
+// vocabulary.  With fewer tiles a wavefront per tile is too little
+// parallelism, so the one-unit-per-wavefront MFMA engine is used instead,
+// like FP8:
+//   - up to four rows and K <= 8192: whole K per workgroup (two tiles per
+//     workgroup when K and N are short);
+//   - otherwise four tiles per workgroup and the fewest K spans per workgroup
+//     that keep the K split at most nine ways (the x slice a workgroup stages
+//     in LDS grows with M and with its spans; short workgroups keep it small).
 // The largest S (K spans per workgroup) from `s_max` down for which the
 // choice is supported (its LDS copy of x fits), with the K split evened out.
 template <typename Fits>
@@ -121,8 +127,8 @@ LaunchCfg fit_spans(int engine, int ct, int ku, int s_max, Fits fits) {
 }
 
 template <typename Fits>
-LaunchCfg pick_whole_k_cfg(int engine, int ku, Fits fits) {
-  return fit_spans(engine, 1, ku, std::min(ku, kMaxWaves), fits);
+LaunchCfg pick_whole_k_cfg(int engine, int ct, int ku, Fits fits) {
+  return fit_spans(engine, ct, ku, std::min(ku, kMaxWaves / ct), fits);
 }
 
 template <typename Fits>
@@ -132,40 +138,36 @@ LaunchCfg pick_short_cfg(int ku, int nt, Fits fits) {
   return fit_spans(1, ct, ku, std::min((ku + kMaxSplit - 1) / kMaxSplit, kMaxWaves / ct), fits);
 }
 
-// Streaming engine (all of x in LDS, whole tiles per wavefront, no K split)
-// whenever x fits: two 8-wavefront workgroups per CU when two copies of x
-// fit, else one workgroup of 11 wavefronts (16 for vocabulary-sized N, whose
-// tiles outnumber the wavefront slots).
-bool pick_stream_cfg(int M, int K, int N, LaunchCfg* out) {
-  const LaunchCfg two{2, 2, 8, 1};
-  if (nvfp4_cfg_supported(two, M, K, false)) {
-    *out = two;
-    return true;
-  }
+// One-unit-per-wavefront MFMA choice (NVFP4 without streaming, and FP8);
+// ku counts K spans of `unit_k`.
+template <typename Fits>
+LaunchCfg pick_oneshot_cfg(int M, int K, int ku, int nt, Fits fits) {
+  if (M <= 4 && K <= 8192) return pick_whole_k_cfg(1, 2 * ku <= kMaxWaves && nt <= 512 ? 2 : 1, ku, fits);
+  return pick_short_cfg(ku, nt, fits);
+}
+
+bool pick_stream_cfg(int M, int K, int N, bool argmax, LaunchCfg* out) {
   const int nt = (N + kTileCols - 1) / kTileCols;
-  const LaunchCfg one{2, 1, nt >= 4096 ? 16 : 11, 1};
-  if (nvfp4_cfg_supported(one, M, K, false)) {
-    *out = one;
-    return true;
-  }
-  return false;
+  if (nt < 512) return false;
+  const LaunchCfg c{2, 1, std::min(12, std::max(4, (nt + 199) / 200)), 1};
+  if (!nvfp4_cfg_supported(c, M, K, argmax)) return false;
+  *out = c;
+  return true;
 }
 
 LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax) {
   const Geometry g = nvfp4_geometry(K, N);
   auto fits = [&](const LaunchCfg& c) { return nvfp4_cfg_supported(c, M, K, argmax); };
-  if (M == 1 && !argmax) return pick_whole_k_cfg(0, g.ku, fits);
+  if (M == 1 && !argmax) return pick_whole_k_cfg(0, g.nt <= 384 ? 2 : 1, g.ku, fits);
   LaunchCfg c;
-  if (pick_stream_cfg(M, K, N, &c)) return c;
-  if (M > 4) return pick_short_cfg(g.ku, g.nt, fits);
-  return pick_whole_k_cfg(1, g.ku, fits);
+  if (pick_stream_cfg(M, K, N, argmax, &c)) return c;
+  return pick_oneshot_cfg(M, K, g.ku, g.nt, fits);
 }
 
 LaunchCfg default_fp8_cfg(int M, int K, int N) {
   const int ku = (K + 511) / 512;
   auto fits = [&](const LaunchCfg& c) { return fp8_cfg_supported(c, M, K); };
-  if (M > 4) return pick_short_cfg(ku, (N + 15) / 16, fits);
-  return pick_whole_k_cfg(1, ku, fits);
+  return pick_oneshot_cfg(M, K, ku, (N + 15) / 16, fits);
 }
 
 // A SwiGLU pair of F columns each packs to swiglu_packed_cols(F) <= kMaxN columns.

@@ -217,10 +217,7 @@ __device__ void stage_x(const Nvfp4Args& a, const Plan& P, _Float16* xs) {
   const int kbase = P.s0 * kUnitK;
   const int blocks_per_row = P.S * 2;  // 1 KiB blocks = 512 halves
   const int kvalid = a.K - kbase;      // halves of each row that exist
-  if (kvalid < P.S * kUnitK) {
-    for (int i = threadIdx.x; i < a.M * RS; i += blockDim.x)
-      if (i % RS >= kvalid) xs[i] = static_cast<_Float16>(0.0f);
-  }
+  if (kvalid < P.S * kUnitK) zero_x_tail(xs, a.M, RS, kvalid, P.S * kUnitK);
   const int nblocks = a.M * blocks_per_row;
   for (int b = P.wave; b < nblocks; b += P.nw) {
     const int m = b / blocks_per_row, blk = b % blocks_per_row;
@@ -386,10 +383,7 @@ __device__ __forceinline__ void load_unit(Unit& u, const uint8_t* p) {
 // Copies x[m][0..K) for m < M into LDS rows of stride RS halves, zero past K.
 __device__ void stage_x_all(const Nvfp4Args& a, _Float16* xs, int RS, int wave, int nw, int lane) {
   const int kp = a.ku * kUnitK;
-  if (a.K < kp) {
-    for (int i = threadIdx.x; i < a.M * RS; i += blockDim.x)
-      if (i % RS >= a.K) xs[i] = static_cast<_Float16>(0.0f);
-  }
+  if (a.K < kp) zero_x_tail(xs, a.M, RS, a.K, kp);
   const int blocks_per_row = kp / 512;  // 1 KiB blocks
   const int nblocks = a.M * blocks_per_row;
   for (int b = wave; b < nblocks; b += nw) {

@@ -33,6 +33,14 @@ WORKLOADS = {
     "gate_up_swiglu": ("swiglu", (8,), 5120, 17408),
     # the lm_head shape verifying one speculative round (k = 7 drafts, M = 8 rows)
     "lm_head_verify": ("nvfp4", (8,), 5120, 151936),
+    # one rank's share under 4-way tensor parallelism (column shards; down and
+    # o_proj shard K), at M = 1, 4 (k = 3 drafts) and 8 (k = 7 drafts)
+    "up_tp4":      ("nvfp4", (1, 4, 8), 5120, 4352),
+    "gate_up_tp4": ("nvfp4", (1, 4, 8), 5120, 8704),
+    "down_tp4":    ("nvfp4", (1, 4, 8), 4352, 5120),
+    "qkv_tp4":     ("fp8", (1, 2, 4), 5120, 1792),
+    "o_proj_tp4":  ("fp8", (1, 2, 4), 1536, 5120),
+    "lm_head_tp4": ("nvfp4", (1, 8), 5120, 37984),
 }
 
 

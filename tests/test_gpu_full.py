@@ -41,14 +41,18 @@ def _ws(op, M, K, N):
     return torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
 
 
-@pytest.mark.parametrize("name", ["up", "gate_up", "down"])
-def test_nvfp4_full_shape_sampled(name):
+@pytest.mark.parametrize("name,ms", [("up", (1, 4)), ("gate_up", (8, 4)), ("down", (8, 4)),
+                                     ("up_tp4", (1, 4, 8)), ("gate_up_tp4", (1, 4, 8)), ("down_tp4", (1, 4, 8))])
+def test_nvfp4_full_shape_sampled(name, ms):
+    """The decode shapes in the benchmark's kernel choice, with M = 4 (k = 3
+    drafts, the long-context setting) beside the listed M, and one rank's
+    share of each shape under 4-way tensor parallelism."""
     _log(f"preparing {name}")
-    case = workload.named_case(name)
+    case = workload.named_case(name, M=8)
     K, N = case["K"], case["N"]
     blob = dev(case["blob"])
     cols = _cols(N)
-    for M in synth.WORKLOADS[name][1]:
+    for M in ms:
         x = dev(case["x"][:M])
         ws = _ws(sk.OP_NVFP4, M, K, N)
         y = torch.empty((M, N), dtype=torch.float16, device="cuda")
@@ -92,7 +96,7 @@ def test_swiglu_gate_up_full_shape_sampled():
         assert np.isfinite(h.float().cpu().numpy()).all()
 
 
-@pytest.mark.parametrize("name", ["qkv", "o_proj"])
+@pytest.mark.parametrize("name", ["qkv", "o_proj", "qkv_tp4", "o_proj_tp4"])
 def test_fp8_full_shape_sampled(name):
     _log(f"preparing {name}")
     case = workload.named_case(name)
@@ -115,9 +119,10 @@ def test_fp8_full_shape_sampled(name):
 
 
 @pytest.mark.timeout(600)
-def test_lm_head_full_shape_argmax_bit_exact():
-    _log("preparing lm_head")
-    case = workload.named_case("lm_head")
+@pytest.mark.parametrize("name", ["lm_head", "lm_head_tp4"])
+def test_lm_head_full_shape_argmax_bit_exact(name):
+    _log(f"preparing {name}")
+    case = workload.named_case(name)
     K, N = case["K"], case["N"]
     blob = dev(case["blob"])
     _log("oracle logits (float64, full rows)")
