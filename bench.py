@@ -13,7 +13,7 @@ shape the measured read ceiling: the library's read probe (skinny_read_probe,
 one 9 KiB block per wavefront like one packed unit) over the same rotating
 copies, plus the probe over a 2 GiB buffer.
 
-    python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head|gate_up_swiglu|lm_head_verify] [--M m]
+    python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head|gate_up_swiglu|lm_head_verify|block] [--M m]
 
 Each step reads a different one of R byte-identical copies of the weights
 (R copies exceed 600 MB) so that the 256 MB Infinity Cache cannot serve them.
@@ -276,6 +276,53 @@ def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_p
     return res, (case if keep_case else None)
 
 
+def measure_block(M, steps, warmup):
+    """One decoder block's GEMMs in the published mixed allocation, through one
+    layer-table call per step: qkv and o_proj in FP8, gate+up (SwiGLU pair) and
+    down in NVFP4.  Each layer reads a different one of R copies per step."""
+    import numpy as np
+    import torch
+    import fp8_quantized_skinny_amd as sk
+    from fp8_quantized_skinny_amd import workload, synth
+
+    t = time.perf_counter()
+    _, _, Kq, Nq = synth.WORKLOADS["qkv"]
+    _, _, Ko, No = synth.WORKLOADS["o_proj"]
+    _, _, Kg, F = synth.WORKLOADS["gate_up_swiglu"]
+    _, _, Kd, Nd = synth.WORKLOADS["down"]
+    qkv, o = workload.fp8_case(M, Kq, Nq), workload.fp8_case(M, Ko, No)
+    gu, dn = workload.swiglu_case(M, Kg, F), workload.nvfp4_case(M, Kd, Nd)
+    wbytes = sum(c["weight_bytes"] for c in (qkv, o, gu, dn))
+    log(f"prepared the block (4 layers, {wbytes / 1e6:.1f} MB) in {time.perf_counter() - t:.1f} s")
+    R = max(2, math.ceil(MIN_ROTATION_BYTES / wbytes))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    tables = []
+    for _ in range(R):
+        tables.append([(sk.LAYER_FP8, dev(qkv["codes"]), dev(qkv["scales"]), Kq, Nq),
+                       (sk.LAYER_FP8, dev(o["codes"]), dev(o["scales"]), Ko, No),
+                       (sk.LAYER_SWIGLU, dev(gu["blob"]), None, Kg, F),
+                       (sk.LAYER_NVFP4, dev(dn["blob"]), None, Kd, Nd)])
+    xs = [dev(c["x"]) for c in (qkv, o, gu, dn)]
+    ys = [torch.empty((M, n), dtype=torch.float16, device="cuda") for n in (Nq, No, F, Nd)]
+    n = sk.layers_workspace_bytes(tables[0], M)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, s):
+        sk.layers_run(tables[i % R], xs, ys, workspace=ws, stream=s)
+    for i in range(warmup):
+        step(i, stream.cuda_stream)
+    torch.cuda.synchronize()
+    gpu_ms = time_graph(step, steps, stream)
+    us = gpu_ms * 1e3 / steps
+    gbs = wbytes / (us * 1e-6) / 1e9
+    log(f"block M={M}: {us:.2f} us per step")
+    return {"workload": f"decoder block M={M}: qkv FP8 {Kq}x{Nq}, o_proj FP8 {Ko}x{No}, "
+                        f"gate+up NVFP4 SwiGLU {Kg}x2x{F}, down NVFP4 {Kd}x{Nd}",
+            "M": M, "weight_bytes": wbytes, "weight_copies": R, "us_per_step": round(us, 3),
+            "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -291,6 +338,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes, "copies": 5}), flush=True)
+        return
+    if args.workload == "block":
+        res = measure_block(args.M or 8, args.steps, args.warmup)
+        print(json.dumps({"metric": METRIC, "value": res["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "ms_per_step": round(res["us_per_step"] * 1e-3, 6),
+                          "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+                          "data": "synthetic", "config": res}), flush=True)
         return
     cfg = tuple(int(v) for v in args.config.split(",")) if args.config else None
     head, case = measure(args.workload, args.M, cfg, args.steps, args.warmup,

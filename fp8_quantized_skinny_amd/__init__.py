@@ -17,6 +17,7 @@ from ._lib import lib
 
 OK, EINVAL, ESHAPE, EALIGN, ESIZE, EHIP, EFORMAT = range(7)
 OP_NVFP4, OP_FP8, OP_LM_HEAD, OP_SWIGLU = 0, 1, 2, 3
+LAYER_NVFP4, LAYER_FP8, LAYER_SWIGLU = 0, 1, 2
 ENGINE_VALU, ENGINE_MFMA, ENGINE_STREAM = 0, 1, 2
 
 
@@ -274,3 +275,48 @@ def lm_head_verify_greedy(w_packed, x, drafts, idx, result, N, workspace=None, s
         st = lib().lm_head_verify_greedy_config(wp, xp, dp, ip, rp, M, K, N, ws, wsb, _stream(stream), *config)
     _check(st, "lm_head_verify_greedy")
     return result
+
+
+def _layer_table(layers):
+    """[(kind, weights, scales or None, K, N)] -> ctypes array of skinny_layer (weights/scales: CUDA tensors)."""
+    import torch
+    from ._lib import SkinnyLayer
+    table = (SkinnyLayer * len(layers))()
+    for i, (kind, w, sc, K, N) in enumerate(layers):
+        table[i].kind = kind
+        table[i].weights = _dev(w, torch.uint8, f"layers[{i}].weights").value
+        table[i].scales = None if sc is None else _dev(sc, torch.float32, f"layers[{i}].scales").value
+        table[i].K, table[i].N = K, N
+    return table
+
+
+def layers_workspace_bytes(layers, M):
+    """Workspace bytes that serve every layer of a mixed-allocation table at M rows."""
+    return int(lib().skinny_layers_workspace_bytes(_layer_table(layers), len(layers), M))
+
+
+def layers_run(layers, xs, ys, workspace=None, stream=None):
+    """Run a mixed-allocation layer table: layer i maps xs[i] (CUDA fp16 [M, K_i]) to ys[i]
+    ([M, N_i]) with nvfp4_gemm, fp8_gemm or nvfp4_gemm_swiglu according to its kind.
+
+    layers: [(kind, weights, scales or None, K, N)], kind LAYER_NVFP4, LAYER_FP8 or LAYER_SWIGLU;
+    weights: the packed blob or the FP8 codes (CUDA uint8), scales: FP8 block scales (CUDA f32)."""
+    import torch
+    n = len(layers)
+    if len(xs) != n or len(ys) != n:
+        raise ValueError("one x and one y per layer")
+    M = xs[0].shape[0]
+    for i, ((kind, w, sc, K, N), x, y) in enumerate(zip(layers, xs, ys)):
+        _shape_checks(x, M, K, y, N, f"ys[{i}]")
+        if kind == LAYER_FP8:
+            small = w.numel() < N * K or sc is None or sc.numel() < (-(-N // 128)) * (-(-K // 128))
+        else:
+            small = w.numel() < packed_bytes(K, swiglu_packed_cols(N) if kind == LAYER_SWIGLU else N)
+        if small:
+            raise ValueError(f"layers[{i}]: weights or scales smaller than its shape requires")
+    table = _layer_table(layers)
+    xp = (ctypes.c_void_p * n)(*[_dev(x, torch.float16, "x").value for x in xs])
+    yp = (ctypes.c_void_p * n)(*[_dev(y, torch.float16, "y").value for y in ys])
+    ws, wsb = _workspace(workspace, int(lib().skinny_layers_workspace_bytes(table, n, M)), "skinny_layers_run")
+    _check(lib().skinny_layers_run(table, n, xp, yp, M, ws, wsb, _stream(stream)), "skinny_layers_run")
+    return ys

@@ -11,6 +11,12 @@ c_int, c_size_t, c_float, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_flo
 P = c_void_p
 
 
+class SkinnyLayer(ctypes.Structure):
+    """struct skinny_layer of skinny.h."""
+    _fields_ = [("kind", c_int), ("weights", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("K", c_int), ("N", c_int)]
+
+
 def _declare(lib):
     sig = {
         "nvfp4_pack": (c_int, [P, P, c_float, c_int, c_int, P, ctypes.POINTER(c_size_t)]),
@@ -35,6 +41,9 @@ def _declare(lib):
         "fp8_quantize": (c_int, [P, c_int, c_int, P, P]),
         "skinny_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
         "skinny_strerror": (ctypes.c_char_p, [c_int]),
+        "skinny_layers_workspace_bytes": (c_size_t, [ctypes.POINTER(SkinnyLayer), c_int, c_int]),
+        "skinny_layers_run": (c_int, [ctypes.POINTER(SkinnyLayer), c_int, ctypes.POINTER(P), ctypes.POINTER(P),
+                                      c_int, P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -57,4 +66,5 @@ EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp
             "fp8_quantize", "skinny_workspace_bytes", "skinny_strerror", "nvfp4_gemm_config",
             "fp8_gemm_config", "lm_head_gemm_argmax_config", "skinny_workspace_bytes_config",
             "skinny_config_supported", "skinny_read_probe", "nvfp4_pack_swiglu", "nvfp4_gemm_swiglu",
-            "nvfp4_gemm_swiglu_config", "lm_head_verify_greedy", "lm_head_verify_greedy_config")
+            "nvfp4_gemm_swiglu_config", "lm_head_verify_greedy", "lm_head_verify_greedy_config",
+            "skinny_layers_workspace_bytes", "skinny_layers_run")

@@ -636,6 +636,82 @@ int lm_head_verify_greedy(const void* w_packed, const uint16_t* x, const int32_t
                                       stream, c.engine, c.ct, c.nw, c.ksplit);
 }
 
+// Host-side checks and workspace need of one layer of a mixed-allocation
+// table, exactly those of the call the layer maps to (so that a table is
+// rejected before anything is enqueued).
+static int layer_check(const skinny_layer& l, const uint16_t* x, const uint16_t* y, int M, size_t* need) {
+  switch (l.kind) {
+    case SKINNY_LAYER_NVFP4: {
+      int s = nvfp4_common_checks(l.weights, x, y, M, l.K, l.N);
+      if (s) return s;
+      if (!aligned(y, 16)) return SKINNY_EALIGN;
+      *need = nvfp4_workspace_layout(default_nvfp4_cfg(M, l.K, l.N, false), M, l.K, l.N, false).total;
+      return SKINNY_OK;
+    }
+    case SKINNY_LAYER_FP8: {
+      if (!l.weights || !l.scales || !x || !y) return SKINNY_EINVAL;
+      int s = check_shape(M, l.K, l.N);
+      if (s) return s;
+      if (!aligned(l.weights, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(l.scales, 4))
+        return SKINNY_EALIGN;
+      *need = fp8_workspace_layout(default_fp8_cfg(M, l.K, l.N), M, l.K, l.N).total;
+      return SKINNY_OK;
+    }
+    case SKINNY_LAYER_SWIGLU: {
+      int s = swiglu_shape(M, l.K, l.N);
+      if (s) return s;
+      s = nvfp4_common_checks(l.weights, x, y, M, l.K, l.N);
+      if (s) return s;
+      if (!aligned(y, 16)) return SKINNY_EALIGN;
+      const int Np = swiglu_packed_cols(l.N);
+      *need = nvfp4_workspace_layout(default_nvfp4_cfg(M, l.K, Np, false), M, l.K, Np, false).total;
+      return SKINNY_OK;
+    }
+    default:
+      return SKINNY_EINVAL;
+  }
+}
+
+size_t skinny_layers_workspace_bytes(const skinny_layer* layers, int n, int M) {
+  if (!layers || n < 1) return 0;
+  size_t most = 0;
+  const uint16_t* fake = reinterpret_cast<const uint16_t*>(static_cast<uintptr_t>(256));  // aligned stand-in
+  for (int i = 0; i < n; ++i) {
+    skinny_layer l = layers[i];
+    if (!l.weights) l.weights = fake;
+    if (l.kind == SKINNY_LAYER_FP8 && !l.scales) l.scales = reinterpret_cast<const float*>(fake);
+    size_t need = 0;
+    if (layer_check(l, fake, fake, M, &need) != SKINNY_OK) return 0;
+    most = std::max(most, need);
+  }
+  return most;
+}
+
+int skinny_layers_run(const skinny_layer* layers, int n, const uint16_t* const* x, uint16_t* const* y, int M,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!layers || !x || !y || n < 1) return SKINNY_EINVAL;
+  for (int i = 0; i < n; ++i) {
+    size_t need = 0;
+    int s = layer_check(layers[i], x[i], y[i], M, &need);
+    if (s) return s;
+    s = check_workspace(workspace, workspace_bytes, need);
+    if (s) return s;
+  }
+  for (int i = 0; i < n; ++i) {
+    const skinny_layer& l = layers[i];
+    int s = SKINNY_OK;
+    if (l.kind == SKINNY_LAYER_NVFP4)
+      s = nvfp4_gemm(l.weights, x[i], y[i], M, l.K, l.N, workspace, workspace_bytes, stream);
+    else if (l.kind == SKINNY_LAYER_FP8)
+      s = fp8_gemm(static_cast<const uint8_t*>(l.weights), l.scales, x[i], y[i], M, l.K, l.N, workspace,
+                   workspace_bytes, stream);
+    else
+      s = nvfp4_gemm_swiglu(l.weights, x[i], y[i], M, l.K, l.N, workspace, workspace_bytes, stream);
+    if (s) return s;  // only a launch error can get here
+  }
+  return SKINNY_OK;
+}
+
 int lm_head_gemm_argmax(const void* w_packed, const uint16_t* x, int32_t* idx, uint16_t* logits,
                         int M, int K, int N, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {

@@ -210,6 +210,43 @@ int lm_head_verify_greedy(const void* w_packed, const uint16_t* x,
                           size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Mixed-allocation layer table: each layer of a published checkpoint runs in
+ * the precision it was published in, FP4 regions through the NVFP4 path and
+ * FP8 regions through the FP8 path, instead of converting the FP8 regions to
+ * NVFP4 (post, section "v1.0 -> v1.1": v1.0 served a derived all-NVFP4
+ * checkpoint, v1.1 the published mixed allocation).
+ *
+ *   kind    : SKINNY_LAYER_NVFP4 (nvfp4_gemm), SKINNY_LAYER_FP8 (fp8_gemm) or
+ *             SKINNY_LAYER_SWIGLU (nvfp4_gemm_swiglu).
+ *   weights : device: the packed blob (nvfp4_pack / nvfp4_pack_swiglu) or the
+ *             FP8 codes [N][K].
+ *   scales  : device fp32 FP8 block scales; NULL for the NVFP4 kinds.
+ *   K, N    : the layer's shape (N = F, the output columns, for a SwiGLU pair).
+ * ------------------------------------------------------------------------- */
+enum { SKINNY_LAYER_NVFP4 = 0, SKINNY_LAYER_FP8 = 1, SKINNY_LAYER_SWIGLU = 2 };
+
+typedef struct skinny_layer {
+  int kind;
+  const void* weights;
+  const float* scales;
+  int K, N;
+} skinny_layer;
+
+/* Workspace bytes that serve every layer of the table at M rows (the largest
+ * single need: the layers run one after another on one stream).  0 if none
+ * is needed or a layer is invalid. */
+size_t skinny_layers_workspace_bytes(const skinny_layer* layers, int n, int M);
+
+/* Runs layer i on x[i] -> y[i] (device fp16 [M][K_i] -> [M][N_i]) for i = 0 ..
+ * n-1, in order on `stream`, each with the library's kernel choice for its
+ * kind and shape.  x and y are host arrays of n device pointers; y[i] may be
+ * x[i+1] to chain layers.  Every layer is checked before any is enqueued: an
+ * invalid one returns its error and nothing runs. */
+int skinny_layers_run(const skinny_layer* layers, int n, const uint16_t* const* x,
+                      uint16_t* const* y, int M, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Host quantizers (offline weight preparation, not part of the GEMM).  They
  * stand in for the pages' offline FP16 -> NVFP4 conversion script (ai-manual
  * article, section "NVFP4 model conversion") and produce the canonical

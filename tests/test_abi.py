@@ -103,6 +103,43 @@ def test_verify_argument_errors():
     assert v(M=1, d=None) == sk.EINVAL and v(M=1, d=None, r=A + 2) == sk.EALIGN
 
 
+def test_layer_table_checks_every_layer_first():
+    """A table is rejected as a whole, before anything is enqueued, by the
+    checks of the call each layer maps to; the workspace serves the largest layer."""
+    from fp8_quantized_skinny_amd._lib import SkinnyLayer
+    L = lib()
+
+    def table(*layers):
+        t = (SkinnyLayer * len(layers))()
+        for i, (kind, w, sc, K, N) in enumerate(layers):
+            t[i].kind, t[i].weights, t[i].scales, t[i].K, t[i].N = kind, w, sc, K, N
+        return t
+
+    ok = [(sk.LAYER_NVFP4, A, None, 256, 512), (sk.LAYER_FP8, A, A, 256, 256), (sk.LAYER_SWIGLU, A, None, 256, 40)]
+    t = table(*ok)
+    ptrs = (ctypes.c_void_p * 4)(A, A, A, A)
+    need = max(sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120), sk.workspace_bytes(sk.OP_FP8, 8, 256, 256))
+    big = table((sk.LAYER_NVFP4, A, None, 17408, 5120), (sk.LAYER_FP8, A, A, 256, 256))
+    assert L.skinny_layers_workspace_bytes(big, 2, 8) == need > 0
+    assert L.skinny_layers_workspace_bytes(t, 3, 1) == max(sk.workspace_bytes(sk.OP_NVFP4, 1, 256, 512),
+                                                          sk.workspace_bytes(sk.OP_FP8, 1, 256, 256),
+                                                          sk.workspace_bytes(sk.OP_SWIGLU, 1, 256, 40))
+    run = lambda t, n, M=1, x=ptrs, y=ptrs, ws=None, wsb=0: L.skinny_layers_run(t, n, x, y, M, ws, wsb, None)
+    assert run(None, 1) == sk.EINVAL and run(t, 0) == sk.EINVAL
+    for bad, code in [((7, A, None, 256, 512), sk.EINVAL),                 # unknown kind
+                      ((sk.LAYER_FP8, A, None, 256, 256), sk.EINVAL),      # FP8 without scales
+                      ((sk.LAYER_NVFP4, MIS, None, 256, 512), sk.EALIGN),
+                      ((sk.LAYER_NVFP4, A, None, 250, 512), sk.ESHAPE),
+                      ((sk.LAYER_SWIGLU, A, None, 256, 0), sk.ESHAPE)]:
+        # the bad layer last: the good ones before it must not have been enqueued either,
+        # which holds because every check runs before the first launch
+        assert run(table(*ok, bad), 4) == code, bad
+    assert run(big, 2, M=8) == sk.EINVAL                                   # missing workspace
+    assert run(t, 3, M=9) == sk.ESHAPE
+    mis = (ctypes.c_void_p * 4)(A, MIS, A, A)
+    assert run(t, 3, x=mis) == sk.EALIGN
+
+
 def test_fp8_gemm_argument_errors():
     L = lib()
     f = lambda **k: L.fp8_gemm(k.get("w", A), k.get("s", A), k.get("x", A), k.get("y", A), k.get("M", 1),

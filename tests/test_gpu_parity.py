@@ -334,3 +334,43 @@ def test_lm_head_verify_greedy_rounds():
             assert list(res) == want_res, (cfg, drafts, list(res), want_res)
     idx, res = run_verify(case, 1, [])
     assert list(res) == [0, int(want_idx[0])]
+
+
+# ------------------------------------------------------ mixed-allocation table
+def test_layer_table_mixed_allocation():
+    """A stack of FP4, FP8 and SwiGLU-pair layers run through one table call:
+    every layer's output against that layer's oracle, at M = 1 and 8, and a
+    chained pair whose second layer reads the first one's output."""
+    nv = workload.nvfp4_case(8, 1040, 300, seed=41)
+    f8 = workload.fp8_case(8, 512, 384, seed=42)
+    sw = workload.swiglu_case(8, 1040, 100, seed=43)
+    dn = workload.nvfp4_case(8, 2064, 48, seed=44)
+    f8b = workload.fp8_case(8, 400, 300, seed=45)
+    layers = [(sk.LAYER_NVFP4, dev(nv["blob"]), None, 1040, 300),
+              (sk.LAYER_FP8, dev(f8["codes"]), dev(f8["scales"]), 512, 384),
+              (sk.LAYER_SWIGLU, dev(sw["blob"]), None, 1040, 100),
+              (sk.LAYER_NVFP4, dev(dn["blob"]), None, 2064, 48),
+              (sk.LAYER_FP8, dev(f8b["codes"]), dev(f8b["scales"]), 400, 300)]
+    for M in (8, 1):
+        refs = [ref_nvfp4(nv, M), ref_fp8(f8, M), oracle.nvfp4_swiglu(sw["x"][:M], sw["gate"], sw["up"]),
+                ref_nvfp4(dn, M), ref_fp8(f8b, M)]
+        xs = [dev(c["x"][:M]) for c in (nv, f8, sw, dn, f8b)]
+        ys = [torch.full((M, l[4]), float("nan"), dtype=torch.float16, device="cuda") for l in layers]
+        n = sk.layers_workspace_bytes(layers, M)
+        ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
+        sk.layers_run(layers, xs, ys, workspace=ws)
+        torch.cuda.synchronize()
+        for i, (y, ref) in enumerate(zip(ys, refs)):
+            _check(y.float().cpu().numpy(), ref, f"layer {i} M={M}")
+    # chain: NVFP4 1040 -> 512, then FP8 512 -> 384 on the first layer's fp16 output
+    a = workload.nvfp4_case(4, 1040, 512, seed=46)
+    b = workload.fp8_case(4, 512, 384, seed=47)
+    chain = [(sk.LAYER_NVFP4, dev(a["blob"]), None, 1040, 512), (sk.LAYER_FP8, dev(b["codes"]), dev(b["scales"]), 512, 384)]
+    mid = torch.empty((4, 512), dtype=torch.float16, device="cuda")
+    out = torch.empty((4, 384), dtype=torch.float16, device="cuda")
+    n = sk.layers_workspace_bytes(chain, 4)
+    sk.layers_run(chain, [dev(a["x"]), mid], [mid, out],
+                  workspace=torch.empty(n, dtype=torch.uint8, device="cuda") if n else None)
+    torch.cuda.synchronize()
+    _check(mid.float().cpu().numpy(), ref_nvfp4(a), "chain layer 0")
+    _check(out.float().cpu().numpy(), oracle.fp8_gemm(mid.cpu().numpy(), b["codes"], b["scales"]), "chain layer 1")
