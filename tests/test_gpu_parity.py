@@ -374,3 +374,72 @@ def test_layer_table_mixed_allocation():
     torch.cuda.synchronize()
     _check(mid.float().cpu().numpy(), ref_nvfp4(a), "chain layer 0")
     _check(out.float().cpu().numpy(), oracle.fp8_gemm(mid.cpu().numpy(), b["codes"], b["scales"]), "chain layer 1")
+
+
+# ------------------------------------------------------------- graph replay
+def test_hip_graph_replays_match_eager():
+    """Every entry point captured in one HIP graph (K-split choices with their
+    workspaces included) and replayed three times, with the outputs cleared by
+    eager fills between replays: each replay equals the eager results bit for
+    bit.  The benchmark times graph replays, and the library records no memset
+    into a stream (workspaces are written before they are read)."""
+    nv = workload.nvfp4_case(8, 2064, 1000, seed=51)
+    f8 = workload.fp8_case(4, 1040, 640, seed=52)
+    sw = workload.swiglu_case(8, 2064, 72, seed=53)
+    lm = workload.nvfp4_case(8, 1024, 3000, seed=54)
+    want_idx = oracle.argmax_rows(ref_nvfp4(lm))[0]
+    drafts = dev(np.asarray(want_idx[:7], np.int32))
+    bufs = {"nv": dev(nv["blob"]), "nvx": dev(nv["x"]), "f8c": dev(f8["codes"]), "f8s": dev(f8["scales"]),
+            "f8x": dev(f8["x"]), "sw": dev(sw["blob"]), "swx": dev(sw["x"]), "lm": dev(lm["blob"]), "lmx": dev(lm["x"])}
+    outs = {"y_nv": torch.empty((8, 1000), dtype=torch.float16, device="cuda"),
+            "y_nv_split": torch.empty((8, 1000), dtype=torch.float16, device="cuda"),
+            "y_f8": torch.empty((4, 640), dtype=torch.float16, device="cuda"),
+            "h": torch.empty((8, 72), dtype=torch.float16, device="cuda"),
+            "h_split": torch.empty((8, 72), dtype=torch.float16, device="cuda"),
+            "idx": torch.empty((8,), dtype=torch.int32, device="cuda"),
+            "vidx": torch.empty((8,), dtype=torch.int32, device="cuda"),
+            "res": torch.empty((9,), dtype=torch.int32, device="cuda")}
+    split = (1, 2, 4, 2)                                   # three K spans over two workgroups
+    f8split = (1, 1, 1, 3)
+    wss = {k: ws_for(op, M, K, N, cfg) for k, (op, M, K, N, cfg) in {
+        "nv": (sk.OP_NVFP4, 8, 2064, 1000, None), "nv_split": (sk.OP_NVFP4, 8, 2064, 1000, split),
+        "f8": (sk.OP_FP8, 4, 1040, 640, f8split), "sw": (sk.OP_SWIGLU, 8, 2064, 72, None),
+        "sw_split": (sk.OP_SWIGLU, 8, 2064, 72, split), "lm": (sk.OP_LM_HEAD, 8, 1024, 3000, None),
+        "lmv": (sk.OP_LM_HEAD, 8, 1024, 3000, None)}.items()}
+    assert wss["nv_split"] is not None and wss["f8"] is not None and wss["sw_split"] is not None
+    assert sk.config_supported(sk.OP_NVFP4, 8, 2064, 1000, split) and sk.config_supported(sk.OP_SWIGLU, 8, 2064, 72, split)
+    assert sk.config_supported(sk.OP_FP8, 4, 1040, 640, f8split)
+
+    def calls(stream):
+        sk.nvfp4_gemm(bufs["nv"], bufs["nvx"], outs["y_nv"], workspace=wss["nv"], stream=stream)
+        sk.nvfp4_gemm(bufs["nv"], bufs["nvx"], outs["y_nv_split"], config=split, workspace=wss["nv_split"], stream=stream)
+        sk.fp8_gemm(bufs["f8c"], bufs["f8s"], bufs["f8x"], outs["y_f8"], config=f8split, workspace=wss["f8"], stream=stream)
+        sk.nvfp4_gemm_swiglu(bufs["sw"], bufs["swx"], outs["h"], workspace=wss["sw"], stream=stream)
+        sk.nvfp4_gemm_swiglu(bufs["sw"], bufs["swx"], outs["h_split"], config=split, workspace=wss["sw_split"], stream=stream)
+        sk.lm_head_gemm_argmax(bufs["lm"], bufs["lmx"], outs["idx"], 3000, workspace=wss["lm"], stream=stream)
+        sk.lm_head_verify_greedy(bufs["lm"], bufs["lmx"], drafts, outs["vidx"], outs["res"], 3000,
+                                 workspace=wss["lmv"], stream=stream)
+
+    calls(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    _check(eager["y_nv"].float().cpu().numpy(), ref_nvfp4(nv), "graph test eager nvfp4")
+    _check(eager["y_nv_split"].float().cpu().numpy(), ref_nvfp4(nv), "graph test eager nvfp4 split")
+    _check(eager["h_split"].float().cpu().numpy(), oracle.nvfp4_swiglu(sw["x"], sw["gate"], sw["up"]), "graph test eager swiglu split")
+    assert list(eager["res"].cpu().numpy()) == [7] + [int(v) for v in want_idx] and np.array_equal(eager["idx"].cpu().numpy(), want_idx)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            calls(cap)
+    for rep in range(3):
+        for k, v in outs.items():                          # eager clears between replays
+            v.fill_(-1) if v.dtype == torch.int32 else v.fill_(float("nan"))
+        for w in wss.values():
+            if w is not None:
+                w.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v, eager[k]), f"replay {rep}: {k} differs from the eager call"
