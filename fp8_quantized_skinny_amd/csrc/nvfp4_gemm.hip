@@ -162,11 +162,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu_m1(Nvfp4Args a) {
     u32x4 c[kChunksPerUnit];
     uint32_t xv[kChunksPerUnit];
     const int kx = (P.s0 + P.s) * kUnitK + 2 * P.lane;
+    // A pair past K reads the last pair of x instead (index in [0, K-2],
+    // even, so the 4-byte load stays in the row): the packed codes and
+    // scales there are zero, so it adds exact zeros for finite x.  Clamping
+    // the address rather than selecting zero after the load keeps the loads
+    // independent; a select on loaded data made the first chunk wait for
+    // half of the unit's loads.
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
       c[j] = load16(p + j * kChunkBytes);
-      const int k = kx + j * kChunkK;
-      xv[j] = k < a.K ? *reinterpret_cast<const uint32_t*>(a.x + k) : 0u;
+      xv[j] = *reinterpret_cast<const uint32_t*>(a.x + min(kx + j * kChunkK, a.K - 2));
     }
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
