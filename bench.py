@@ -7,11 +7,13 @@ scales) per step divided by the time per step, with every input already
 resident in HBM.  The headline workload is the NVFP4 GEMV at M = 1,
 K = 5120, N = 17408 (an MLP up-projection at decode): one step is one
 nvfp4_gemm call.  The same line also carries the two NVFP4 M = 8 shapes (fused
-gate+up 5120 x 34816 and down 17408 x 5120) and the gate+up shape with the
-fused SwiGLU epilogue (nvfp4_gemm_swiglu, h[8, 17408]), timed the same way, and for each
-shape the measured read ceiling: the library's read probe (skinny_read_probe,
-one 9 KiB block per wavefront like one packed unit) over the same rotating
-copies, plus the probe over a 2 GiB buffer.
+gate+up 5120 x 34816 and down 17408 x 5120), the gate+up shape with the
+fused SwiGLU epilogue (nvfp4_gemm_swiglu, h[8, 17408]) and one decoder block's
+four GEMMs in the published FP8/FP4 mix (skinny_layers_run) at M = 8, timed
+the same way.  For the headline and the two plain M = 8 shapes it also reports
+the measured read ceiling: the library's read probe (skinny_read_probe, one
+9 KiB block per wavefront like one packed unit) over the same rotating copies,
+plus the probe over a 2 GiB buffer.
 
     python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head|gate_up_swiglu|lm_head_verify|block] [--M m]
 
@@ -351,10 +353,12 @@ def main():
                          keep_case=not args.no_cpu_baseline, ceiling=not args.headline_only,
                          large_probe=True)
     companions = []
+    block = None
     if not args.headline_only and args.workload == "up" and cfg is None:
         for name in ("gate_up", "down", "gate_up_swiglu"):
             r, _ = measure(name, 8, None, args.steps, args.warmup, ceiling=name != "gate_up_swiglu")
             companions.append(r)
+        block = measure_block(8, args.steps, args.warmup)
     value = head["GB/s"]
     out = {
         "metric": METRIC,
@@ -370,7 +374,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {**head, "timed": "one HIP-graph replay of K steps, weights rotated over R copies",
-                   "m8_shapes": companions},
+                   "m8_shapes": companions, "decoder_block_m8": block},
         "roofline": {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4),
                      "traffic": None if cfg else recorded_traffic(args.workload, head["M"]),
