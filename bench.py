@@ -15,7 +15,7 @@ the measured read ceiling: the library's read probe (skinny_read_probe, one
 9 KiB block per wavefront like one packed unit) over the same rotating copies,
 plus the probe over a 2 GiB buffer.
 
-    python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head|gate_up_swiglu|lm_head_verify|block] [--M m]
+    python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head|gate_up_swiglu|lm_head_verify|block|qkv_packed|o_proj_packed] [--M m]
 
 Each step reads a different one of R byte-identical copies of the weights
 (R copies exceed 600 MB) so that the 256 MB Infinity Cache cannot serve them.
@@ -66,6 +66,8 @@ def log(msg):
 
 
 def describe(case, name):
+    if name.endswith("_packed"):
+        return f"FP8 E4M3 W8A16 {name} M={case['M']} K={case['K']} N={case['N']} (codes packed by fp8_pack)"
     if case["fmt"] == "swiglu":
         return f"NVFP4 W4A16 {name} M={case['M']} K={case['K']} F={case['F']} (gate and up, h = silu(gate) * up)"
     fmt = "NVFP4 W4A16" if case["fmt"] == "nvfp4" else "FP8 E4M3 W8A16"
@@ -212,6 +214,7 @@ def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_p
     t = time.perf_counter()
     case = (workload.nvfp4_case(M, K, N) if fmt == "nvfp4" else
             workload.swiglu_case(M, K, N) if fmt == "swiglu" else workload.fp8_case(M, K, N))
+    packed = fmt == "fp8p"
     log(f"prepared {describe(case, name)} in {time.perf_counter() - t:.1f} s")
     wbytes = case["weight_bytes"]
     R = max(2, math.ceil(MIN_ROTATION_BYTES / wbytes))
@@ -224,7 +227,8 @@ def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_p
         copies = [dev(case["blob"]) for _ in range(R)]
         scales = None
     else:
-        copies = [dev(case["codes"]) for _ in range(R)]
+        codes = sk.fp8_pack(case["codes"], K, N) if packed else case["codes"]
+        copies = [dev(codes) for _ in range(R)]
         scales = dev(case["scales"])
     verify = name == "lm_head_verify"
     op = (sk.OP_LM_HEAD if name in ("lm_head", "lm_head_verify") else sk.OP_SWIGLU if fmt == "swiglu" else
@@ -251,6 +255,9 @@ def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_p
         elif op == sk.OP_SWIGLU:   # N is F here; y holds h[M, F]
             st = (L.nvfp4_gemm_swiglu_config(w, xp, yp, M, K, N, wsp, wsn, s, *cfg) if cfg
                   else L.nvfp4_gemm_swiglu(w, xp, yp, M, K, N, wsp, wsn, s))
+        elif packed:
+            st = (L.fp8_gemm_packed_config(w, scales.data_ptr(), xp, yp, M, K, N, wsp, wsn, s, *cfg) if cfg
+                  else L.fp8_gemm_packed(w, scales.data_ptr(), xp, yp, M, K, N, wsp, wsn, s))
         else:
             st = (L.fp8_gemm_config(w, scales.data_ptr(), xp, yp, M, K, N, wsp, wsn, s, *cfg) if cfg
                   else L.fp8_gemm(w, scales.data_ptr(), xp, yp, M, K, N, wsp, wsn, s))
@@ -280,8 +287,9 @@ def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_p
 
 def measure_block(M, steps, warmup):
     """One decoder block's GEMMs in the published mixed allocation, through one
-    layer-table call per step: qkv and o_proj in FP8, gate+up (SwiGLU pair) and
-    down in NVFP4.  Each layer reads a different one of R copies per step."""
+    layer-table call per step: qkv and o_proj in FP8 (codes packed by
+    fp8_pack), gate+up (SwiGLU pair) and down in NVFP4.  Each layer reads a
+    different one of R copies per step."""
     import numpy as np
     import torch
     import fp8_quantized_skinny_amd as sk
@@ -298,10 +306,11 @@ def measure_block(M, steps, warmup):
     log(f"prepared the block (4 layers, {wbytes / 1e6:.1f} MB) in {time.perf_counter() - t:.1f} s")
     R = max(2, math.ceil(MIN_ROTATION_BYTES / wbytes))
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    qkv_p, o_p = sk.fp8_pack(qkv["codes"], Kq, Nq), sk.fp8_pack(o["codes"], Ko, No)
     tables = []
     for _ in range(R):
-        tables.append([(sk.LAYER_FP8, dev(qkv["codes"]), dev(qkv["scales"]), Kq, Nq),
-                       (sk.LAYER_FP8, dev(o["codes"]), dev(o["scales"]), Ko, No),
+        tables.append([(sk.LAYER_FP8_PACKED, dev(qkv_p), dev(qkv["scales"]), Kq, Nq),
+                       (sk.LAYER_FP8_PACKED, dev(o_p), dev(o["scales"]), Ko, No),
                        (sk.LAYER_SWIGLU, dev(gu["blob"]), None, Kg, F),
                        (sk.LAYER_NVFP4, dev(dn["blob"]), None, Kd, Nd)])
     xs = [dev(c["x"]) for c in (qkv, o, gu, dn)]
@@ -319,7 +328,7 @@ def measure_block(M, steps, warmup):
     us = gpu_ms * 1e3 / steps
     gbs = wbytes / (us * 1e-6) / 1e9
     log(f"block M={M}: {us:.2f} us per step")
-    return {"workload": f"decoder block M={M}: qkv FP8 {Kq}x{Nq}, o_proj FP8 {Ko}x{No}, "
+    return {"workload": f"decoder block M={M}: qkv FP8 {Kq}x{Nq}, o_proj FP8 {Ko}x{No} (packed), "
                         f"gate+up NVFP4 SwiGLU {Kg}x2x{F}, down NVFP4 {Kd}x{Nd}",
             "M": M, "weight_bytes": wbytes, "weight_copies": R, "us_per_step": round(us, 3),
             "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}

@@ -17,7 +17,7 @@ from ._lib import lib
 
 OK, EINVAL, ESHAPE, EALIGN, ESIZE, EHIP, EFORMAT = range(7)
 OP_NVFP4, OP_FP8, OP_LM_HEAD, OP_SWIGLU = 0, 1, 2, 3
-LAYER_NVFP4, LAYER_FP8, LAYER_SWIGLU = 0, 1, 2
+LAYER_NVFP4, LAYER_FP8, LAYER_SWIGLU, LAYER_FP8_PACKED = 0, 1, 2, 3
 ENGINE_VALU, ENGINE_MFMA, ENGINE_STREAM = 0, 1, 2
 
 
@@ -207,6 +207,45 @@ def nvfp4_gemm_swiglu(w_packed, x, h, workspace=None, stream=None, config=None):
     return h
 
 
+def fp8_pack(codes, K, N):
+    """Canonical FP8 codes [N][K] (host) -> packed blob (host uint8 array) for fp8_gemm_packed."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    if codes.size < N * K:
+        raise ValueError("codes smaller than N x K")
+    size = ctypes.c_size_t(0)
+    _check(lib().fp8_pack(_host_ptr(codes), K, N, None, ctypes.byref(size)), "fp8_pack")
+    out = np.zeros(size.value, np.uint8)
+    _check(lib().fp8_pack(_host_ptr(codes), K, N, _host_ptr(out), ctypes.byref(size)), "fp8_pack")
+    return out
+
+
+def fp8_packed_bytes(K, N):
+    size = ctypes.c_size_t(0)
+    dummy = np.zeros(1, np.uint8)
+    _check(lib().fp8_pack(_host_ptr(dummy), K, N, None, ctypes.byref(size)), "fp8_pack")
+    return size.value
+
+
+def fp8_gemm_packed(w_packed, block_scales, x, y, workspace=None, stream=None, config=None):
+    """y[M, N] fp16 = x . (E4M3(c) * S) with the codes as an fp8_pack blob (CUDA uint8)."""
+    import torch
+    M, K = x.shape
+    N = y.shape[-1]
+    _shape_checks(x, M, K, y, N, "y")
+    if w_packed.numel() < fp8_packed_bytes(K, N) or block_scales.numel() < (-(-N // 128)) * (-(-K // 128)):
+        raise ValueError("w_packed or block_scales smaller than the shape requires")
+    wp = _dev(w_packed, torch.uint8, "w_packed")
+    sp = _dev(block_scales, torch.float32, "block_scales")
+    xp, yp = _dev(x, torch.float16, "x"), _dev(y, torch.float16, "y")
+    ws, wsb = _workspace(workspace, workspace_bytes(OP_FP8, M, K, N, config), "fp8_gemm_packed")
+    if config is None:
+        st = lib().fp8_gemm_packed(wp, sp, xp, yp, M, K, N, ws, wsb, _stream(stream))
+    else:
+        st = lib().fp8_gemm_packed_config(wp, sp, xp, yp, M, K, N, ws, wsb, _stream(stream), *config)
+    _check(st, "fp8_gemm_packed")
+    return y
+
+
 def fp8_gemm(w, block_scales, x, y, workspace=None, stream=None, config=None):
     """y[M, N] fp16 = x . (E4M3(w) * S); w CUDA uint8 [N, K], block_scales CUDA f32 [N/128, K/128]."""
     import torch
@@ -308,8 +347,9 @@ def layers_run(layers, xs, ys, workspace=None, stream=None):
     M = xs[0].shape[0]
     for i, ((kind, w, sc, K, N), x, y) in enumerate(zip(layers, xs, ys)):
         _shape_checks(x, M, K, y, N, f"ys[{i}]")
-        if kind == LAYER_FP8:
-            small = w.numel() < N * K or sc is None or sc.numel() < (-(-N // 128)) * (-(-K // 128))
+        if kind in (LAYER_FP8, LAYER_FP8_PACKED):
+            need = N * K if kind == LAYER_FP8 else fp8_packed_bytes(K, N)
+            small = w.numel() < need or sc is None or sc.numel() < (-(-N // 128)) * (-(-K // 128))
         else:
             small = w.numel() < packed_bytes(K, swiglu_packed_cols(N) if kind == LAYER_SWIGLU else N)
         if small:

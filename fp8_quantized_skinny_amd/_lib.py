@@ -28,6 +28,10 @@ def _declare(lib):
                                              c_int, c_int, c_int, c_int]),
         "fp8_gemm": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
         "fp8_gemm_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int, c_int]),
+        "fp8_pack": (c_int, [P, c_int, c_int, P, ctypes.POINTER(c_size_t)]),
+        "fp8_gemm_packed": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
+        "fp8_gemm_packed_config": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P,
+                                           c_int, c_int, c_int, c_int]),
         "lm_head_gemm_argmax": (c_int, [P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
         "lm_head_verify_greedy": (c_int, [P, P, P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
         "lm_head_verify_greedy_config": (c_int, [P, P, P, P, P, c_int, c_int, c_int, P, c_size_t, P,
@@ -67,4 +71,5 @@ EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp
             "fp8_gemm_config", "lm_head_gemm_argmax_config", "skinny_workspace_bytes_config",
             "skinny_config_supported", "skinny_read_probe", "nvfp4_pack_swiglu", "nvfp4_gemm_swiglu",
             "nvfp4_gemm_swiglu_config", "lm_head_verify_greedy", "lm_head_verify_greedy_config",
-            "skinny_layers_workspace_bytes", "skinny_layers_run")
+            "skinny_layers_workspace_bytes", "skinny_layers_run", "fp8_pack", "fp8_gemm_packed",
+            "fp8_gemm_packed_config")

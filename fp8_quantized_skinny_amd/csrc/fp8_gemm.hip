@@ -20,6 +20,11 @@
 // two 16-byte pieces K = 128j + 64h + 16grp .. +16 (h = 0, 1) of column c, so
 // each load instruction covers 64 contiguous bytes of 16 columns.  Pieces past
 // K or columns past N read a clamped valid address and are zeroed.
+//
+// The packed variant reads the same pieces from a blob of fp8_pack: 8 KiB
+// units (one tile x 512 K) in span-major order, in which piece 2j + h of a
+// unit holds each lane's 16 bytes next to each other, so every load
+// instruction is one contiguous KiB, as for NVFP4 (padding is zero codes).
 #include <hip/hip_runtime.h>
 
 #include "common.cuh"
@@ -30,9 +35,10 @@ namespace {
 
 constexpr int kFp8UnitChunks = 4;
 constexpr int kFp8UnitK = kFp8UnitChunks * kChunkK;  // 512
+static_assert(kFp8UnitK == kFp8PackK && 2 * kFp8UnitChunks * 1024 == kFp8UnitBytes, "FP8 packed unit");
 
 struct Fp8Args {
-  const uint8_t* w;
+  const uint8_t* w;  // canonical codes [N][K], or the packed units (fp8_pack) of the blob
   const float* scales;
   const _Float16* x;
   _Float16* y;
@@ -104,7 +110,7 @@ __device__ __forceinline__ void fp8_steps(const u32x4 (&w)[kFp8UnitChunks][2], c
   }
 }
 
-template <int CT>
+template <int CT, bool PACKED>
 __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(8))) void fp8_mfma(Fp8Args a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const Fp8Plan P(a, CT);
@@ -131,15 +137,27 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
     // Codes: pieces past K load from the row start instead (x is zero there,
     // so they add exact zeros); no select on loaded data, which would make
     // every load wait for the previous one.
-    const int n = min(tt * kTileCols + cl, a.N - 1);
-    const uint8_t* row = a.w + static_cast<size_t>(n) * a.K;
-    const int k0 = u * kFp8UnitK + grp * 16;
+    if (PACKED) {
+      // Unit (tt, u) of the span-major blob; an idle wavefront's u (past the
+      // last unit) is clamped to a real unit it never uses.
+      const uint8_t* up =
+          a.w + (static_cast<size_t>(min(u, a.ku - 1)) * a.nt + tt) * kFp8UnitBytes + P.lane * 16;
 #pragma unroll
-    for (int j = 0; j < kFp8UnitChunks; ++j) {
+      for (int j = 0; j < kFp8UnitChunks; ++j) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = k0 + j * kChunkK + 64 * h;
-        w[j][h] = load16(row + (k + 16 <= a.K ? k : 0));
+        for (int h = 0; h < 2; ++h) w[j][h] = load16(up + (2 * j + h) * 1024);
+      }
+    } else {
+      const int n = min(tt * kTileCols + cl, a.N - 1);
+      const uint8_t* row = a.w + static_cast<size_t>(n) * a.K;
+      const int k0 = u * kFp8UnitK + grp * 16;
+#pragma unroll
+      for (int j = 0; j < kFp8UnitChunks; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = k0 + j * kChunkK + 64 * h;
+          w[j][h] = load16(row + (k + 16 <= a.K ? k : 0));
+        }
       }
     }
   }
@@ -189,18 +207,21 @@ bool fp8_cfg_supported(const LaunchCfg& c, int M, int K) {
   return fp8_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
 }
 
-#define SKINNY_FP8_DISPATCH(CT)                                                    \
-  if (cfg.ct == CT) {                                                              \
-    hipLaunchKernelGGL((fp8_mfma<CT>), grid, dim3(cfg.nw * 64), lds, stream, a);   \
-    e = hipGetLastError();                                                         \
+#define SKINNY_FP8_DISPATCH(CT)                                                           \
+  if (cfg.ct == CT) {                                                                     \
+    if (packed)                                                                           \
+      hipLaunchKernelGGL((fp8_mfma<CT, true>), grid, dim3(cfg.nw * 64), lds, stream, a);  \
+    else                                                                                  \
+      hipLaunchKernelGGL((fp8_mfma<CT, false>), grid, dim3(cfg.nw * 64), lds, stream, a); \
+    e = hipGetLastError();                                                                \
   }
 
 hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x, uint16_t* y, int M,
-                      int K, int N, const LaunchCfg& cfg, void* workspace, hipStream_t stream) {
+                      int K, int N, const LaunchCfg& cfg, void* workspace, hipStream_t stream, bool packed) {
   const WorkspaceLayout wl = fp8_workspace_layout(cfg, M, K, N);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   Fp8Args a;
-  a.w = w;
+  a.w = packed ? w + kHeaderBytes : w;
   a.scales = scales;
   a.x = reinterpret_cast<const _Float16*>(x);
   a.y = reinterpret_cast<_Float16*>(y);

@@ -435,6 +435,54 @@ int nvfp4_pack_swiglu(const uint8_t* gate_codes, const uint8_t* gate_scales, flo
   return SKINNY_OK;
 }
 
+size_t fp8_packed_bytes(int K, int N) {
+  const size_t ku = (K + kFp8PackK - 1) / kFp8PackK, nt = (N + kTileCols - 1) / kTileCols;
+  return kHeaderBytes + ku * nt * kFp8UnitBytes;
+}
+
+int fp8_pack(const uint8_t* codes, int K, int N, void* out, size_t* out_bytes) {
+  if (!codes || !out_bytes) return SKINNY_EINVAL;
+  if (K < 16 || K % 16 != 0 || K > kMaxK || N < 1 || N > kMaxN) return SKINNY_ESHAPE;
+  const size_t total = fp8_packed_bytes(K, N);
+  if (!out) {
+    *out_bytes = total;
+    return SKINNY_OK;
+  }
+  if (*out_bytes < total) return SKINNY_ESIZE;
+  const int ku = (K + kFp8PackK - 1) / kFp8PackK, nt = (N + kTileCols - 1) / kTileCols;
+  uint8_t* blob = static_cast<uint8_t*>(out);
+  std::memset(blob, 0, total);
+  Fp8Header h{};
+  h.magic = kFp8BlobMagic;
+  h.version = kFp8BlobVersion;
+  h.K = K;
+  h.N = N;
+  h.ku = ku;
+  h.nt = nt;
+  h.unit_bytes = kFp8UnitBytes;
+  h.units_off = kHeaderBytes;
+  h.units_bytes = total - kHeaderBytes;
+  std::memcpy(blob, &h, sizeof(h));
+  // Piece q = 2j + h of unit (t, u), lane l = 16grp + c: 16 codes of column
+  // 16t + c from K = 512u + 128j + 64h + 16grp on (K % 16 == 0: a run is all
+  // in or all out of range).
+  parallel_for(nt, [&](int, int t0, int t1) {
+    for (int t = t0; t < t1; ++t)
+      for (int u = 0; u < ku; ++u) {
+        uint8_t* unit = blob + kHeaderBytes + (static_cast<size_t>(u) * nt + t) * kFp8UnitBytes;
+        for (int q = 0; q < 8; ++q)
+          for (int lane = 0; lane < 64; ++lane) {
+            const int n = t * kTileCols + (lane & 15);
+            const int k = u * kFp8PackK + (q >> 1) * 128 + (q & 1) * 64 + (lane >> 4) * 16;
+            if (n < N && k < K)
+              std::memcpy(unit + q * 1024 + lane * 16, codes + static_cast<size_t>(n) * K + k, 16);
+          }
+      }
+  });
+  *out_bytes = total;
+  return SKINNY_OK;
+}
+
 int nvfp4_quantize(const float* w, int K, int N, uint8_t* codes, uint8_t* scales, float* g_out) {
   if (!w || !codes || !scales || !g_out) return SKINNY_EINVAL;
   if (K < 16 || K % 16 != 0 || K > kMaxK || N < 1 || N > kMaxN) return SKINNY_ESHAPE;
@@ -563,6 +611,31 @@ int fp8_gemm_config(const uint8_t* w, const float* block_scales, const uint16_t*
   return launch_status(launch_fp8(w, block_scales, x, y, M, K, N, cfg, workspace, stream));
 }
 
+int fp8_gemm_packed_config(const void* w_packed, const float* block_scales, const uint16_t* x, uint16_t* y,
+                           int M, int K, int N, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           int engine, int ct, int nw, int ksplit) {
+  if (!w_packed || !block_scales || !x || !y) return SKINNY_EINVAL;
+  int s = check_shape(M, K, N);
+  if (s) return s;
+  if (!aligned(w_packed, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(block_scales, 4))
+    return SKINNY_EALIGN;
+  const LaunchCfg cfg{engine, ct, nw, ksplit};
+  if (!fp8_cfg_supported(cfg, M, K)) return SKINNY_EINVAL;
+  s = check_workspace(workspace, workspace_bytes, fp8_workspace_layout(cfg, M, K, N).total);
+  if (s) return s;
+  return launch_status(launch_fp8(static_cast<const uint8_t*>(w_packed), block_scales, x, y, M, K, N, cfg,
+                                  workspace, stream, true));
+}
+
+int fp8_gemm_packed(const void* w_packed, const float* block_scales, const uint16_t* x, uint16_t* y, int M,
+                    int K, int N, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int s = check_shape(M, K, N);
+  if (s) return s;
+  const LaunchCfg c = default_fp8_cfg(M, K, N);
+  return fp8_gemm_packed_config(w_packed, block_scales, x, y, M, K, N, workspace, workspace_bytes, stream,
+                                c.engine, c.ct, c.nw, c.ksplit);
+}
+
 int fp8_gemm(const uint8_t* w, const float* block_scales, const uint16_t* x, uint16_t* y,
              int M, int K, int N, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int s = check_shape(M, K, N);
@@ -651,7 +724,8 @@ static int layer_check(const skinny_layer& l, const uint16_t* x, const uint16_t*
       *need = nvfp4_workspace_layout(default_nvfp4_cfg(M, l.K, l.N, false), M, l.K, l.N, false).total;
       return SKINNY_OK;
     }
-    case SKINNY_LAYER_FP8: {
+    case SKINNY_LAYER_FP8:
+    case SKINNY_LAYER_FP8_PACKED: {
       if (!l.weights || !l.scales || !x || !y) return SKINNY_EINVAL;
       int s = check_shape(M, l.K, l.N);
       if (s) return s;
@@ -682,7 +756,8 @@ size_t skinny_layers_workspace_bytes(const skinny_layer* layers, int n, int M) {
   for (int i = 0; i < n; ++i) {
     skinny_layer l = layers[i];
     if (!l.weights) l.weights = fake;
-    if (l.kind == SKINNY_LAYER_FP8 && !l.scales) l.scales = reinterpret_cast<const float*>(fake);
+    if ((l.kind == SKINNY_LAYER_FP8 || l.kind == SKINNY_LAYER_FP8_PACKED) && !l.scales)
+      l.scales = reinterpret_cast<const float*>(fake);
     size_t need = 0;
     if (layer_check(l, fake, fake, M, &need) != SKINNY_OK) return 0;
     most = std::max(most, need);
@@ -708,6 +783,8 @@ int skinny_layers_run(const skinny_layer* layers, int n, const uint16_t* const* 
     else if (l.kind == SKINNY_LAYER_FP8)
       s = fp8_gemm(static_cast<const uint8_t*>(l.weights), l.scales, x[i], y[i], M, l.K, l.N, workspace,
                    workspace_bytes, stream);
+    else if (l.kind == SKINNY_LAYER_FP8_PACKED)
+      s = fp8_gemm_packed(l.weights, l.scales, x[i], y[i], M, l.K, l.N, workspace, workspace_bytes, stream);
     else
       s = nvfp4_gemm_swiglu(l.weights, x[i], y[i], M, l.K, l.N, workspace, workspace_bytes, stream);
     if (s) return s;  // only a launch error can get here

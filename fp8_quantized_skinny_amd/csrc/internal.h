@@ -77,6 +77,29 @@ struct Geometry {
 };
 Geometry nvfp4_geometry(int K, int N);
 
+// ---------------------------------------------------------------------------
+// Packed FP8 blob (fp8_pack), optional: the canonical [N][K] codes work too.
+//
+//   [0, 256)     header (Fp8Header, zero padded)
+//   [256, ...)   units: KU x NT units of 8192 bytes, span-major: unit (t, u)
+//                at 256 + (u * NT + t) * 8192
+//
+// Unit (t, u) covers columns 16t .. 16t+15 and K 512u .. 512u+511: eight
+// 1 KiB pieces q = 2j + h; in piece q, lane l = 16*grp + c owns bytes
+// [16l, 16l+16): the E4M3 codes of column 16t+c at K = 512u + 128j + 64h +
+// 16grp + i (i = 0..15).  K is padded to a multiple of 512 and N to a
+// multiple of 16 with zero codes.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kFp8BlobMagic = 0x38464B53u;  // "SKF8" little-endian
+constexpr uint32_t kFp8BlobVersion = 1;
+constexpr int kFp8PackK = 512;
+constexpr size_t kFp8UnitBytes = 8192;
+struct Fp8Header {
+  uint32_t magic, version, K, N, ku, nt, unit_bytes, reserved;
+  uint64_t units_off, units_bytes;
+};
+static_assert(sizeof(Fp8Header) <= kHeaderBytes, "header too large");
+
 // Launch parameters picked by the host for one call.
 struct LaunchCfg {
   int engine;  // 0 = VALU dot2 (M = 1 only), 1 = MFMA 16x16x32 f16, 2 = streaming MFMA
@@ -104,9 +127,10 @@ hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y,
                         int M, int K, int N, const LaunchCfg& cfg,
                         int32_t* idx, void* workspace, hipStream_t stream, int swiglu_F = 0,
                         const int32_t* drafts = nullptr, int32_t* verify = nullptr);
+// packed: w is an fp8_pack blob (header included) instead of canonical codes.
 hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x,
                       uint16_t* y, int M, int K, int N, const LaunchCfg& cfg,
-                      void* workspace, hipStream_t stream);
+                      void* workspace, hipStream_t stream, bool packed = false);
 bool nvfp4_cfg_supported(const LaunchCfg& cfg, int M, int K, bool argmax);
 bool fp8_cfg_supported(const LaunchCfg& cfg, int M, int K);
 size_t nvfp4_mfma_lds_bytes(int M, int S, int nw);

@@ -41,6 +41,9 @@ WORKLOADS = {
     "qkv_tp4":     ("fp8", (1, 2, 4), 5120, 1792),
     "o_proj_tp4":  ("fp8", (1, 2, 4), 1536, 5120),
     "lm_head_tp4": ("nvfp4", (1, 8), 5120, 37984),
+    # the FP8 shapes with the codes reordered by fp8_pack
+    "qkv_packed":    ("fp8p", (1, 2, 4), 5120, 7168),
+    "o_proj_packed": ("fp8p", (1, 2, 4), 6144, 5120),
 }
 
 

@@ -164,6 +164,29 @@ int fp8_gemm(const uint8_t* w, const float* block_scales, const uint16_t* x,
              size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * fp8_pack / fp8_gemm_packed -- the FP8 GEMM on codes reordered once for
+ * 128-bit coalesced loads, as nvfp4_pack does for NVFP4 (the codes and their
+ * values are unchanged; only the byte order differs).
+ *
+ * fp8_pack: codes host uint8 [N][K] (K % 16 == 0); out host buffer of
+ * *out_bytes bytes, or NULL to query the size.  The blob is a 256-byte header
+ * (magic "SKF8", version, K, N) followed by 8 KiB units, one per 16 columns x
+ * 512 K (zero codes past K and N), all tiles of the first 512-K span, then
+ * of the next, each ordered so that every 16-byte load of a wavefront lane is
+ * contiguous with its neighbours' (one KiB per load instruction).  The caller
+ * uploads the blob as-is.
+ *
+ * fp8_gemm_packed: w_packed = that blob in device memory, for exactly this K
+ * and N (not checked: device memory); everything else as fp8_gemm, same
+ * results bit for bit.
+ * ------------------------------------------------------------------------- */
+int fp8_pack(const uint8_t* codes, int K, int N, void* out, size_t* out_bytes);
+int fp8_gemm_packed(const void* w_packed, const float* block_scales,
+                    const uint16_t* x, uint16_t* y, int M, int K, int N,
+                    void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * lm_head_gemm_argmax -- vocabulary-sized NVFP4 GEMM with a fused per-row
  * argmax (post: the native 4-bit lm_head row of the bandwidth table; the
  * drafter should propose greedy / local-argmax tokens, section "This is a
@@ -216,14 +239,15 @@ int lm_head_verify_greedy(const void* w_packed, const uint16_t* x,
  * NVFP4 (post, section "v1.0 -> v1.1": v1.0 served a derived all-NVFP4
  * checkpoint, v1.1 the published mixed allocation).
  *
- *   kind    : SKINNY_LAYER_NVFP4 (nvfp4_gemm), SKINNY_LAYER_FP8 (fp8_gemm) or
- *             SKINNY_LAYER_SWIGLU (nvfp4_gemm_swiglu).
- *   weights : device: the packed blob (nvfp4_pack / nvfp4_pack_swiglu) or the
- *             FP8 codes [N][K].
+ *   kind    : SKINNY_LAYER_NVFP4 (nvfp4_gemm), SKINNY_LAYER_FP8 (fp8_gemm),
+ *             SKINNY_LAYER_SWIGLU (nvfp4_gemm_swiglu) or
+ *             SKINNY_LAYER_FP8_PACKED (fp8_gemm_packed).
+ *   weights : device: the packed blob (nvfp4_pack / nvfp4_pack_swiglu /
+ *             fp8_pack) or the canonical FP8 codes [N][K].
  *   scales  : device fp32 FP8 block scales; NULL for the NVFP4 kinds.
  *   K, N    : the layer's shape (N = F, the output columns, for a SwiGLU pair).
  * ------------------------------------------------------------------------- */
-enum { SKINNY_LAYER_NVFP4 = 0, SKINNY_LAYER_FP8 = 1, SKINNY_LAYER_SWIGLU = 2 };
+enum { SKINNY_LAYER_NVFP4 = 0, SKINNY_LAYER_FP8 = 1, SKINNY_LAYER_SWIGLU = 2, SKINNY_LAYER_FP8_PACKED = 3 };
 
 typedef struct skinny_layer {
   int kind;
@@ -299,6 +323,11 @@ int fp8_gemm_config(const uint8_t* w, const float* block_scales,
                     const uint16_t* x, uint16_t* y, int M, int K, int N,
                     void* workspace, size_t workspace_bytes, hipStream_t stream,
                     int engine, int ct, int nw, int ksplit);
+int fp8_gemm_packed_config(const void* w_packed, const float* block_scales,
+                           const uint16_t* x, uint16_t* y, int M, int K, int N,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, int engine, int ct, int nw,
+                           int ksplit);
 int lm_head_gemm_argmax_config(const void* w_packed, const uint16_t* x,
                                int32_t* idx, uint16_t* logits, int M, int K,
                                int N, void* workspace, size_t workspace_bytes,

@@ -337,6 +337,49 @@ def test_pack_places_every_byte_once(K, N):
     assert not units[~mask].any()
 
 
+@pytest.mark.parametrize("K,N", [(512, 16), (400, 20), (1040, 33), (16, 1)])
+def test_fp8_pack_places_every_byte_once(K, N):
+    """Every code lands where the documented FP8 unit layout says; the rest is zero."""
+    rng = np.random.default_rng(K * 7 + N)
+    codes = rng.integers(1, 256, size=(N, K), dtype=np.uint8)          # no zero code, so padding is visible
+    blob = sk.fp8_pack(codes, K, N)
+    ku, nt = -(-K // 512), -(-N // 16)
+    assert blob.size == 256 + ku * nt * 8192 == sk.fp8_packed_bytes(K, N)
+    h = blob[:64]
+    assert bytes(h[:4]) == b"SKF8" and list(h[4:32].view(np.uint32)) == [1, K, N, ku, nt, 8192, 0]
+    units = blob[256:].reshape(ku, nt, 8, 4, 16, 16)                   # [span][tile][piece][grp][c][byte]
+    seen = np.zeros(codes.shape, np.int64)
+    mask = np.zeros(units.shape, bool)
+    for n in range(N):
+        t, c = divmod(n, 16)
+        for k in range(K):
+            u, r = divmod(k, 512)
+            j, r = divmod(r, 128)
+            hh, r = divmod(r, 64)
+            grp, i = divmod(r, 16)
+            assert units[u, t, 2 * j + hh, grp, c, i] == codes[n, k]
+            seen[n, k] += 1
+            mask[u, t, 2 * j + hh, grp, c, i] = True
+    assert (seen == 1).all() and not units[~mask].any()
+
+
+def test_fp8_pack_errors_and_packed_gemm_arguments():
+    L = lib()
+    c = np.zeros((4, 256), np.uint8)
+    size = ctypes.c_size_t(0)
+    assert L.fp8_pack(c.ctypes.data, 256, 4, None, ctypes.byref(size)) == sk.OK and size.value == 256 + 8192
+    assert L.fp8_pack(None, 256, 4, None, ctypes.byref(size)) == sk.EINVAL
+    assert L.fp8_pack(c.ctypes.data, 250, 4, None, ctypes.byref(size)) == sk.ESHAPE
+    out = np.zeros(256 + 8192 - 1, np.uint8)
+    size.value = out.size
+    assert L.fp8_pack(c.ctypes.data, 256, 4, out.ctypes.data, ctypes.byref(size)) == sk.ESIZE
+    g = lambda M=1, K=256, N=256, w=A, s=A, x=A, y=A: L.fp8_gemm_packed(w, s, x, y, M, K, N, None, 0, None)
+    assert g(w=None) == sk.EINVAL and g(s=None) == sk.EINVAL
+    assert g(M=9) == sk.ESHAPE and g(K=24) == sk.ESHAPE
+    assert g(w=MIS) == sk.EALIGN and g(y=MIS) == sk.EALIGN and g(s=A + 2) == sk.EALIGN
+    assert L.fp8_gemm_packed_config(A, A, A, A, 1, 256, 256, None, 0, None, 0, 1, 1, 1) == sk.EINVAL
+
+
 def test_pack_is_deterministic():
     w, _ = synth.draw(1, 384, 48, seed=2)
     c, s, g = sk.nvfp4_quantize(w)

@@ -102,6 +102,7 @@ def test_fp8_full_shape_sampled(name):
     case = workload.named_case(name)
     K, N = case["K"], case["N"]
     w, s = dev(case["codes"]), dev(case["scales"])
+    wp = dev(sk.fp8_pack(case["codes"], K, N))
     cols = _cols(N)
     for M in synth.WORKLOADS[name][1]:
         ws = _ws(sk.OP_FP8, M, K, N)
@@ -109,8 +110,11 @@ def test_fp8_full_shape_sampled(name):
         sk.fp8_gemm(w, s, dev(case["x"][:M]), y, workspace=ws)
         y2 = torch.empty_like(y)
         sk.fp8_gemm(w, s, dev(case["x"][:M]), y2, workspace=ws)
+        yp = torch.empty_like(y)
+        sk.fp8_gemm_packed(wp, s, dev(case["x"][:M]), yp, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(y, y2), "not deterministic"
+        assert torch.equal(y, yp), "packed codes give a different result"
         got = y.float().cpu().numpy()[:, cols]
         ref = oracle.fp8_gemm(case["x"][:M], case["codes"], case["scales"], cols=cols)
         m = oracle.compare(got, ref)

@@ -79,12 +79,16 @@ def run_nvfp4(case, M=None, config=None, guard=0):
     return y.float().cpu().numpy()
 
 
-def run_fp8(case, M=None, config=None):
+def run_fp8(case, M=None, config=None, packed=False):
     M = case["M"] if M is None else M
     K, N = case["K"], case["N"]
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    sk.fp8_gemm(dev(case["codes"]), dev(case["scales"]), dev(case["x"][:M]), y, config=config,
-                workspace=ws_for(sk.OP_FP8, M, K, N, config))
+    ws = ws_for(sk.OP_FP8, M, K, N, config)
+    if packed:
+        sk.fp8_gemm_packed(dev(sk.fp8_pack(case["codes"], K, N)), dev(case["scales"]), dev(case["x"][:M]), y,
+                           config=config, workspace=ws)
+    else:
+        sk.fp8_gemm(dev(case["codes"]), dev(case["scales"]), dev(case["x"][:M]), y, config=config, workspace=ws)
     torch.cuda.synchronize()
     return y.float().cpu().numpy()
 
@@ -138,12 +142,13 @@ def test_fp8_one_hot_reproduces_codes_exactly():
     deq = oracle.fp8_dequant(codes, scales)
     assert np.array_equal(deq.astype(np.float16).astype(np.float64), deq)
     eye = np.eye(K, dtype=np.float16)
-    for cfg in cfgs(1, K, unit_k=512):
-        out = np.empty((K, N))
-        for r0 in range(0, K, 8):
-            case["x"] = eye[r0:r0 + 8]
-            out[r0:r0 + 8] = run_fp8(case, M=8, config=cfg)
-        assert np.array_equal(out, deq), f"config {cfg}"
+    for packed in (False, True):
+        for cfg in cfgs(1, K, unit_k=512):
+            out = np.empty((K, N))
+            for r0 in range(0, K, 8):
+                case["x"] = eye[r0:r0 + 8]
+                out[r0:r0 + 8] = run_fp8(case, M=8, config=cfg, packed=packed)
+            assert np.array_equal(out, deq), f"config {cfg} packed={packed}"
 
 
 # -------------------------------------------------------- tolerance parity
@@ -221,11 +226,15 @@ SMALL_FP8 = [(1, 256, 256), (2, 272, 100), (4, 400, 300), (8, 1040, 1000), (3, 1
 
 @pytest.mark.parametrize("shape", SMALL_FP8)
 def test_fp8_parity_all_configs(shape):
+    """Canonical and packed codes, every kernel choice: within the bounds of the
+    oracle, and the packed path equal to the canonical one bit for bit (same
+    pieces in the same registers, only the byte order in memory differs)."""
     case = workload.fp8_case(*shape, seed=sum(shape))
     ref = ref_fp8(case)
-    for cfg in cfgs(1, case["K"], unit_k=512):
-        _check(run_fp8(case, config=cfg), ref, f"{shape} {cfg}")
-    _check(run_fp8(case), ref, f"{shape} default")
+    for cfg in cfgs(1, case["K"], unit_k=512) + [None]:
+        y = run_fp8(case, config=cfg)
+        _check(y, ref, f"{shape} {cfg}")
+        assert np.array_equal(run_fp8(case, config=cfg, packed=True), y), f"{shape} {cfg} packed"
 
 
 def test_deterministic_repeats(small_nvfp4):
@@ -350,11 +359,12 @@ def test_layer_table_mixed_allocation():
               (sk.LAYER_FP8, dev(f8["codes"]), dev(f8["scales"]), 512, 384),
               (sk.LAYER_SWIGLU, dev(sw["blob"]), None, 1040, 100),
               (sk.LAYER_NVFP4, dev(dn["blob"]), None, 2064, 48),
-              (sk.LAYER_FP8, dev(f8b["codes"]), dev(f8b["scales"]), 400, 300)]
+              (sk.LAYER_FP8, dev(f8b["codes"]), dev(f8b["scales"]), 400, 300),
+              (sk.LAYER_FP8_PACKED, dev(sk.fp8_pack(f8b["codes"], 400, 300)), dev(f8b["scales"]), 400, 300)]
     for M in (8, 1):
         refs = [ref_nvfp4(nv, M), ref_fp8(f8, M), oracle.nvfp4_swiglu(sw["x"][:M], sw["gate"], sw["up"]),
-                ref_nvfp4(dn, M), ref_fp8(f8b, M)]
-        xs = [dev(c["x"][:M]) for c in (nv, f8, sw, dn, f8b)]
+                ref_nvfp4(dn, M), ref_fp8(f8b, M), ref_fp8(f8b, M)]
+        xs = [dev(c["x"][:M]) for c in (nv, f8, sw, dn, f8b, f8b)]
         ys = [torch.full((M, l[4]), float("nan"), dtype=torch.float16, device="cuda") for l in layers]
         n = sk.layers_workspace_bytes(layers, M)
         ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
@@ -362,6 +372,7 @@ def test_layer_table_mixed_allocation():
         torch.cuda.synchronize()
         for i, (y, ref) in enumerate(zip(ys, refs)):
             _check(y.float().cpu().numpy(), ref, f"layer {i} M={M}")
+        assert torch.equal(ys[4], ys[5]), "packed FP8 layer differs from the canonical one"
     # chain: NVFP4 1040 -> 512, then FP8 512 -> 384 on the first layer's fp16 output
     a = workload.nvfp4_case(4, 1040, 512, seed=46)
     b = workload.fp8_case(4, 512, 384, seed=47)
