@@ -38,15 +38,18 @@ __global__ __launch_bounds__(kFinalizeThreads) void finalize_splits(const float*
   if (n0 < N) {
     const float* p = part + static_cast<size_t>(m) * N + n0;
     const size_t stride = static_cast<size_t>(M) * N;
-    // Batches of eight splits: the loads of a batch are all issued before the
-    // first add, so a call with ksplit <= 8 waits for memory only once.
+    // Batches of kBatch splits: the loads of a batch are all issued before
+    // the first add, so a call with ksplit <= kBatch (the library's own
+    // choices split at most nine ways) waits for memory only once.
+    constexpr int kBatch = 16;
     vecf s = vecf(0.0f);
-    for (int k0 = 0; k0 < ksplit; k0 += 8) {
-      vecf v[8];
+    for (int k0 = 0; k0 < ksplit; k0 += kBatch) {
+      vecf v[kBatch];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = k0 + i < ksplit ? *reinterpret_cast<const vecf*>(p + (k0 + i) * stride) : vecf(0.0f);
+      for (int i = 0; i < kBatch; ++i)
+        v[i] = k0 + i < ksplit ? *reinterpret_cast<const vecf*>(p + (k0 + i) * stride) : vecf(0.0f);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kBatch; ++i)
         if (k0 + i < ksplit) s += v[i];
     }
     const float g = gptr ? *gptr : 1.0f;
