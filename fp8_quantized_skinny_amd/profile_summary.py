@@ -114,9 +114,9 @@ def main(argv=None):
             print(f"{k:48s} {len(v):6d} {v.mean():9.3f} {np.median(v):9.3f} "
                   f"{np.percentile(v, 10):8.3f} {np.percentile(v, 90):8.3f}")
     else:
-        print(f"{'kernel':48s} {'counter':14s} {'dispatches':>10s} {'median_per_dispatch':>20s}")
+        print(f"{'kernel':48s} {'counter':18s} {'dispatches':>10s} {'median_per_dispatch':>20s}")
         for (k, c), v in sorted(counter_rows(a.db, a.match).items()):
-            print(f"{k:48s} {c:14s} {len(v):10d} {np.median(v):20.4f}")
+            print(f"{k:48s} {c:18s} {len(v):10d} {np.median(v):20.4f}")
 
 
 if __name__ == "__main__":
