@@ -99,7 +99,20 @@ def cpu_baseline(case):
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
             "sample": f"the whole workload ({case['N']} columns), {calls} calls in {dt:.1f} s; "
                       f"decode and dequantize on 1 thread, float64 matmul on {blas_threads} BLAS "
-                      f"threads; host has {os.cpu_count()} CPUs"}
+                      f"threads; host has {os.cpu_count()} CPUs, {len(os.sched_getaffinity(0))} "
+                      f"usable by this process ({cpu_model()})"}
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, or "unknown CPU"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.partition(":")[2].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def recorded_traffic(name, M):
