@@ -41,6 +41,10 @@ def _dev(t, dtype, name):
     import torch
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if t.device.index != torch.cuda.current_device():
+        # The kernels run on the current device; a buffer of another device
+        # would be passed to them as a foreign address.
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
