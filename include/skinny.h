@@ -30,6 +30,12 @@
  *     memory: the caller owns every buffer.
  *   - GEMM calls are asynchronous on the caller's stream; faults of the kernel
  *     itself surface at the next synchronisation (HIP semantics).
+ *   - Device buffers are passed as bare pointers, so the library cannot check
+ *     their sizes or a device blob's header on the host: the caller
+ *     guarantees that each buffer holds what the call's shape needs (a blob
+ *     packed for exactly this K and N, x of M * K, y of M * N elements).  Any
+ *     other buffer gives undefined results and may read out of bounds.  The
+ *     Python binding checks these sizes before every call.
  *   - K must be a multiple of 16 (one NVFP4 scale block); N >= 1; K >= 16.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  */
