@@ -11,6 +11,7 @@ import re
 
 import numpy as np
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import oracle
 import fp8_quantized_skinny_amd as sk
@@ -413,6 +414,27 @@ def test_host_quantizer_special_inputs():
     # huge dynamic range: saturation paths agree with the oracle
     w = np.geomspace(1e-30, 1e30, 32 * 16).astype(np.float32).reshape(32, 16)
     w[::3] *= -1
+    c1, s1, g1 = sk.nvfp4_quantize(w)
+    c2, s2, g2 = oracle.nvfp4_quantize(w)
+    assert g1 == g2 and np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    a1, b1 = sk.fp8_quantize(w)
+    a2, b2 = oracle.fp8_quantize(w)
+    assert np.array_equal(a1, a2) and np.array_equal(b1, b2)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 16), st.integers(1, 40), st.integers(0, 2**31 - 1),
+       st.floats(-40.0, 26.0), st.floats(0.0, 12.0), st.floats(0.0, 0.5))
+def test_host_quantizers_match_oracle_random_shapes_and_ranges(k_blocks, N, seed, lo, span, zero_frac):
+    """Host quantizers against the oracle, bit for bit, on random shapes, dynamic
+    ranges (magnitudes log-uniform over [10^lo, 10^(lo+span)], from float32
+    subnormals up to 10^38), signs and zeros."""
+    K = 16 * k_blocks
+    rng = np.random.default_rng(seed)
+    mag = 10.0 ** rng.uniform(lo, lo + span, size=(K, N))
+    w = (np.where(rng.random((K, N)) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+    w[rng.random((K, N)) < zero_frac] = 0.0
+    assert np.isfinite(w).all()                # 10^38 is below the float32 maximum
     c1, s1, g1 = sk.nvfp4_quantize(w)
     c2, s2, g2 = oracle.nvfp4_quantize(w)
     assert g1 == g2 and np.array_equal(c1, c2) and np.array_equal(s1, s2)
