@@ -390,7 +390,7 @@ def test_layer_table_mixed_allocation():
 # ------------------------------------------------------------- graph replay
 def test_hip_graph_replays_match_eager():
     """Every entry point captured in one HIP graph (K-split choices with their
-    workspaces included) and replayed three times, with the outputs cleared by
+    workspaces included, packed FP8 and a two-layer table too) and replayed three times, with the outputs cleared by
     eager fills between replays: each replay equals the eager results bit for
     bit.  The benchmark times graph replays, and the library records no memset
     into a stream (workspaces are written before they are read)."""
@@ -401,7 +401,10 @@ def test_hip_graph_replays_match_eager():
     want_idx = oracle.argmax_rows(ref_nvfp4(lm))[0]
     drafts = dev(np.asarray(want_idx[:7], np.int32))
     bufs = {"nv": dev(nv["blob"]), "nvx": dev(nv["x"]), "f8c": dev(f8["codes"]), "f8s": dev(f8["scales"]),
-            "f8x": dev(f8["x"]), "sw": dev(sw["blob"]), "swx": dev(sw["x"]), "lm": dev(lm["blob"]), "lmx": dev(lm["x"])}
+            "f8x": dev(f8["x"]), "sw": dev(sw["blob"]), "swx": dev(sw["x"]), "lm": dev(lm["blob"]), "lmx": dev(lm["x"]),
+            "f8p": dev(sk.fp8_pack(f8["codes"], 1040, 640)), "nvx4": dev(nv["x"][:4])}
+    # a two-layer table at M = 4: NVFP4 then packed FP8 (independent inputs)
+    layers = [(sk.LAYER_NVFP4, bufs["nv"], None, 2064, 1000), (sk.LAYER_FP8_PACKED, bufs["f8p"], bufs["f8s"], 1040, 640)]
     outs = {"y_nv": torch.empty((8, 1000), dtype=torch.float16, device="cuda"),
             "y_nv_split": torch.empty((8, 1000), dtype=torch.float16, device="cuda"),
             "y_f8": torch.empty((4, 640), dtype=torch.float16, device="cuda"),
@@ -409,14 +412,19 @@ def test_hip_graph_replays_match_eager():
             "h_split": torch.empty((8, 72), dtype=torch.float16, device="cuda"),
             "idx": torch.empty((8,), dtype=torch.int32, device="cuda"),
             "vidx": torch.empty((8,), dtype=torch.int32, device="cuda"),
-            "res": torch.empty((9,), dtype=torch.int32, device="cuda")}
+            "res": torch.empty((9,), dtype=torch.int32, device="cuda"),
+            "y_f8p": torch.empty((4, 640), dtype=torch.float16, device="cuda"),
+            "ly_nv": torch.empty((4, 1000), dtype=torch.float16, device="cuda"),
+            "ly_f8p": torch.empty((4, 640), dtype=torch.float16, device="cuda")}
     split = (1, 2, 4, 2)                                   # three K spans over two workgroups
     f8split = (1, 1, 1, 3)
     wss = {k: ws_for(op, M, K, N, cfg) for k, (op, M, K, N, cfg) in {
         "nv": (sk.OP_NVFP4, 8, 2064, 1000, None), "nv_split": (sk.OP_NVFP4, 8, 2064, 1000, split),
         "f8": (sk.OP_FP8, 4, 1040, 640, f8split), "sw": (sk.OP_SWIGLU, 8, 2064, 72, None),
         "sw_split": (sk.OP_SWIGLU, 8, 2064, 72, split), "lm": (sk.OP_LM_HEAD, 8, 1024, 3000, None),
-        "lmv": (sk.OP_LM_HEAD, 8, 1024, 3000, None)}.items()}
+        "lmv": (sk.OP_LM_HEAD, 8, 1024, 3000, None), "f8p": (sk.OP_FP8, 4, 1040, 640, f8split)}.items()}
+    n_layers = sk.layers_workspace_bytes(layers, 4)
+    wss["layers"] = torch.empty(n_layers, dtype=torch.uint8, device="cuda") if n_layers else None
     assert wss["nv_split"] is not None and wss["f8"] is not None and wss["sw_split"] is not None
     assert sk.config_supported(sk.OP_NVFP4, 8, 2064, 1000, split) and sk.config_supported(sk.OP_SWIGLU, 8, 2064, 72, split)
     assert sk.config_supported(sk.OP_FP8, 4, 1040, 640, f8split)
@@ -430,6 +438,10 @@ def test_hip_graph_replays_match_eager():
         sk.lm_head_gemm_argmax(bufs["lm"], bufs["lmx"], outs["idx"], 3000, workspace=wss["lm"], stream=stream)
         sk.lm_head_verify_greedy(bufs["lm"], bufs["lmx"], drafts, outs["vidx"], outs["res"], 3000,
                                  workspace=wss["lmv"], stream=stream)
+        sk.fp8_gemm_packed(bufs["f8p"], bufs["f8s"], bufs["f8x"], outs["y_f8p"], config=f8split, workspace=wss["f8p"],
+                           stream=stream)
+        sk.layers_run(layers, [bufs["nvx4"], bufs["f8x"]], [outs["ly_nv"], outs["ly_f8p"]], workspace=wss["layers"],
+                      stream=stream)
 
     calls(torch.cuda.current_stream())
     torch.cuda.synchronize()
@@ -438,6 +450,9 @@ def test_hip_graph_replays_match_eager():
     _check(eager["y_nv_split"].float().cpu().numpy(), ref_nvfp4(nv), "graph test eager nvfp4 split")
     _check(eager["h_split"].float().cpu().numpy(), oracle.nvfp4_swiglu(sw["x"], sw["gate"], sw["up"]), "graph test eager swiglu split")
     assert list(eager["res"].cpu().numpy()) == [7] + [int(v) for v in want_idx] and np.array_equal(eager["idx"].cpu().numpy(), want_idx)
+    assert torch.equal(eager["y_f8p"], eager["y_f8"]), "packed FP8 differs from canonical FP8"
+    _check(eager["ly_nv"].float().cpu().numpy(), ref_nvfp4(nv, 4), "graph test eager layer table, NVFP4 layer")
+    _check(eager["ly_f8p"].float().cpu().numpy(), ref_fp8(f8), "graph test eager layer table, packed FP8 layer")
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     with torch.cuda.stream(cap):
