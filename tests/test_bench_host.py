@@ -52,3 +52,31 @@ def test_read_probe_size_rejects_tiny_buffers():
     bench = _bench()
     with pytest.raises(ValueError):
         bench.probe_size(10**6, [_Buf(100)])
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_use():
+    """--gpus N > 1 ends with status 2 and says why; it touches no GPU first."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("name,M,weight_bytes", [("up", 1, 50135044), ("gate_up", 8, 100270084),
+                                                 ("down", 8, 50135044)])
+def test_recorded_traffic_is_plausible_when_current(name, M, weight_bytes):
+    """The HBM traffic bench.py reports comes from a committed counter summary
+    taken on the current kernel sources.  When one exists, it must lie near the
+    weight bytes (every byte read once; 2% below for the copy calibration's
+    own error) and at most 1.2 times them (x, partial sums, line rounding)."""
+    traffic = _bench().recorded_traffic(name, M)
+    if traffic is None:
+        pytest.skip(f"no counter summary for {name} M={M} on the current kernel sources")
+    assert 0.98 * weight_bytes <= traffic <= 1.2 * weight_bytes
+
+
+def test_cpu_model_is_a_name():
+    name = _bench().cpu_model()
+    assert isinstance(name, str) and name.strip()
