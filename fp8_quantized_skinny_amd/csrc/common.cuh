@@ -123,6 +123,23 @@ __device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k)
   return k;
 }
 
+// Largest key of each of R independent values over the WIDTH lanes of each
+// lane group (every lane gets them).  Each shuffle step exchanges all R
+// values before comparing any, so the R reductions share one LDS round trip
+// per step; reducing them one after another waits for a round trip at every
+// step of every value (6 x R waits over 64 lanes).
+template <int R, int WIDTH = 64>
+__device__ __forceinline__ void wave_max_keys(unsigned long long (&k)[R]) {
+#pragma unroll
+  for (int off = WIDTH / 2; off >= 1; off >>= 1) {
+    unsigned long long o[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) o[r] = __shfl_xor(k[r], off, WIDTH);
+#pragma unroll
+    for (int r = 0; r < R; ++r) k[r] = o[r] > k[r] ? o[r] : k[r];
+  }
+}
+
 }  // namespace skinny
 
 #endif

@@ -349,8 +349,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
     // Largest key over the 16 columns of each row group, then over the
     // workgroup's tiles: one candidate per row.
     __shared__ unsigned long long best[kMaxWaves][kMaxRows];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) key[i] = wave_max_key<16>(key[i]);
+    wave_max_keys<4, 16>(key);
     if (P.wave < CT && P.lane < 32 && cl == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) best[P.wave][grp * 4 + i] = key[i];
@@ -466,15 +465,20 @@ __device__ __forceinline__ void stream_units(const StreamCtx& c, Unit& A, Unit& 
     }
     const int n = (c.t0 + ti * c.step) * kTileCols + cl;
     const bool col_ok = c.lane < 32 && n < a.N;
+    unsigned long long key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = grp * 4 + i;
       const bool ok = col_ok && m < a.M;
       const float v = c.g * acc[i];
       if (ok && a.y) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(v);
-      if (EPI == kEpiArgmax) {
-        const unsigned long long k = wave_max_key<16>(ok ? argmax_key(v, n) : 0ull);
-        if (c.lane < 32 && cl == 0) c.best[grp * 4 + i] = k > c.best[grp * 4 + i] ? k : c.best[grp * 4 + i];
+      key[i] = ok ? argmax_key(v, n) : 0ull;
+    }
+    if (EPI == kEpiArgmax) {
+      wave_max_keys<4, 16>(key);
+      if (c.lane < 32 && cl == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c.best[grp * 4 + i] = key[i] > c.best[grp * 4 + i] ? key[i] : c.best[grp * 4 + i];
       }
     }
     acc = f32x4{0.f, 0.f, 0.f, 0.f};

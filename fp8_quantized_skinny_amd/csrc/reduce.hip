@@ -53,13 +53,17 @@ __global__ __launch_bounds__(kFinalizeThreads) void finalize_splits(const float*
         if (k0 + i < ksplit) s += v[i];
     }
     const float g = gptr ? *gptr : 1.0f;
+    typedef _Float16 vech __attribute__((ext_vector_type(COLS)));
+    vech h;
 #pragma unroll
     for (int c = 0; c < COLS; ++c) {
       const float v = g * s[c];
-      if (y) y[static_cast<size_t>(m) * N + n0 + c] = static_cast<_Float16>(v);
+      h[c] = static_cast<_Float16>(v);
       const unsigned long long k = argmax_key(v, n0 + c);
       key = k > key ? k : key;
     }
+    // One store of the COLS halves (8-byte aligned: N and n0 are multiples of COLS).
+    if (y) *reinterpret_cast<vech*>(y + static_cast<size_t>(m) * N + n0) = h;
   }
   if (ARGMAX) {
     key = wave_max_key(key);
@@ -101,10 +105,10 @@ __global__ __launch_bounds__(256) void argmax_reduce(const unsigned long long* c
     for (int m = 0; m < kMaxRows; ++m) k[m] = v[m] > k[m] ? v[m] : k[m];
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  wave_max_keys<kMaxRows>(k);
+  if (lane == 0) {
 #pragma unroll
-  for (int m = 0; m < kMaxRows; ++m) {
-    const unsigned long long w = wave_max_key(k[m]);
-    if (lane == 0) red[wave][m] = w;
+    for (int m = 0; m < kMaxRows; ++m) red[wave][m] = k[m];
   }
   __syncthreads();
   if (threadIdx.x < static_cast<unsigned>(M)) {
