@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int k = k0 + j * kChunkK + 64 * h;
-          w[j][h] = load16(row + (k + 16 <= a.K ? k : 0));
+          w[j][h] = load16_shared_line(row + (k + 16 <= a.K ? k : 0));
         }
       }
     }
