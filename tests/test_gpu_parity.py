@@ -273,15 +273,18 @@ def test_lm_head_argmax_and_logits(shape):
     assert np.array_equal(idx, want)
 
 
-def test_lm_head_ties_go_to_lowest_column():
-    M, K, N = 4, 256, 700
+@pytest.mark.parametrize("M,K", [(4, 256), (8, 2048)])
+def test_lm_head_ties_go_to_lowest_column(M, K):
+    """Exact ties in every row; M = 8 fills both four-row groups of the MFMA
+    output and K = 2048 adds K-split choices (argmax in the split reduction)."""
+    N = 700
     case = workload.nvfp4_case(M, K, N, seed=21)
     ref = ref_nvfp4(case)
     best = oracle.argmax_rows(ref)[0]
     codes, scales = case["codes"].copy(), case["scales"].copy()
     # Copy each row's winning column into a lower and a higher column: exact ties.
     for m, b in enumerate(best):
-        for dst in (max(int(b) - 37, 0) if m % 2 else 3, N - 1 - m):
+        for dst in (max(int(b) - 37, 0) if m % 2 else 3 + m, N - 1 - m):
             codes[dst], scales[dst] = codes[b], scales[b]
     case2 = dict(case, codes=codes, scales=scales, blob=sk.nvfp4_pack(codes, scales, case["g"], K, N))
     ref2 = ref_nvfp4(case2)
