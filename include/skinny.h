@@ -371,8 +371,9 @@ size_t skinny_workspace_bytes(int op, int M, int K, int N);
  * skinny_read_probe -- measurement helper, not part of the GEMM path.
  *
  * Reads floor(bytes / 9216) blocks of 9216 bytes of the device buffer `buf`,
- * each by one wavefront with nine 16-byte loads per lane (the access shape of
- * one NVFP4 unit), and writes nothing else but possibly one word to `sink`
+ * each by one wavefront with nine 16-byte non-temporal loads per lane (the
+ * access shape and cache policy of one NVFP4 unit's loads in the GEMM
+ * kernels), and writes nothing else but possibly one word to `sink`
  * (device, 4 bytes).  Timing it gives the HBM read ceiling that the GEMM
  * kernels are rated against (the post, section "What I actually built",
  * rates its kernels against a measured read-only ceiling).  Asynchronous on

@@ -150,6 +150,20 @@ def test_fp8_gemm_argument_errors():
     assert f(w=MIS) == sk.EALIGN and f(s=A + 2) == sk.EALIGN
 
 
+def test_read_probe_argument_errors():
+    """The read probe checks its arguments on the host: no buffer or sink,
+    misalignment and buffers smaller than one 9216-byte block are refused
+    before anything reaches the GPU (the pointers here are never touched)."""
+    L = lib()
+    P = 0x10000
+    assert L.skinny_read_probe(None, 9216, P, None) == sk.EINVAL
+    assert L.skinny_read_probe(P, 9216, None, None) == sk.EINVAL
+    assert L.skinny_read_probe(P + 8, 9216, P, None) == sk.EALIGN
+    assert L.skinny_read_probe(P, 9216, P + 2, None) == sk.EALIGN
+    assert L.skinny_read_probe(P, 9215, P, None) == sk.ESIZE
+    assert L.skinny_read_probe(P, 0, P, None) == sk.ESIZE
+
+
 def test_lm_head_argument_errors():
     L = lib()
     need = sk.workspace_bytes(sk.OP_LM_HEAD, 1, 256, 512)

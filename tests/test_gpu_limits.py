@@ -152,3 +152,16 @@ def test_zero_activations_give_zero_outputs():
     sk.fp8_gemm(dev(c8), dev(s8), z[:4].contiguous(), y, workspace=_ws(sk.OP_FP8, 4, K, N))
     torch.cuda.synchronize()
     assert (y == 0).all()
+
+
+def test_read_probe_reads_without_writing():
+    """The read probe over a zeroed buffer (a whole number of 9216-byte blocks
+    plus a ragged tail it must not read) leaves its sink word untouched: it
+    folds what it loads and writes only on a 2^-64 chance that zeros never hit."""
+    from fp8_quantized_skinny_amd._lib import lib
+    buf = torch.zeros(9216 * 37 + 100, dtype=torch.uint8, device="cuda")
+    sink = torch.full((1,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    for nbytes in (9216, 9216 * 37, 9216 * 37 + 100):
+        assert lib().skinny_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0x5A5A5A5A
