@@ -348,6 +348,38 @@ def test_lm_head_verify_greedy_rounds():
     assert list(res) == [0, int(want_idx[0])]
 
 
+def test_calls_on_two_streams_do_not_interfere():
+    """The library keeps no state between calls: a K-split NVFP4 GEMM (GEMM
+    kernel plus split reduction) and an lm_head argmax (streaming kernel plus
+    key reduction) issued together on two streams, each with its own
+    workspace, four rounds in a row, give bit for bit what each gives alone."""
+    a = workload.nvfp4_case(8, 4096, 3000, seed=41)       # default choice splits K four ways
+    b = workload.nvfp4_case(8, 1024, 20000, seed=42)      # streaming engine, argmax epilogue
+    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 4096, 3000) > 0
+    wa, xa, wb, xb = dev(a["blob"]), dev(a["x"]), dev(b["blob"]), dev(b["x"])
+    wsa = ws_for(sk.OP_NVFP4, 8, 4096, 3000, None)
+    wsb = ws_for(sk.OP_LM_HEAD, 8, 1024, 20000, None)
+    ya_ref = torch.empty((8, 3000), dtype=torch.float16, device="cuda")
+    ib_ref = torch.empty((8,), dtype=torch.int32, device="cuda")
+    sk.nvfp4_gemm(wa, xa, ya_ref, workspace=wsa)
+    sk.lm_head_gemm_argmax(wb, xb, ib_ref, 20000, workspace=wsb)
+    torch.cuda.synchronize()
+    assert np.array_equal(ib_ref.cpu().numpy(), oracle.argmax_rows(ref_nvfp4(b))[0])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for s in (s1, s2):
+        s.wait_stream(torch.cuda.current_stream())
+    ya = [torch.full((8, 3000), float("nan"), dtype=torch.float16, device="cuda") for _ in range(4)]
+    ib = [torch.full((8,), -7, dtype=torch.int32, device="cuda") for _ in range(4)]
+    torch.cuda.synchronize()
+    for r in range(4):
+        sk.nvfp4_gemm(wa, xa, ya[r], workspace=wsa, stream=s1)
+        sk.lm_head_gemm_argmax(wb, xb, ib[r], 20000, workspace=wsb, stream=s2)
+    torch.cuda.synchronize()
+    for r in range(4):
+        assert torch.equal(ya[r], ya_ref), f"round {r}: GEMM on a second stream differs"
+        assert torch.equal(ib[r], ib_ref), f"round {r}: argmax on a second stream differs"
+
+
 # ------------------------------------------------------ mixed-allocation table
 def test_layer_table_mixed_allocation():
     """A stack of FP4, FP8 and SwiGLU-pair layers run through one table call:
