@@ -191,6 +191,124 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+// ---------------------------------------------------------------------------
+// VALU engine, M = 1.
+// ---------------------------------------------------------------------------
+// Half a chunk of one lane (16 E4M3 codes in four dwords, 16 consecutive K)
+// against x pairs broadcast from lanes 0..7 (lo) or 8..15 (hi) of the lane's
+// 16-lane row, accumulated into p.  As in the NVFP4 GEMV, one asm block widens
+// the codes (v_cvt_scalef32_pk_f16_fp8, exact, two per instruction, low half
+// of each dword first) and runs eight v_dot2c_f32_f16 whose x operand is read
+// through DPP row_newbcast, with its own wait states: two before the first DPP
+// read and two after the last v_dot2c.
+#define SKINNY_FP8_HALF_DOT(NAME, R0, R1, R2, R3, R4, R5, R6, R7)                                \
+  __device__ __forceinline__ float NAME(float p, uint32_t xv, const u32x4& w) {                 \
+    uint32_t t0, t1, t2, t3, t4, t5, t6, t7;                                                    \
+    asm("v_cvt_scalef32_pk_f16_fp8 %1, %9, 1.0\n"                                               \
+        "v_cvt_scalef32_pk_f16_fp8 %2, %9, 1.0 op_sel:[1,0,0]\n"                                \
+        "v_cvt_scalef32_pk_f16_fp8 %3, %10, 1.0\n"                                              \
+        "v_cvt_scalef32_pk_f16_fp8 %4, %10, 1.0 op_sel:[1,0,0]\n"                               \
+        "v_cvt_scalef32_pk_f16_fp8 %5, %11, 1.0\n"                                              \
+        "v_cvt_scalef32_pk_f16_fp8 %6, %11, 1.0 op_sel:[1,0,0]\n"                               \
+        "v_cvt_scalef32_pk_f16_fp8 %7, %12, 1.0\n"                                              \
+        "v_cvt_scalef32_pk_f16_fp8 %8, %12, 1.0 op_sel:[1,0,0]\n"                               \
+        "s_nop 1\n"                                                                             \
+        "v_dot2c_f32_f16_dpp %0, %13, %1 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %13, %2 row_newbcast:" #R1 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %13, %3 row_newbcast:" #R2 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %13, %4 row_newbcast:" #R3 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %13, %5 row_newbcast:" #R4 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %13, %6 row_newbcast:" #R5 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %13, %7 row_newbcast:" #R6 " row_mask:0xf bank_mask:0xf\n"     \
+        "v_dot2c_f32_f16_dpp %0, %13, %8 row_newbcast:" #R7 " row_mask:0xf bank_mask:0xf\n"     \
+        "s_nop 1\n"                                                                             \
+        : "+v"(p), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), \
+          "=&v"(t7)                                                                             \
+        : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(xv));                                     \
+    return p;                                                                                   \
+  }
+SKINNY_FP8_HALF_DOT(fp8_half_dot_lo, 0, 1, 2, 3, 4, 5, 6, 7)
+SKINNY_FP8_HALF_DOT(fp8_half_dot_hi, 8, 9, 10, 11, 12, 13, 14, 15)
+#undef SKINNY_FP8_HALF_DOT
+
+// One unit per wavefront, as in the MFMA engine; lane 16r + q holds, for each
+// chunk j, the x pair the lanes of row r need at step q % 8 of half q / 8:
+// x[512u + 128j + 64(q/8) + 16r + 2(q%8) ..+2].  Each chunk's sum over its
+// 128 K is multiplied by its block scale in fp32.  x needs no LDS copy.
+template <int CT, bool PACKED>
+__global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu_m1(Fp8Args a) {
+  __shared__ float red[kMaxWaves][16];
+  const Fp8Plan P(a, CT);
+  const int q = P.lane & 15, r = P.lane >> 4;
+  const int tt = min(P.tile0 + P.t, a.nt - 1);
+  const int u = min(P.s0 + P.s, a.ku - 1);  // an idle wavefront loads a real unit it never uses
+  // Block scales first (wave-uniform); a K block past K gets scale 0 (its
+  // x pairs are zero or its codes are, below).
+  float sc[kFp8UnitChunks];
+  {
+    const float* srow = a.scales + static_cast<size_t>(min(tt * kTileCols, a.N - 1) / 128) * a.kb;
+#pragma unroll
+    for (int j = 0; j < kFp8UnitChunks; ++j) {
+      const int kb = u * kFp8UnitChunks + j;
+      sc[j] = kb < a.kb ? srow[kb] : 0.0f;
+    }
+  }
+  u32x4 w[kFp8UnitChunks][2];
+  uint32_t xv[kFp8UnitChunks];
+  const int kx = u * kFp8UnitK + 64 * (q >> 3) + 16 * r + 2 * (q & 7);
+  if (PACKED) {
+    const uint8_t* up = a.w + (static_cast<size_t>(u) * a.nt + tt) * kFp8UnitBytes + P.lane * 16;
+#pragma unroll
+    for (int j = 0; j < kFp8UnitChunks; ++j) {
+      w[j][0] = load16(up + (2 * j) * 1024);
+      w[j][1] = load16(up + (2 * j + 1) * 1024);
+      xv[j] = *reinterpret_cast<const uint32_t*>(a.x + min(kx + j * kChunkK, a.K - 2));
+    }
+  } else {
+    const int cl = P.lane & 15, grp = P.lane >> 4;
+    const uint8_t* row = a.w + static_cast<size_t>(min(tt * kTileCols + cl, a.N - 1)) * a.K;
+    const int k0 = u * kFp8UnitK + grp * 16;
+#pragma unroll
+    for (int j = 0; j < kFp8UnitChunks; ++j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = k0 + j * kChunkK + 64 * h;
+        w[j][h] = load16_shared_line(row + (k + 16 <= a.K ? k : 0));
+      }
+      xv[j] = *reinterpret_cast<const uint32_t*>(a.x + min(kx + j * kChunkK, a.K - 2));
+    }
+  }
+  float acc = 0.0f;
+  if (P.active) {
+#pragma unroll
+    for (int j = 0; j < kFp8UnitChunks; ++j) {
+      // Canonical codes past K are real codes of the row start: their x pair
+      // must be zero (packed codes past K are zero, so the clamped pair adds
+      // nothing).  Selected here, where this x word is needed anyway.
+      const uint32_t x = PACKED || kx + j * kChunkK < a.K ? xv[j] : 0u;
+      const float p = fp8_half_dot_hi(fp8_half_dot_lo(0.0f, x, w[j][0]), x, w[j][1]);
+      acc = __builtin_fmaf(p, sc[j], acc);
+    }
+  }
+  acc = sum_over_rows(acc);
+  if (P.lane < 16) red[P.wave][P.lane] = acc;
+  __syncthreads();
+
+  // Wavefront t < CT finishes local tile t: its K units in order, then the
+  // output or, with a K split, this split's partial sum.
+  if (P.wave < CT && P.lane < 16 && P.tile0 + P.wave < a.nt) {
+    float tot = 0.0f;
+    for (int s = 0; s < P.sw; ++s) tot += red[P.wave * P.S + s][P.lane];
+    const int n = (P.tile0 + P.wave) * kTileCols + P.lane;
+    if (n < a.N) {
+      if (a.ksplit > 1)
+        a.part[static_cast<size_t>(blockIdx.y) * a.N + n] = tot;
+      else
+        a.y[n] = static_cast<_Float16>(tot);
+    }
+  }
+}
+
 size_t fp8_lds_bytes(int M, int S, int nw) {
   return ((static_cast<size_t>(M) * (S * kFp8UnitK + 8) * 2 + 15) & ~static_cast<size_t>(15)) +
          static_cast<size_t>(nw) * 32 * sizeof(f32x4);
@@ -198,17 +316,25 @@ size_t fp8_lds_bytes(int M, int S, int nw) {
 
 }  // namespace
 
+// (engine, ct, nw, ksplit): engine 1 = MFMA (M <= 8), engine 0 = VALU (M = 1).
 bool fp8_cfg_supported(const LaunchCfg& c, int M, int K) {
-  if (c.engine != 1 || !(c.ct == 1 || c.ct == 2 || c.ct == 4 || c.ct == 8)) return false;
+  if (!(c.engine == 1 || (c.engine == 0 && M == 1))) return false;
+  if (!(c.ct == 1 || c.ct == 2 || c.ct == 4 || c.ct == 8)) return false;
   if (c.nw < 1 || c.nw > kMaxWaves || c.nw % c.ct != 0 || c.ksplit < 1) return false;
   const int ku = (K + kFp8UnitK - 1) / kFp8UnitK;
   const int S = c.nw / c.ct;
   if (static_cast<long>(c.ksplit) * S < ku || static_cast<long>(c.ksplit - 1) * S >= ku) return false;
-  return fp8_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
+  return c.engine == 0 || fp8_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
 }
 
 #define SKINNY_FP8_DISPATCH(CT)                                                           \
-  if (cfg.ct == CT) {                                                                     \
+  if (cfg.ct == CT && cfg.engine == 0) {                                                  \
+    if (packed)                                                                           \
+      hipLaunchKernelGGL((fp8_valu_m1<CT, true>), grid, dim3(cfg.nw * 64), 0, stream, a); \
+    else                                                                                  \
+      hipLaunchKernelGGL((fp8_valu_m1<CT, false>), grid, dim3(cfg.nw * 64), 0, stream, a); \
+    e = hipGetLastError();                                                                \
+  } else if (cfg.ct == CT) {                                                              \
     if (packed)                                                                           \
       hipLaunchKernelGGL((fp8_mfma<CT, true>), grid, dim3(cfg.nw * 64), lds, stream, a);  \
     else                                                                                  \
