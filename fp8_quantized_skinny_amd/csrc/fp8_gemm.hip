@@ -195,49 +195,237 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
 // VALU engine, M = 1.
 // ---------------------------------------------------------------------------
 // Half a chunk of one lane (16 E4M3 codes in four dwords, 16 consecutive K)
-// against x pairs broadcast from lanes 0..7 (lo) or 8..15 (hi) of the lane's
-// 16-lane row, accumulated into p.  As in the NVFP4 GEMV, one asm block widens
-// the codes (v_cvt_scalef32_pk_f16_fp8, exact, two per instruction, low half
-// of each dword first) and runs eight v_dot2c_f32_f16 whose x operand is read
-// through DPP row_newbcast, with its own wait states: two before the first DPP
-// read and two after the last v_dot2c.
-#define SKINNY_FP8_HALF_DOT(NAME, R0, R1, R2, R3, R4, R5, R6, R7)                                \
-  __device__ __forceinline__ float NAME(float p, uint32_t xv, const u32x4& w) {                 \
-    uint32_t t0, t1, t2, t3, t4, t5, t6, t7;                                                    \
-    asm("v_cvt_scalef32_pk_f16_fp8 %1, %9, 1.0\n"                                               \
-        "v_cvt_scalef32_pk_f16_fp8 %2, %9, 1.0 op_sel:[1,0,0]\n"                                \
-        "v_cvt_scalef32_pk_f16_fp8 %3, %10, 1.0\n"                                              \
-        "v_cvt_scalef32_pk_f16_fp8 %4, %10, 1.0 op_sel:[1,0,0]\n"                               \
-        "v_cvt_scalef32_pk_f16_fp8 %5, %11, 1.0\n"                                              \
-        "v_cvt_scalef32_pk_f16_fp8 %6, %11, 1.0 op_sel:[1,0,0]\n"                               \
-        "v_cvt_scalef32_pk_f16_fp8 %7, %12, 1.0\n"                                              \
-        "v_cvt_scalef32_pk_f16_fp8 %8, %12, 1.0 op_sel:[1,0,0]\n"                               \
-        "s_nop 1\n"                                                                             \
-        "v_dot2c_f32_f16_dpp %0, %13, %1 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf\n"     \
-        "v_dot2c_f32_f16_dpp %0, %13, %2 row_newbcast:" #R1 " row_mask:0xf bank_mask:0xf\n"     \
-        "v_dot2c_f32_f16_dpp %0, %13, %3 row_newbcast:" #R2 " row_mask:0xf bank_mask:0xf\n"     \
-        "v_dot2c_f32_f16_dpp %0, %13, %4 row_newbcast:" #R3 " row_mask:0xf bank_mask:0xf\n"     \
-        "v_dot2c_f32_f16_dpp %0, %13, %5 row_newbcast:" #R4 " row_mask:0xf bank_mask:0xf\n"     \
-        "v_dot2c_f32_f16_dpp %0, %13, %6 row_newbcast:" #R5 " row_mask:0xf bank_mask:0xf\n"     \
-        "v_dot2c_f32_f16_dpp %0, %13, %7 row_newbcast:" #R6 " row_mask:0xf bank_mask:0xf\n"     \
-        "v_dot2c_f32_f16_dpp %0, %13, %8 row_newbcast:" #R7 " row_mask:0xf bank_mask:0xf\n"     \
-        "s_nop 1\n"                                                                             \
-        : "+v"(p), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), \
-          "=&v"(t7)                                                                             \
-        : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(xv));                                     \
-    return p;                                                                                   \
+// against the x pairs of MR rows, each broadcast from lanes 0..7 (lo) or
+// 8..15 (hi) of the lane's 16-lane row, accumulated into p[m].  As in the
+// NVFP4 GEMV, one asm block widens the codes once (v_cvt_scalef32_pk_f16_fp8,
+// exact, two per instruction, low half of each dword first) and runs MR x 8
+// v_dot2c_f32_f16 whose x operand is read through DPP row_newbcast, with its
+// own wait states: two before the first DPP read and two after the last
+// v_dot2c.  Keeping the widening inside the block stops the compiler from
+// widening a whole unit ahead of use.
+__device__ __forceinline__ void fp8_half_dot1_lo(float (&p)[1], const uint32_t (&xv)[1], const u32x4& w) {
+  uint32_t t0, t1, t2, t3, t4, t5, t6, t7;
+  asm("v_cvt_scalef32_pk_f16_fp8 %1, %9, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %2, %9, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %3, %10, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %4, %10, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %5, %11, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %6, %11, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %7, %12, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %8, %12, 1.0 op_sel:[1,0,0]\n"
+      "s_nop 1\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %1 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %2 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %3 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %4 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %5 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %6 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %7 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %8 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      : "+v"(p[0]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+      : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(xv[0]));
+}
+__device__ __forceinline__ void fp8_half_dot1_hi(float (&p)[1], const uint32_t (&xv)[1], const u32x4& w) {
+  uint32_t t0, t1, t2, t3, t4, t5, t6, t7;
+  asm("v_cvt_scalef32_pk_f16_fp8 %1, %9, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %2, %9, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %3, %10, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %4, %10, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %5, %11, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %6, %11, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %7, %12, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %8, %12, 1.0 op_sel:[1,0,0]\n"
+      "s_nop 1\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %1 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %2 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %3 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %4 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %5 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %6 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %7 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %13, %8 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      : "+v"(p[0]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+      : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(xv[0]));
+}
+__device__ __forceinline__ void fp8_half_dot2_lo(float (&p)[2], const uint32_t (&xv)[2], const u32x4& w) {
+  uint32_t t0, t1, t2, t3, t4, t5, t6, t7;
+  asm("v_cvt_scalef32_pk_f16_fp8 %2, %10, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %3, %10, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %4, %11, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %5, %11, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %6, %12, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %7, %12, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %8, %13, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %9, %13, 1.0 op_sel:[1,0,0]\n"
+      "s_nop 1\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      : "+v"(p[0]), "+v"(p[1]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+      : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(xv[0]), "v"(xv[1]));
+}
+__device__ __forceinline__ void fp8_half_dot2_hi(float (&p)[2], const uint32_t (&xv)[2], const u32x4& w) {
+  uint32_t t0, t1, t2, t3, t4, t5, t6, t7;
+  asm("v_cvt_scalef32_pk_f16_fp8 %2, %10, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %3, %10, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %4, %11, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %5, %11, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %6, %12, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %7, %12, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %8, %13, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %9, %13, 1.0 op_sel:[1,0,0]\n"
+      "s_nop 1\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %2 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %3 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %4 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %5 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %7 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %8 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %14, %9 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %2 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %3 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %4 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %5 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %7 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %8 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %15, %9 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      : "+v"(p[0]), "+v"(p[1]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+      : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(xv[0]), "v"(xv[1]));
+}
+__device__ __forceinline__ void fp8_half_dot4_lo(float (&p)[4], const uint32_t (&xv)[4], const u32x4& w) {
+  uint32_t t0, t1, t2, t3, t4, t5, t6, t7;
+  asm("v_cvt_scalef32_pk_f16_fp8 %4, %12, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %5, %12, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %6, %13, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %7, %13, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %8, %14, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %9, %14, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %10, %15, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %11, %15, 1.0 op_sel:[1,0,0]\n"
+      "s_nop 1\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+      : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(xv[0]), "v"(xv[1]), "v"(xv[2]), "v"(xv[3]));
+}
+__device__ __forceinline__ void fp8_half_dot4_hi(float (&p)[4], const uint32_t (&xv)[4], const u32x4& w) {
+  uint32_t t0, t1, t2, t3, t4, t5, t6, t7;
+  asm("v_cvt_scalef32_pk_f16_fp8 %4, %12, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %5, %12, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %6, %13, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %7, %13, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %8, %14, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %9, %14, 1.0 op_sel:[1,0,0]\n"
+      "v_cvt_scalef32_pk_f16_fp8 %10, %15, 1.0\n"
+      "v_cvt_scalef32_pk_f16_fp8 %11, %15, 1.0 op_sel:[1,0,0]\n"
+      "s_nop 1\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %4 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %5 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %6 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %7 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %8 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %9 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %10 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %0, %16, %11 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %4 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %5 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %6 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %7 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %8 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %9 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %10 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %1, %17, %11 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %4 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %5 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %6 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %7 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %8 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %9 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %10 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %2, %18, %11 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %4 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %5 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %6 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %7 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %8 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %9 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %10 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_dot2c_f32_f16_dpp %3, %19, %11 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+      : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(xv[0]), "v"(xv[1]), "v"(xv[2]), "v"(xv[3]));
+}
+
+template <int MR>
+__device__ __forceinline__ void fp8_half_dot(float (&p)[MR], const uint32_t (&xv)[MR], const u32x4& w, bool hi) {
+  if constexpr (MR == 1) {
+    if (hi) fp8_half_dot1_hi(p, xv, w); else fp8_half_dot1_lo(p, xv, w);
+  } else if constexpr (MR == 2) {
+    if (hi) fp8_half_dot2_hi(p, xv, w); else fp8_half_dot2_lo(p, xv, w);
+  } else {
+    if (hi) fp8_half_dot4_hi(p, xv, w); else fp8_half_dot4_lo(p, xv, w);
   }
-SKINNY_FP8_HALF_DOT(fp8_half_dot_lo, 0, 1, 2, 3, 4, 5, 6, 7)
-SKINNY_FP8_HALF_DOT(fp8_half_dot_hi, 8, 9, 10, 11, 12, 13, 14, 15)
-#undef SKINNY_FP8_HALF_DOT
+}
 
 // One unit per wavefront, as in the MFMA engine; lane 16r + q holds, for each
-// chunk j, the x pair the lanes of row r need at step q % 8 of half q / 8:
-// x[512u + 128j + 64(q/8) + 16r + 2(q%8) ..+2].  Each chunk's sum over its
-// 128 K is multiplied by its block scale in fp32.  x needs no LDS copy.
-template <int CT, bool PACKED>
-__global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu_m1(Fp8Args a) {
-  __shared__ float red[kMaxWaves][16];
+// chunk j and row m, the x pair the lanes of its row r need at step q % 8 of
+// half q / 8: x[m][512u + 128j + 64(q/8) + 16r + 2(q%8) ..+2].  Each chunk's
+// sum over its 128 K is multiplied by its block scale in fp32.  x needs no
+// LDS copy.  MR rows per instance (M = 3 runs as MR = 4: its fourth row
+// reads row 2 again and is never stored).
+template <int CT, bool PACKED, int MR>
+__global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
+  __shared__ float red[kMaxWaves][MR][16];
   const Fp8Plan P(a, CT);
   const int q = P.lane & 15, r = P.lane >> 4;
   const int tt = min(P.tile0 + P.t, a.nt - 1);
@@ -254,15 +442,20 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu_m1(Fp8Args a) {
     }
   }
   u32x4 w[kFp8UnitChunks][2];
-  uint32_t xv[kFp8UnitChunks];
+  uint32_t xv[kFp8UnitChunks][MR];
   const int kx = u * kFp8UnitK + 64 * (q >> 3) + 16 * r + 2 * (q & 7);
+  const _Float16* xr[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) xr[m] = a.x + static_cast<size_t>(min(m, a.M - 1)) * a.K;
   if (PACKED) {
     const uint8_t* up = a.w + (static_cast<size_t>(u) * a.nt + tt) * kFp8UnitBytes + P.lane * 16;
 #pragma unroll
     for (int j = 0; j < kFp8UnitChunks; ++j) {
       w[j][0] = load16(up + (2 * j) * 1024);
       w[j][1] = load16(up + (2 * j + 1) * 1024);
-      xv[j] = *reinterpret_cast<const uint32_t*>(a.x + min(kx + j * kChunkK, a.K - 2));
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        xv[j][m] = *reinterpret_cast<const uint32_t*>(xr[m] + min(kx + j * kChunkK, a.K - 2));
     }
   } else {
     const int cl = P.lane & 15, grp = P.lane >> 4;
@@ -275,36 +468,56 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu_m1(Fp8Args a) {
         const int k = k0 + j * kChunkK + 64 * h;
         w[j][h] = load16_shared_line(row + (k + 16 <= a.K ? k : 0));
       }
-      xv[j] = *reinterpret_cast<const uint32_t*>(a.x + min(kx + j * kChunkK, a.K - 2));
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        xv[j][m] = *reinterpret_cast<const uint32_t*>(xr[m] + min(kx + j * kChunkK, a.K - 2));
     }
   }
-  float acc = 0.0f;
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
   if (P.active) {
 #pragma unroll
     for (int j = 0; j < kFp8UnitChunks; ++j) {
-      // Canonical codes past K are real codes of the row start: their x pair
-      // must be zero (packed codes past K are zero, so the clamped pair adds
-      // nothing).  Selected here, where this x word is needed anyway.
-      const uint32_t x = PACKED || kx + j * kChunkK < a.K ? xv[j] : 0u;
-      const float p = fp8_half_dot_hi(fp8_half_dot_lo(0.0f, x, w[j][0]), x, w[j][1]);
-      acc = __builtin_fmaf(p, sc[j], acc);
+      // Canonical codes past K are real codes of the row start: their x pairs
+      // must be zero (packed codes past K are zero, so the clamped pairs add
+      // nothing).  Selected here, where these x words are needed anyway.
+      const bool in = PACKED || kx + j * kChunkK < a.K;
+      uint32_t x[MR];
+      float p[MR];
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        x[m] = in ? xv[j][m] : 0u;
+        p[m] = 0.0f;
+      }
+      fp8_half_dot<MR>(p, x, w[j][0], false);
+      fp8_half_dot<MR>(p, x, w[j][1], true);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) acc[m] = __builtin_fmaf(p[m], sc[j], acc[m]);
     }
   }
-  acc = sum_over_rows(acc);
-  if (P.lane < 16) red[P.wave][P.lane] = acc;
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const float v = sum_over_rows(acc[m]);
+    if (P.lane < 16) red[P.wave][m][P.lane] = v;
+  }
   __syncthreads();
 
   // Wavefront t < CT finishes local tile t: its K units in order, then the
-  // output or, with a K split, this split's partial sum.
+  // output rows or, with a K split, this split's partial sums.
   if (P.wave < CT && P.lane < 16 && P.tile0 + P.wave < a.nt) {
-    float tot = 0.0f;
-    for (int s = 0; s < P.sw; ++s) tot += red[P.wave * P.S + s][P.lane];
     const int n = (P.tile0 + P.wave) * kTileCols + P.lane;
     if (n < a.N) {
-      if (a.ksplit > 1)
-        a.part[static_cast<size_t>(blockIdx.y) * a.N + n] = tot;
-      else
-        a.y[n] = static_cast<_Float16>(tot);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        if (m >= a.M) break;
+        float tot = 0.0f;
+        for (int s = 0; s < P.sw; ++s) tot += red[P.wave * P.S + s][m][P.lane];
+        if (a.ksplit > 1)
+          a.part[(static_cast<size_t>(blockIdx.y) * a.M + m) * a.N + n] = tot;
+        else
+          a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(tot);
+      }
     }
   }
 }
@@ -316,9 +529,9 @@ size_t fp8_lds_bytes(int M, int S, int nw) {
 
 }  // namespace
 
-// (engine, ct, nw, ksplit): engine 1 = MFMA (M <= 8), engine 0 = VALU (M = 1).
+// (engine, ct, nw, ksplit): engine 1 = MFMA (M <= 8), engine 0 = VALU (M <= 4).
 bool fp8_cfg_supported(const LaunchCfg& c, int M, int K) {
-  if (!(c.engine == 1 || (c.engine == 0 && M == 1))) return false;
+  if (!(c.engine == 1 || (c.engine == 0 && M <= 4))) return false;
   if (!(c.ct == 1 || c.ct == 2 || c.ct == 4 || c.ct == 8)) return false;
   if (c.nw < 1 || c.nw > kMaxWaves || c.nw % c.ct != 0 || c.ksplit < 1) return false;
   const int ku = (K + kFp8UnitK - 1) / kFp8UnitK;
@@ -327,13 +540,29 @@ bool fp8_cfg_supported(const LaunchCfg& c, int M, int K) {
   return c.engine == 0 || fp8_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
 }
 
+// The VALU engine's instance for M rows (M = 3 runs as four rows).
+template <int CT, bool PACKED>
+void launch_fp8_valu_rows(const Fp8Args& a, dim3 grid, dim3 blk, hipStream_t stream) {
+  if (a.M == 1)
+    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 1>), grid, blk, 0, stream, a);
+  else if (a.M == 2)
+    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 2>), grid, blk, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 4>), grid, blk, 0, stream, a);
+}
+
+template <int CT>
+hipError_t launch_fp8_valu(const Fp8Args& a, dim3 grid, int nw, bool packed, hipStream_t stream) {
+  if (packed)
+    launch_fp8_valu_rows<CT, true>(a, grid, dim3(nw * 64), stream);
+  else
+    launch_fp8_valu_rows<CT, false>(a, grid, dim3(nw * 64), stream);
+  return hipGetLastError();
+}
+
 #define SKINNY_FP8_DISPATCH(CT)                                                           \
   if (cfg.ct == CT && cfg.engine == 0) {                                                  \
-    if (packed)                                                                           \
-      hipLaunchKernelGGL((fp8_valu_m1<CT, true>), grid, dim3(cfg.nw * 64), 0, stream, a); \
-    else                                                                                  \
-      hipLaunchKernelGGL((fp8_valu_m1<CT, false>), grid, dim3(cfg.nw * 64), 0, stream, a); \
-    e = hipGetLastError();                                                                \
+    e = launch_fp8_valu<CT>(a, grid, cfg.nw, packed, stream);                             \
   } else if (cfg.ct == CT) {                                                              \
     if (packed)                                                                           \
       hipLaunchKernelGGL((fp8_mfma<CT, true>), grid, dim3(cfg.nw * 64), lds, stream, a);  \

@@ -100,10 +100,11 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 //
 // NVFP4 GEMV (M = 1, no argmax): VALU engine, whole K per workgroup (K beyond
 // 16 spans split over workgroups, evened out), two tiles per workgroup when
-// there are few tiles (N <= 6144), else one.  FP8 at M = 1: its VALU engine,
+// there are few tiles (N <= 6144), else one.  FP8 at M <= 2: its VALU engine,
 // whole K per workgroup, two tiles only when 2 * K spans <= 16 and N <= 6144
 // (on qkv and o_proj one tile of 10 or 12 units was within 0.03 us of the
-// fastest choice, and 0.3 to 0.6 us ahead of the MFMA engine).
+// fastest choice at M = 1, 0.3 to 0.6 us ahead of the MFMA engine, and about
+// 0.1 to 0.2 us ahead at M = 2; at M = 4 the MFMA engine is faster).
 //
 // Other NVFP4 calls: the streaming engine when there are enough column tiles
 // to keep the CUs busy with whole tiles (N >= 8192) and all of x fits in LDS
@@ -171,9 +172,9 @@ LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax) {
 LaunchCfg default_fp8_cfg(int M, int K, int N) {
   const int ku = (K + 511) / 512, nt = (N + 15) / 16;
   auto fits = [&](const LaunchCfg& c) { return fp8_cfg_supported(c, M, K); };
-  // M = 1: the VALU engine, whole K per workgroup (two tiles per workgroup
+  // M <= 2: the VALU engine, whole K per workgroup (two tiles per workgroup
   // only when both fit whole: 2 * ku <= 16 and few tiles).
-  if (M == 1) return pick_whole_k_cfg(0, 2 * ku <= kMaxWaves && nt <= 384 ? 2 : 1, ku, fits);
+  if (M <= 2) return pick_whole_k_cfg(0, 2 * ku <= kMaxWaves && nt <= 384 ? 2 : 1, ku, fits);
   return pick_oneshot_cfg(M, K, ku, nt, fits);
 }
 

@@ -82,10 +82,11 @@ def test_explicit_config_rejections():
     assert cfg(1, 1, 1, 0, 1) == sk.EINVAL
     assert cfg(1, 1, 1, 4, 0) == sk.EINVAL
     assert cfg(1, 1, 1, 4, 2) == sk.EINVAL          # K = 256 has one K span: no split possible
-    # FP8 VALU engine: M = 1 only
-    assert L.fp8_gemm_config(A, A, A, A, 2, 256, 512, None, 0, None, 0, 1, 4, 1) == sk.EINVAL
+    # FP8 VALU engine: M <= 4
+    assert L.fp8_gemm_config(A, A, A, A, 5, 256, 512, None, 0, None, 0, 1, 4, 1) == sk.EINVAL
     assert sk.config_supported(sk.OP_FP8, 1, 5120, 7168, (0, 1, 10, 1))
-    assert not sk.config_supported(sk.OP_FP8, 2, 5120, 7168, (0, 1, 10, 1))
+    assert sk.config_supported(sk.OP_FP8, 4, 5120, 7168, (0, 1, 10, 1))
+    assert not sk.config_supported(sk.OP_FP8, 5, 5120, 7168, (0, 1, 10, 1))
     assert L.lm_head_gemm_argmax_config(A, A, A, None, 1, 256, 512, A, 256, None, 0, 1, 4, 1) == sk.EINVAL
     # a K split needs its workspace
     big = lambda ws, wsb: L.nvfp4_gemm_config(A, A, A, 8, 17408, 5120, ws, wsb, None, 1, 1, 4, 5)
@@ -395,7 +396,7 @@ def test_fp8_pack_errors_and_packed_gemm_arguments():
     assert g(w=None) == sk.EINVAL and g(s=None) == sk.EINVAL
     assert g(M=9) == sk.ESHAPE and g(K=24) == sk.ESHAPE
     assert g(w=MIS) == sk.EALIGN and g(y=MIS) == sk.EALIGN and g(s=A + 2) == sk.EALIGN
-    assert L.fp8_gemm_packed_config(A, A, A, A, 2, 256, 256, None, 0, None, 0, 1, 1, 1) == sk.EINVAL  # VALU: M = 1 only
+    assert L.fp8_gemm_packed_config(A, A, A, A, 5, 256, 256, None, 0, None, 0, 1, 1, 1) == sk.EINVAL  # VALU: M <= 4
 
 
 def test_pack_is_deterministic():

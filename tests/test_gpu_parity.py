@@ -149,12 +149,17 @@ def test_fp8_one_hot_reproduces_codes_exactly():
                 case["x"] = eye[r0:r0 + 8]
                 out[r0:r0 + 8] = run_fp8(case, M=8, config=cfg, packed=packed)
             assert np.array_equal(out, deq), f"config {cfg} packed={packed}"
-        # the VALU engine (M = 1): one row at a time, a sample of rows in every chunk and unit
+        # the VALU engine (M <= 4): one and three rows at a time (three rows run
+        # as four, the fourth a copy never stored), a sample of rows in every chunk
         for cfg in cfgs(0, K, unit_k=512):
             for r0 in list(range(0, K, 7)) + [K - 1]:
                 case["x"] = eye[r0:r0 + 1]
                 got = run_fp8(case, M=1, config=cfg, packed=packed)
                 assert np.array_equal(got[0], deq[r0]), f"VALU config {cfg} packed={packed} row {r0}"
+            for r0 in list(range(0, K - 2, 11)) + [K - 3]:
+                case["x"] = eye[r0:r0 + 3]
+                got = run_fp8(case, M=3, config=cfg, packed=packed)
+                assert np.array_equal(got, deq[r0:r0 + 3]), f"VALU config {cfg} packed={packed} rows {r0}..+3"
 
 
 # -------------------------------------------------------- tolerance parity
@@ -237,7 +242,7 @@ def test_fp8_parity_all_configs(shape):
     pieces in the same registers, only the byte order in memory differs)."""
     case = workload.fp8_case(*shape, seed=sum(shape))
     ref = ref_fp8(case)
-    valu = cfgs(0, case["K"], unit_k=512) if case["M"] == 1 else []
+    valu = cfgs(0, case["K"], unit_k=512) if case["M"] <= 4 else []
     for cfg in cfgs(1, case["K"], unit_k=512) + valu + [None]:
         y = run_fp8(case, config=cfg)
         _check(y, ref, f"{shape} {cfg}")
