@@ -7,16 +7,22 @@
 // "v1.0 -> v1.1"); the codes are read in their canonical [N][K] order.
 //
 // A 16-column tile times one 128-K chunk lies inside one 128 x 128 scale
-// block, so each chunk is contracted on the matrix cores into a fresh fp32
-// partial (E4M3 -> fp16 is exact) that is then added to the accumulator times
-// the block scale in fp32.
+// block, so each chunk is contracted into a fresh fp32 partial (E4M3 -> fp16
+// is exact) that is then added to the accumulator times the block scale in
+// fp32.  Two engines contract a chunk:
+//   * MFMA (M = 1..8): v_mfma_f32_16x16x32_f16 with x rows, padded to 16,
+//     from an LDS copy as operand A (the default from M = 3);
+//   * VALU (M <= 4): v_dot2c_f32_f16 with each row's x pairs read from
+//     global memory and broadcast across 16 lanes by DPP row_newbcast, as in
+//     the NVFP4 GEMV; no LDS copy of x (the default at M <= 2).
 //
 // Work split follows the NVFP4 kernels: a unit is one 16-column tile x 512 K
 // (four chunks, 8 KiB of codes); every wavefront loads one unit at once and
 // contracts it; a workgroup is CT tiles x S units along K (nw = CT * S), with
 // a K split over workgroups when K has more units (partial sums stored with
-// plain stores and added in split order by the reduction kernel).  x is copied into LDS once
-// per workgroup with direct-to-LDS loads.  Lane (grp, c) reads, per chunk, the
+// plain stores and added in split order by the reduction kernel).  The MFMA
+// engine copies x into LDS once per workgroup with direct-to-LDS loads.
+// Lane (grp, c) reads, per chunk, the
 // two 16-byte pieces K = 128j + 64h + 16grp .. +16 (h = 0, 1) of column c, so
 // each load instruction covers 64 contiguous bytes of 16 columns.  Pieces past
 // K or columns past N read a clamped valid address and are zeroed.

@@ -2,8 +2,9 @@
 //
 // y[m][n] = g * sum_k x[m][k] * e2m1(q[n][k]) * e4m3(s[n][k/16]),  1 <= M <= 8.
 //
-// The weights are read once, compressed, straight from HBM into VGPRs and
-// widened to fp16 in registers just before use; there is no dequantized copy
+// The weights are read once, compressed, straight from HBM into VGPRs (with
+// the streaming cache policy: no weight byte is read twice) and widened to
+// fp16 in registers just before use; there is no dequantized copy
 // anywhere ("NVFP4 on Volta!" author's post, section "What I actually
 // built").  Decode at batch 1..8 is bound by that weight stream, so the
 // design is about keeping as many 128-bit loads in flight as the chip holds.
