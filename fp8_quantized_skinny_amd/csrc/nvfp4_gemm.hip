@@ -151,7 +151,7 @@ SKINNY_BLOCK_DOT(block_dot_lo, 0, 1, 2, 3, 4, 5, 6, 7)
 SKINNY_BLOCK_DOT(block_dot_hi, 8, 9, 10, 11, 12, 13, 14, 15)
 #undef SKINNY_BLOCK_DOT
 
-template <int CT, bool SWIGLU>
+template <int CT, int EPI>
 __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu_m1(Nvfp4Args a) {
   __shared__ float red[kMaxWaves][16];
   const Plan P(a, CT);
@@ -190,19 +190,34 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu_m1(Nvfp4Args a) {
   // Wavefront t < CT finishes local tile t: its spans in order, then the
   // output or, with a K split, this split's partial sum.
   const bool fin = P.wave < CT && P.lane < 16 && P.tile0 + P.wave < a.nt;
+  const int n = (P.tile0 + P.wave) * kTileCols + P.lane;
+  float tot = 0.0f;
   if (fin) {
-    float tot = 0.0f;
     for (int s = 0; s < P.sw; ++s) tot += red[P.wave * P.S + s][P.lane];
-    const int n = (P.tile0 + P.wave) * kTileCols + P.lane;
-    if (SWIGLU && a.ksplit == 1) {  // lanes 0..15 of the wavefront are all here
+    if (EPI == kEpiSwiglu && a.ksplit == 1) {  // lanes 0..15 of the wavefront are all here
       const float h = swiglu_pair(tot, *a.gptr, *a.g2ptr);
       const int f = (P.tile0 + P.wave) * 8 + P.lane;
       if (P.lane < 8 && f < a.F) a.y[f] = static_cast<_Float16>(h);
     } else if (n < a.N) {
       if (a.ksplit > 1)
         a.part[static_cast<size_t>(blockIdx.y) * a.N + n] = tot;
-      else
+      else if (EPI != kEpiArgmax || a.y)  // the lm_head's logits are optional
         a.y[n] = static_cast<_Float16>(*a.gptr * tot);
+    }
+  }
+  if (EPI == kEpiArgmax) {
+    // lm_head (M = 1, no K split): the (fp32 logit, column) key of each of
+    // this workgroup's tiles, then of the workgroup, as its one candidate.
+    // Every lane runs the shuffles; lanes outside a finished tile hold 0.
+    __shared__ unsigned long long best[kMaxWaves];
+    unsigned long long key = fin && n < a.N ? argmax_key(*a.gptr * tot, n) : 0ull;
+    key = wave_max_key<16>(key);
+    if (P.lane == 0) best[P.wave] = key;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long k = 0ull;
+      for (int t = 0; t < CT; ++t) k = best[t] > k ? best[t] : k;
+      a.cand[blockIdx.x] = k;
     }
   }
 }
@@ -580,7 +595,7 @@ bool nvfp4_cfg_supported(const LaunchCfg& c, int M, int K, bool argmax) {
   const int ku = (K + kUnitK - 1) / kUnitK;
   const int S = c.nw / c.ct;
   if (static_cast<long>(c.ksplit) * S < ku || static_cast<long>(c.ksplit - 1) * S >= ku) return false;
-  if (c.engine == 0) return M == 1 && !argmax;
+  if (c.engine == 0) return M == 1;
   if (c.engine != 1) return false;
   return nvfp4_mfma_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
 }
@@ -588,8 +603,9 @@ bool nvfp4_cfg_supported(const LaunchCfg& c, int M, int K, bool argmax) {
 #define SKINNY_NVFP4_DISPATCH(CT)                                                                       \
   if (cfg.ct == CT) {                                                                                   \
     if (cfg.engine == 0)                                                                                \
-      return epi == kEpiSwiglu ? launch(nvfp4_valu_m1<CT, true>, grid, cfg.nw, 0, a, stream)            \
-                               : launch(nvfp4_valu_m1<CT, false>, grid, cfg.nw, 0, a, stream);          \
+      return epi == kEpiSwiglu                      ? launch(nvfp4_valu_m1<CT, kEpiSwiglu>, grid, cfg.nw, 0, a, stream) \
+             : epi == kEpiArgmax && cfg.ksplit == 1 ? launch(nvfp4_valu_m1<CT, kEpiArgmax>, grid, cfg.nw, 0, a, stream) \
+                                                    : launch(nvfp4_valu_m1<CT, kEpiPlain>, grid, cfg.nw, 0, a, stream);  \
     if (epi == kEpiArgmax && cfg.ksplit == 1)                                                           \
       return launch(nvfp4_mfma<CT, kEpiArgmax>, grid, cfg.nw, lds, a, stream);                          \
     if (epi == kEpiSwiglu && cfg.ksplit == 1)                                                           \

@@ -120,6 +120,40 @@ __global__ __launch_bounds__(256) void argmax_reduce(const unsigned long long* c
   }
 }
 
+// One row (M = 1), up to tens of thousands of candidates (one per workgroup
+// of the lm_head GEMV): every thread reads 16 keys per round before
+// comparing any, so 16384 candidates cost one memory round trip.  Reads
+// past the last candidate repeat it (a maximum does not change).  With
+// `result`, a round of M = 1 has no drafts: it commits idx[0].
+constexpr int kRowReduceThreads = 1024;
+constexpr int kRowReduceDepth = 16;
+__global__ __launch_bounds__(kRowReduceThreads) void argmax_reduce_row(const unsigned long long* cand, int groups,
+                                                                    int32_t* idx, int32_t* result) {
+  __shared__ unsigned long long red[kRowReduceThreads / 64];
+  unsigned long long k = 0ull;
+  for (int g0 = threadIdx.x; g0 < groups; g0 += kRowReduceThreads * kRowReduceDepth) {
+    unsigned long long v[kRowReduceDepth];
+#pragma unroll
+    for (int b = 0; b < kRowReduceDepth; ++b) v[b] = cand[min(g0 + b * kRowReduceThreads, groups - 1)];
+#pragma unroll
+    for (int b = 0; b < kRowReduceDepth; ++b) k = v[b] > k ? v[b] : k;
+  }
+  k = wave_max_key(k);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = k;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long best = 0ull;
+    for (int w = 0; w < kRowReduceThreads / 64; ++w) best = red[w] > best ? red[w] : best;
+    // No candidate at all (every logit NaN) leaves the all-ones index -1.
+    const int32_t i = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFull));
+    idx[0] = i;
+    if (result) {
+      result[0] = 0;
+      result[1] = i;
+    }
+  }
+}
+
 // SwiGLU pair of a K split: thread f of block (x, m) adds the split partials
 // of gate column 16 * (f / 8) + f % 8 and of its up column eight further on,
 // each in split order, and writes h[m][f] = silu(g * gate) * (g2 * up).
@@ -165,7 +199,10 @@ hipError_t launch_finalize_swiglu(const float* part, int ksplit, int M, int N, i
 
 hipError_t launch_argmax_reduce(const unsigned long long* cand, int groups, int M, int32_t* idx,
                                 hipStream_t stream, const int32_t* drafts, int32_t* result) {
-  hipLaunchKernelGGL(argmax_reduce, dim3(1), dim3(256), 0, stream, cand, groups, M, idx, drafts, result);
+  if (M == 1)
+    hipLaunchKernelGGL(argmax_reduce_row, dim3(1), dim3(kRowReduceThreads), 0, stream, cand, groups, idx, result);
+  else
+    hipLaunchKernelGGL(argmax_reduce, dim3(1), dim3(256), 0, stream, cand, groups, M, idx, drafts, result);
   return hipGetLastError();
 }
 

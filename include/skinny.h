@@ -299,7 +299,8 @@ int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales);
 /* ---------------------------------------------------------------------------
  * The GEMM calls with an explicit kernel choice instead of the
  * library's pick (same arguments and results, used to compare kernels):
- *   engine : 0 = VALU dot2 engine (nvfp4_gemm with M == 1; fp8_gemm and
+ *   engine : 0 = VALU dot2 engine (nvfp4_gemm, lm_head_gemm_argmax and
+ *                lm_head_verify_greedy with M == 1; fp8_gemm and
  *                fp8_gemm_packed with M <= 4),
  *            1 = MFMA 16x16x32 f16 engine (all calls, M = 1..8),
  *            2 = streaming MFMA engine (nvfp4_gemm and lm_head_gemm_argmax,

@@ -87,7 +87,8 @@ def test_explicit_config_rejections():
     assert sk.config_supported(sk.OP_FP8, 1, 5120, 7168, (0, 1, 10, 1))
     assert sk.config_supported(sk.OP_FP8, 4, 5120, 7168, (0, 1, 10, 1))
     assert not sk.config_supported(sk.OP_FP8, 5, 5120, 7168, (0, 1, 10, 1))
-    assert L.lm_head_gemm_argmax_config(A, A, A, None, 1, 256, 512, A, 256, None, 0, 1, 4, 1) == sk.EINVAL
+    assert L.lm_head_gemm_argmax_config(A, A, A, None, 2, 256, 512, A, 256, None, 0, 1, 4, 1) == sk.EINVAL
+    assert sk.config_supported(sk.OP_LM_HEAD, 1, 5120, 151936, (0, 1, 5, 1))
     # a K split needs its workspace
     big = lambda ws, wsb: L.nvfp4_gemm_config(A, A, A, 8, 17408, 5120, ws, wsb, None, 1, 1, 4, 5)
     need = sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 1, 4, 5))

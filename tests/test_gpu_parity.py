@@ -277,7 +277,8 @@ def test_lm_head_argmax_and_logits(shape):
     case = workload.nvfp4_case(*shape, seed=sum(shape))
     ref = ref_nvfp4(case)
     want, margin = oracle.argmax_rows(ref)
-    for cfg in cfgs(1, K) + stream_cfgs(sk.OP_LM_HEAD, M, K, N):
+    valu = cfgs(0, K) if M == 1 else []
+    for cfg in valu + cfgs(1, K) + stream_cfgs(sk.OP_LM_HEAD, M, K, N):
         idx, lg = run_lm_head(case, M, config=cfg, logits=True)
         assert np.array_equal(idx, want), f"{shape} {cfg}: {idx} vs {want} (margins {margin})"
         _check(lg, ref, f"{shape} {cfg} logits")
@@ -285,10 +286,11 @@ def test_lm_head_argmax_and_logits(shape):
     assert np.array_equal(idx, want)
 
 
-@pytest.mark.parametrize("M,K", [(4, 256), (8, 2048)])
+@pytest.mark.parametrize("M,K", [(4, 256), (8, 2048), (1, 2048)])
 def test_lm_head_ties_go_to_lowest_column(M, K):
     """Exact ties in every row; M = 8 fills both four-row groups of the MFMA
-    output and K = 2048 adds K-split choices (argmax in the split reduction)."""
+    output, K = 2048 adds K-split choices (argmax in the split reduction) and
+    M = 1 adds the VALU engine's candidates and the one-row key reduction."""
     N = 700
     case = workload.nvfp4_case(M, K, N, seed=21)
     ref = ref_nvfp4(case)
@@ -301,9 +303,31 @@ def test_lm_head_ties_go_to_lowest_column(M, K):
     case2 = dict(case, codes=codes, scales=scales, blob=sk.nvfp4_pack(codes, scales, case["g"], K, N))
     ref2 = ref_nvfp4(case2)
     want, _ = oracle.argmax_rows(ref2)
-    for cfg in cfgs(1, K) + stream_cfgs(sk.OP_LM_HEAD, M, K, N):
+    valu = cfgs(0, K) if M == 1 else []
+    for cfg in valu + cfgs(1, K) + stream_cfgs(sk.OP_LM_HEAD, M, K, N):
         idx, _ = run_lm_head(case2, M, config=cfg)
         assert np.array_equal(idx, want), f"{cfg}: {idx} vs {want}"
+
+
+def test_lm_head_one_row_with_more_candidates_than_one_reduction_round():
+    """M = 1 on one 16-column tile per workgroup: 18750 candidates, more than
+    the 16384 that the one-row key reduction reads in one round.  The winning
+    column is moved into the last tile, so it is found only in the second
+    round; the logits are checked too."""
+    M, K, N = 1, 256, 300000
+    case = workload.nvfp4_case(M, K, N, seed=24)
+    b = int(oracle.argmax_rows(ref_nvfp4(case))[0][0])
+    dst = N - 5
+    codes, scales = case["codes"].copy(), case["scales"].copy()
+    codes[[b, dst]], scales[[b, dst]] = codes[[dst, b]], scales[[dst, b]]
+    case2 = dict(case, codes=codes, scales=scales, blob=sk.nvfp4_pack(codes, scales, case["g"], K, N))
+    ref2 = ref_nvfp4(case2)
+    want, margin = oracle.argmax_rows(ref2)
+    assert want[0] == dst
+    for cfg in [(0, 1, 1, 1), (0, 2, 2, 1), None]:
+        idx, lg = run_lm_head(case2, M, config=cfg, logits=True)
+        assert np.array_equal(idx, want), (cfg, idx, want, margin)
+        _check(lg, ref2, f"{cfg} logits")
 
 
 def test_lm_head_zero_weights_and_shared_workspace():
