@@ -27,10 +27,11 @@
 //
 // Two engines (lane l = 16*grp + c handles column c of the tile and the
 // 32-K run 128j + 32grp .. +32 of every chunk j):
-//   * VALU (M = 1): v_dot2c_f32_f16 whose x operand is read through DPP
+//   * VALU (M = 1, 2): v_dot2c_f32_f16 whose x operand is read through DPP
 //     row_newbcast (lane 16r + i holds the x pair that every lane of row r
 //     needs at step i), each 16-K block's sum scaled by its E4M3 scale in fp32,
-//     the four rows that split a column's K added with lane shuffles.
+//     the four rows that split a column's K added with lane shuffles.  At
+//     M = 2 each widened code pair feeds one v_dot2c per x row.
 //   * MFMA (M = 1..8): v_mfma_f32_16x16x32_f16 with the widened weights
 //     (E2M1 * E4M3 in fp16, exact) as operand B and the x rows, zero-padded to
 //     16, as operand A.  The workgroup's x slice is copied into LDS with
@@ -107,7 +108,7 @@ __device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
 }
 
 // ---------------------------------------------------------------------------
-// VALU engine, M = 1.
+// VALU engine, M = 1 and 2.
 // ---------------------------------------------------------------------------
 // Sixteen codes (two dwords, one 16-K block) against x pairs broadcast from
 // lanes 0..7 (lo) or 8..15 (hi) of the lane's own 16-lane row.  One asm block
@@ -151,73 +152,151 @@ SKINNY_BLOCK_DOT(block_dot_lo, 0, 1, 2, 3, 4, 5, 6, 7)
 SKINNY_BLOCK_DOT(block_dot_hi, 8, 9, 10, 11, 12, 13, 14, 15)
 #undef SKINNY_BLOCK_DOT
 
-template <int CT, int EPI>
-__global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu_m1(Nvfp4Args a) {
-  __shared__ float red[kMaxWaves][16];
+// The same for two rows of x (M = 2): the codes are widened once and feed
+// sixteen v_dot2c, eight per row; the wait states are those of the one-row
+// block.
+#define SKINNY_BLOCK_DOT2(NAME, R0, R1, R2, R3, R4, R5, R6, R7)                                          \
+  __device__ __forceinline__ void NAME(uint32_t x0, uint32_t x1, uint32_t w0, uint32_t w1, float& p0,   \
+                                       float& p1) {                                                     \
+    p0 = 0.0f;                                                                                          \
+    p1 = 0.0f;                                                                                          \
+    uint32_t t0, t1, t2, t3, t4, t5, t6, t7;                                                            \
+    asm("v_cvt_scalef32_pk_f16_fp4 %2, %10, 1.0\n"                                                     \
+        "v_cvt_scalef32_pk_f16_fp4 %3, %10, 1.0 op_sel:[1,0,0]\n"                                      \
+        "v_cvt_scalef32_pk_f16_fp4 %4, %10, 1.0 op_sel:[0,1,0]\n"                                      \
+        "v_cvt_scalef32_pk_f16_fp4 %5, %10, 1.0 op_sel:[1,1,0]\n"                                      \
+        "v_cvt_scalef32_pk_f16_fp4 %6, %11, 1.0\n"                                                     \
+        "v_cvt_scalef32_pk_f16_fp4 %7, %11, 1.0 op_sel:[1,0,0]\n"                                      \
+        "v_cvt_scalef32_pk_f16_fp4 %8, %11, 1.0 op_sel:[0,1,0]\n"                                      \
+        "v_cvt_scalef32_pk_f16_fp4 %9, %11, 1.0 op_sel:[1,1,0]\n"                                      \
+        "s_nop 1\n"                                                                                     \
+        "v_dot2c_f32_f16_dpp %0, %12, %2 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %1, %13, %2 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %0, %12, %3 row_newbcast:" #R1 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %1, %13, %3 row_newbcast:" #R1 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %0, %12, %4 row_newbcast:" #R2 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %1, %13, %4 row_newbcast:" #R2 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %0, %12, %5 row_newbcast:" #R3 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %1, %13, %5 row_newbcast:" #R3 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %0, %12, %6 row_newbcast:" #R4 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %1, %13, %6 row_newbcast:" #R4 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %0, %12, %7 row_newbcast:" #R5 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %1, %13, %7 row_newbcast:" #R5 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %0, %12, %8 row_newbcast:" #R6 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %1, %13, %8 row_newbcast:" #R6 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %0, %12, %9 row_newbcast:" #R7 " row_mask:0xf bank_mask:0xf\n"             \
+        "v_dot2c_f32_f16_dpp %1, %13, %9 row_newbcast:" #R7 " row_mask:0xf bank_mask:0xf\n"             \
+        "s_nop 1\n"                                                                                     \
+        : "+v"(p0), "+v"(p1), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5),         \
+          "=&v"(t6), "=&v"(t7)                                                                          \
+        : "v"(w0), "v"(w1), "v"(x0), "v"(x1));                                                          \
+  }
+SKINNY_BLOCK_DOT2(block_dot2_lo, 0, 1, 2, 3, 4, 5, 6, 7)
+SKINNY_BLOCK_DOT2(block_dot2_hi, 8, 9, 10, 11, 12, 13, 14, 15)
+#undef SKINNY_BLOCK_DOT2
+
+// MR rows of x (MR = M = 1 or 2), one unit per wavefront.
+template <int CT, int EPI, int MR>
+__global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu(Nvfp4Args a) {
+  __shared__ float red[kMaxWaves][MR][16];
   const Plan P(a, CT);
-  float acc = 0.0f;
+  float acc[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) acc[r] = 0.0f;
   if (P.active) {
-    // The whole unit plus this lane's x pair of each chunk (k = 1024g + 128j + 2*lane).
+    // The whole unit plus this lane's x pair of each chunk and row (k = 1024g + 128j + 2*lane).
     const uint8_t* p = P.unit_ptr(a);
     const u32x4 sv = load16(p + kChunksPerUnit * kChunkBytes);
     u32x4 c[kChunksPerUnit];
-    uint32_t xv[kChunksPerUnit];
+    uint32_t xv[MR][kChunksPerUnit];
     const int kx = (P.s0 + P.s) * kUnitK + 2 * P.lane;
-    // A pair past K reads the last pair of x instead (index in [0, K-2],
-    // even, so the 4-byte load stays in the row): the packed codes and
-    // scales there are zero, so it adds exact zeros for finite x.  Clamping
-    // the address rather than selecting zero after the load keeps the loads
-    // independent; a select on loaded data made the first chunk wait for
-    // half of the unit's loads.
+    // A pair past K reads the last pair of its row instead (index in
+    // [0, K-2], even, so the 4-byte load stays in the row): the packed codes
+    // and scales there are zero, so it adds exact zeros for finite x.
+    // Clamping the address rather than selecting zero after the load keeps
+    // the loads independent; a select on loaded data made the first chunk
+    // wait for half of the unit's loads.
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
       c[j] = load16(p + j * kChunkBytes);
-      xv[j] = *reinterpret_cast<const uint32_t*>(a.x + min(kx + j * kChunkK, a.K - 2));
+#pragma unroll
+      for (int r = 0; r < MR; ++r)
+        xv[r][j] = *reinterpret_cast<const uint32_t*>(a.x + static_cast<size_t>(r) * a.K +
+                                                      min(kx + j * kChunkK, a.K - 2));
     }
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
       const uint32_t sd = dword(sv, j >> 1);
       const float s0 = (j & 1) ? e4m3f<2>(sd) : e4m3f<0>(sd);
       const float s1 = (j & 1) ? e4m3f<3>(sd) : e4m3f<1>(sd);
-      acc = __builtin_fmaf(block_dot_lo(xv[j], c[j].x, c[j].y), s0, acc);
-      acc = __builtin_fmaf(block_dot_hi(xv[j], c[j].z, c[j].w), s1, acc);
+      if constexpr (MR == 1) {
+        acc[0] = __builtin_fmaf(block_dot_lo(xv[0][j], c[j].x, c[j].y), s0, acc[0]);
+        acc[0] = __builtin_fmaf(block_dot_hi(xv[0][j], c[j].z, c[j].w), s1, acc[0]);
+      } else {
+        float p0, p1;
+        block_dot2_lo(xv[0][j], xv[1][j], c[j].x, c[j].y, p0, p1);
+        acc[0] = __builtin_fmaf(p0, s0, acc[0]);
+        acc[1] = __builtin_fmaf(p1, s0, acc[1]);
+        block_dot2_hi(xv[0][j], xv[1][j], c[j].z, c[j].w, p0, p1);
+        acc[0] = __builtin_fmaf(p0, s1, acc[0]);
+        acc[1] = __builtin_fmaf(p1, s1, acc[1]);
+      }
     }
   }
-  acc = sum_over_rows(acc);
-  if (P.lane < 16) red[P.wave][P.lane] = acc;
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    acc[r] = sum_over_rows(acc[r]);
+    if (P.lane < 16) red[P.wave][r][P.lane] = acc[r];
+  }
   __syncthreads();
 
   // Wavefront t < CT finishes local tile t: its spans in order, then the
-  // output or, with a K split, this split's partial sum.
+  // outputs or, with a K split, this split's partial sums.
   const bool fin = P.wave < CT && P.lane < 16 && P.tile0 + P.wave < a.nt;
   const int n = (P.tile0 + P.wave) * kTileCols + P.lane;
-  float tot = 0.0f;
+  float tot[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) tot[r] = 0.0f;
   if (fin) {
-    for (int s = 0; s < P.sw; ++s) tot += red[P.wave * P.S + s][P.lane];
+    for (int s = 0; s < P.sw; ++s) {
+#pragma unroll
+      for (int r = 0; r < MR; ++r) tot[r] += red[P.wave * P.S + s][r][P.lane];
+    }
     if (EPI == kEpiSwiglu && a.ksplit == 1) {  // lanes 0..15 of the wavefront are all here
-      const float h = swiglu_pair(tot, *a.gptr, *a.g2ptr);
       const int f = (P.tile0 + P.wave) * 8 + P.lane;
-      if (P.lane < 8 && f < a.F) a.y[f] = static_cast<_Float16>(h);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const float h = swiglu_pair(tot[r], *a.gptr, *a.g2ptr);
+        if (P.lane < 8 && f < a.F) a.y[static_cast<size_t>(r) * a.F + f] = static_cast<_Float16>(h);
+      }
     } else if (n < a.N) {
-      if (a.ksplit > 1)
-        a.part[static_cast<size_t>(blockIdx.y) * a.N + n] = tot;
-      else if (EPI != kEpiArgmax || a.y)  // the lm_head's logits are optional
-        a.y[n] = static_cast<_Float16>(*a.gptr * tot);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        if (a.ksplit > 1)
+          a.part[(static_cast<size_t>(blockIdx.y) * MR + r) * a.N + n] = tot[r];
+        else if (EPI != kEpiArgmax || a.y)  // the lm_head's logits are optional
+          a.y[static_cast<size_t>(r) * a.N + n] = static_cast<_Float16>(*a.gptr * tot[r]);
+      }
     }
   }
   if (EPI == kEpiArgmax) {
-    // lm_head (M = 1, no K split): the (fp32 logit, column) key of each of
-    // this workgroup's tiles, then of the workgroup, as its one candidate.
+    // lm_head (no K split): per row, the (fp32 logit, column) key of each of
+    // this workgroup's tiles, then of the workgroup, as its candidate.
     // Every lane runs the shuffles; lanes outside a finished tile hold 0.
-    __shared__ unsigned long long best[kMaxWaves];
-    unsigned long long key = fin && n < a.N ? argmax_key(*a.gptr * tot, n) : 0ull;
-    key = wave_max_key<16>(key);
-    if (P.lane == 0) best[P.wave] = key;
+    __shared__ unsigned long long best[kMaxWaves][MR];
+    unsigned long long key[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) key[r] = fin && n < a.N ? argmax_key(*a.gptr * tot[r], n) : 0ull;
+    wave_max_keys<MR, 16>(key);
+    if (P.lane == 0) {
+#pragma unroll
+      for (int r = 0; r < MR; ++r) best[P.wave][r] = key[r];
+    }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < MR) {
       unsigned long long k = 0ull;
-      for (int t = 0; t < CT; ++t) k = best[t] > k ? best[t] : k;
-      a.cand[blockIdx.x] = k;
+      for (int t = 0; t < CT; ++t) k = best[t][threadIdx.x] > k ? best[t][threadIdx.x] : k;
+      a.cand[static_cast<size_t>(blockIdx.x) * MR + threadIdx.x] = k;
     }
   }
 }
@@ -563,6 +642,12 @@ hipError_t launch(Kern k, dim3 grid, int nw, size_t lds, const Nvfp4Args& a, hip
   return hipGetLastError();
 }
 
+template <int CT, int EPI>
+hipError_t launch_valu(dim3 grid, int nw, const Nvfp4Args& a, hipStream_t stream) {
+  return a.M == 2 ? launch(nvfp4_valu<CT, EPI, 2>, grid, nw, 0, a, stream)
+                  : launch(nvfp4_valu<CT, EPI, 1>, grid, nw, 0, a, stream);
+}
+
 }  // namespace
 
 size_t nvfp4_stream_lds_bytes(int M, int K, int nw) {
@@ -595,7 +680,7 @@ bool nvfp4_cfg_supported(const LaunchCfg& c, int M, int K, bool argmax) {
   const int ku = (K + kUnitK - 1) / kUnitK;
   const int S = c.nw / c.ct;
   if (static_cast<long>(c.ksplit) * S < ku || static_cast<long>(c.ksplit - 1) * S >= ku) return false;
-  if (c.engine == 0) return M == 1;
+  if (c.engine == 0) return M <= 2;
   if (c.engine != 1) return false;
   return nvfp4_mfma_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
 }
@@ -603,9 +688,9 @@ bool nvfp4_cfg_supported(const LaunchCfg& c, int M, int K, bool argmax) {
 #define SKINNY_NVFP4_DISPATCH(CT)                                                                       \
   if (cfg.ct == CT) {                                                                                   \
     if (cfg.engine == 0)                                                                                \
-      return epi == kEpiSwiglu                      ? launch(nvfp4_valu_m1<CT, kEpiSwiglu>, grid, cfg.nw, 0, a, stream) \
-             : epi == kEpiArgmax && cfg.ksplit == 1 ? launch(nvfp4_valu_m1<CT, kEpiArgmax>, grid, cfg.nw, 0, a, stream) \
-                                                    : launch(nvfp4_valu_m1<CT, kEpiPlain>, grid, cfg.nw, 0, a, stream);  \
+      return epi == kEpiSwiglu                      ? launch_valu<CT, kEpiSwiglu>(grid, cfg.nw, a, stream) \
+             : epi == kEpiArgmax && cfg.ksplit == 1 ? launch_valu<CT, kEpiArgmax>(grid, cfg.nw, a, stream) \
+                                                    : launch_valu<CT, kEpiPlain>(grid, cfg.nw, a, stream);  \
     if (epi == kEpiArgmax && cfg.ksplit == 1)                                                           \
       return launch(nvfp4_mfma<CT, kEpiArgmax>, grid, cfg.nw, lds, a, stream);                          \
     if (epi == kEpiSwiglu && cfg.ksplit == 1)                                                           \

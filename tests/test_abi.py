@@ -64,8 +64,8 @@ def test_nvfp4_gemm_argument_errors():
 def test_explicit_config_rejections():
     L = lib()
     cfg = lambda *c: L.nvfp4_gemm_config(A, A, A, c[0], 256, 512, None, 0, None, *c[1:])
-    # VALU engine is M = 1 only; unknown engine / tile counts / wave counts / splits are rejected.
-    assert cfg(2, 0, 1, 4, 1) == sk.EINVAL
+    # VALU engine is M <= 2 only; unknown engine / tile counts / wave counts / splits are rejected.
+    assert cfg(3, 0, 1, 4, 1) == sk.EINVAL
     assert cfg(1, 3, 1, 4, 1) == sk.EINVAL
     # streaming engine: no K split, 1 or 2 workgroups per CU, at most 9 K spans, NVFP4 calls only
     assert cfg(1, 2, 1, 4, 2) == sk.EINVAL
@@ -87,8 +87,13 @@ def test_explicit_config_rejections():
     assert sk.config_supported(sk.OP_FP8, 1, 5120, 7168, (0, 1, 10, 1))
     assert sk.config_supported(sk.OP_FP8, 4, 5120, 7168, (0, 1, 10, 1))
     assert not sk.config_supported(sk.OP_FP8, 5, 5120, 7168, (0, 1, 10, 1))
-    assert L.lm_head_gemm_argmax_config(A, A, A, None, 2, 256, 512, A, 256, None, 0, 1, 4, 1) == sk.EINVAL
+    # NVFP4 VALU engine: M <= 2
+    assert L.lm_head_gemm_argmax_config(A, A, A, None, 3, 256, 512, A, 256, None, 0, 1, 4, 1) == sk.EINVAL
+    assert L.nvfp4_gemm_config(A, A, A, 3, 256, 512, None, 0, None, 0, 1, 4, 1) == sk.EINVAL
     assert sk.config_supported(sk.OP_LM_HEAD, 1, 5120, 151936, (0, 1, 5, 1))
+    assert sk.config_supported(sk.OP_LM_HEAD, 2, 5120, 151936, (0, 1, 5, 1))
+    assert sk.config_supported(sk.OP_SWIGLU, 2, 5120, 17408, (0, 1, 5, 1))
+    assert not sk.config_supported(sk.OP_NVFP4, 3, 5120, 17408, (0, 1, 5, 1))
     # a K split needs its workspace
     big = lambda ws, wsb: L.nvfp4_gemm_config(A, A, A, 8, 17408, 5120, ws, wsb, None, 1, 1, 4, 5)
     need = sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 1, 4, 5))

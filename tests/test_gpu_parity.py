@@ -103,7 +103,8 @@ def ref_fp8(case, M=None):
     return oracle.fp8_gemm(case["x"][:M], case["codes"], case["scales"])
 
 
-SMALL_NVFP4 = [(1, 256, 512), (1, 272, 100), (3, 400, 300), (8, 1040, 1000), (8, 2064, 48), (1, 3088, 200), (2, 16, 7)]
+SMALL_NVFP4 = [(1, 256, 512), (1, 272, 100), (3, 400, 300), (8, 1040, 1000), (8, 2064, 48), (1, 3088, 200), (2, 16, 7),
+               (2, 2064, 333)]
 
 
 @pytest.fixture(scope="module")
@@ -121,14 +122,14 @@ def test_nvfp4_one_hot_reproduces_dequantized_weights_exactly(K, N):
     assert np.array_equal(deq.astype(np.float16).astype(np.float64), deq)
     eye = torch.eye(K, dtype=torch.float16, device="cuda")
     for cfg in cfgs(1, K) + cfgs(0, K) + stream_cfgs(sk.OP_NVFP4, 8, K, N):
-        rows = 1 if cfg[0] == 0 else 8
-        out = np.empty((K, N))
-        ws = ws_for(sk.OP_NVFP4, rows, K, N, cfg)
-        for r0 in range(0, K, rows):
-            y = torch.empty((rows, N), dtype=torch.float16, device="cuda")
-            sk.nvfp4_gemm(blob, eye[r0:r0 + rows].contiguous(), y, config=cfg, workspace=ws)
-            out[r0:r0 + rows] = y.float().cpu().numpy()
-        assert np.array_equal(out, deq), f"config {cfg}: {np.argwhere(out != deq)[:5]}"
+        for rows in ((1, 2) if cfg[0] == 0 else (8,)):
+            out = np.empty((K, N))
+            ws = ws_for(sk.OP_NVFP4, rows, K, N, cfg)
+            for r0 in range(0, K, rows):
+                y = torch.empty((rows, N), dtype=torch.float16, device="cuda")
+                sk.nvfp4_gemm(blob, eye[r0:r0 + rows].contiguous(), y, config=cfg, workspace=ws)
+                out[r0:r0 + rows] = y.float().cpu().numpy()
+            assert np.array_equal(out, deq), f"config {cfg} rows {rows}: {np.argwhere(out != deq)[:5]}"
 
 
 def test_fp8_one_hot_reproduces_codes_exactly():
@@ -167,7 +168,7 @@ def test_fp8_one_hot_reproduces_codes_exactly():
 def test_nvfp4_parity_all_configs(small_nvfp4, shape):
     case = small_nvfp4[shape]
     ref = ref_nvfp4(case)
-    choices = (cfgs(1, case["K"]) + (cfgs(0, case["K"]) if case["M"] == 1 else [])
+    choices = (cfgs(1, case["K"]) + (cfgs(0, case["K"]) if case["M"] <= 2 else [])
                + stream_cfgs(sk.OP_NVFP4, case["M"], case["K"], case["N"]))
     for cfg in choices:
         _check(run_nvfp4(case, config=cfg), ref, f"{shape} {cfg}")
@@ -181,10 +182,14 @@ def test_nvfp4_every_m():
         _check(run_nvfp4(case, M=M), ref, f"M={M} default")
         _check(run_nvfp4(case, M=M, config=(1, 2, 2, 2)), ref, f"M={M} mfma split")
         _check(run_nvfp4(case, M=M, config=(2, 1, 16, 1)), ref, f"M={M} streaming")
+        if M <= 2:
+            _check(run_nvfp4(case, M=M, config=(0, 1, 1, 2)), ref, f"M={M} VALU split")
+            _check(run_nvfp4(case, M=M, config=(0, 2, 4, 1)), ref, f"M={M} VALU")
 
 
 # ------------------------------------------------------------ SwiGLU pair
-SMALL_SWIGLU = [(1, 256, 8), (1, 272, 13), (3, 400, 100), (8, 1040, 500), (8, 2064, 21), (1, 3088, 40), (2, 16, 5)]
+SMALL_SWIGLU = [(1, 256, 8), (1, 272, 13), (3, 400, 100), (8, 1040, 500), (8, 2064, 21), (1, 3088, 40), (2, 16, 5),
+                (2, 2064, 40)]
 
 
 def run_swiglu(case, M=None, config=None, guard=0):
@@ -206,7 +211,7 @@ def test_nvfp4_swiglu_parity_all_configs(shape):
     M, K, F = shape
     case = workload.swiglu_case(M, K, F, seed=sum(shape) + 7)
     ref = oracle.nvfp4_swiglu(case["x"], case["gate"], case["up"])
-    choices = (cfgs(1, K) + (cfgs(0, K) if M == 1 else [])
+    choices = (cfgs(1, K) + (cfgs(0, K) if M <= 2 else [])
                + stream_cfgs(sk.OP_SWIGLU, M, K, F))
     assert choices
     for cfg in choices:
@@ -271,13 +276,13 @@ def run_lm_head(case, M, config=None, logits=False, ws=None):
     return idx.cpu().numpy(), (lg.float().cpu().numpy() if logits else None)
 
 
-@pytest.mark.parametrize("shape", [(1, 256, 1000), (8, 512, 3000), (5, 272, 777), (8, 1024, 16)])
+@pytest.mark.parametrize("shape", [(1, 256, 1000), (8, 512, 3000), (5, 272, 777), (8, 1024, 16), (2, 2064, 1500)])
 def test_lm_head_argmax_and_logits(shape):
     M, K, N = shape
     case = workload.nvfp4_case(*shape, seed=sum(shape))
     ref = ref_nvfp4(case)
     want, margin = oracle.argmax_rows(ref)
-    valu = cfgs(0, K) if M == 1 else []
+    valu = cfgs(0, K) if M <= 2 else []
     for cfg in valu + cfgs(1, K) + stream_cfgs(sk.OP_LM_HEAD, M, K, N):
         idx, lg = run_lm_head(case, M, config=cfg, logits=True)
         assert np.array_equal(idx, want), f"{shape} {cfg}: {idx} vs {want} (margins {margin})"
@@ -286,11 +291,12 @@ def test_lm_head_argmax_and_logits(shape):
     assert np.array_equal(idx, want)
 
 
-@pytest.mark.parametrize("M,K", [(4, 256), (8, 2048), (1, 2048)])
+@pytest.mark.parametrize("M,K", [(4, 256), (8, 2048), (1, 2048), (2, 1024)])
 def test_lm_head_ties_go_to_lowest_column(M, K):
     """Exact ties in every row; M = 8 fills both four-row groups of the MFMA
     output, K = 2048 adds K-split choices (argmax in the split reduction) and
-    M = 1 adds the VALU engine's candidates and the one-row key reduction."""
+    M = 1 and 2 add the VALU engine's candidates, M = 1 the one-row key
+    reduction."""
     N = 700
     case = workload.nvfp4_case(M, K, N, seed=21)
     ref = ref_nvfp4(case)
@@ -303,7 +309,7 @@ def test_lm_head_ties_go_to_lowest_column(M, K):
     case2 = dict(case, codes=codes, scales=scales, blob=sk.nvfp4_pack(codes, scales, case["g"], K, N))
     ref2 = ref_nvfp4(case2)
     want, _ = oracle.argmax_rows(ref2)
-    valu = cfgs(0, K) if M == 1 else []
+    valu = cfgs(0, K) if M <= 2 else []
     for cfg in valu + cfgs(1, K) + stream_cfgs(sk.OP_LM_HEAD, M, K, N):
         idx, _ = run_lm_head(case2, M, config=cfg)
         assert np.array_equal(idx, want), f"{cfg}: {idx} vs {want}"
@@ -382,6 +388,13 @@ def test_lm_head_verify_greedy_rounds():
             assert list(res) == want_res, (cfg, drafts, list(res), want_res)
     idx, res = run_verify(case, 1, [])
     assert list(res) == [0, int(want_idx[0])]
+    # M = 2 (one draft), accepted and rejected, on the VALU engine and the default choice
+    for cfg in [(0, 1, 2, 1), (0, 2, 2, 2), None]:
+        for d in ([int(want_idx[0])], [(int(want_idx[0]) + 1) % N]):
+            idx, res = run_verify(case, 2, d, config=cfg)
+            assert np.array_equal(idx, want_idx[:2]), (cfg, idx, want_idx[:2])
+            L, committed = oracle.verify_greedy(want_idx[:2], d)
+            assert list(res) == [L] + committed + [-1] * (1 - L), (cfg, d, list(res))
 
 
 def test_calls_on_two_streams_do_not_interfere():
