@@ -102,11 +102,12 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 // vocabulary the GEMV reads at 6.95 TB/s against 6.5 TB/s for the streaming
 // engine): VALU engine, whole K per workgroup (K beyond
 // 16 spans split over workgroups, evened out), two tiles per workgroup when
-// there are few tiles (N <= 6144), else one.  NVFP4 at M = 2 takes the same
-// choice only when K needs a split (more than 16 spans): on the 17408 x 5120
-// down projection it took 12.7 us against 13.7 us for the MFMA engine, while
-// on the whole-K shapes (up, gate+up, lm_head) the MFMA and streaming engines
-// were 2 to 15% faster.  FP8 at M <= 2: its VALU engine,
+// there are few tiles (N <= 6144), else one.  NVFP4 at M = 2 without argmax
+// takes the same choice when there are few tiles (N <= 6144): on the
+// 17408 x 5120 down projection it took 12.7 us against 13.7 us for the MFMA
+// engine, and 6.0 against 6.5-6.7 us on one rank's 4-way share of up and
+// down; with more tiles (up, gate+up) and on the lm_head the MFMA and
+// streaming engines were faster.  FP8 at M <= 2: its VALU engine,
 // whole K per workgroup, two tiles only when 2 * K spans <= 16 and N <= 6144
 // (on qkv and o_proj one tile of 10 or 12 units was within 0.03 us of the
 // fastest choice at M = 1, 0.3 to 0.6 us ahead of the MFMA engine, and about
@@ -169,7 +170,7 @@ bool pick_stream_cfg(int M, int K, int N, bool argmax, LaunchCfg* out) {
 LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax) {
   const Geometry g = nvfp4_geometry(K, N);
   auto fits = [&](const LaunchCfg& c) { return nvfp4_cfg_supported(c, M, K, argmax); };
-  if (M == 1 || (M == 2 && !argmax && g.ku > kMaxWaves)) return pick_whole_k_cfg(0, g.nt <= 384 ? 2 : 1, g.ku, fits);
+  if (M == 1 || (M == 2 && !argmax && g.nt <= 384)) return pick_whole_k_cfg(0, g.nt <= 384 ? 2 : 1, g.ku, fits);
   LaunchCfg c;
   if (pick_stream_cfg(M, K, N, argmax, &c)) return c;
   return pick_oneshot_cfg(M, K, g.ku, g.nt, fits);
