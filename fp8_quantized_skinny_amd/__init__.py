@@ -68,6 +68,13 @@ def workspace_bytes(op, M, K, N, config=None):
     return int(lib().skinny_workspace_bytes_config(op, M, K, N, *config))
 
 
+def default_config(op, M, K, N):
+    """The library's own kernel choice (engine, ct, nw, ksplit) for this op and shape."""
+    v = [ctypes.c_int() for _ in range(4)]
+    _check(lib().skinny_default_config(op, M, K, N, *[ctypes.byref(c) for c in v]), "skinny_default_config")
+    return tuple(c.value for c in v)
+
+
 def config_supported(op, M, K, N, config):
     """True if the explicit kernel choice (engine, ct, nw, ksplit) is supported for this op and shape."""
     return bool(lib().skinny_config_supported(op, M, K, N, *config))

@@ -40,6 +40,7 @@ def _declare(lib):
                                                c_int, c_int, c_int, c_int]),
         "skinny_workspace_bytes_config": (c_size_t, [c_int] * 8),
         "skinny_config_supported": (c_int, [c_int] * 8),
+        "skinny_default_config": (c_int, [c_int] * 4 + [ctypes.POINTER(c_int)] * 4),
         "skinny_read_probe": (c_int, [P, c_size_t, P, P]),
         "nvfp4_quantize": (c_int, [P, c_int, c_int, P, P, ctypes.POINTER(c_float)]),
         "fp8_quantize": (c_int, [P, c_int, c_int, P, P]),
@@ -72,4 +73,4 @@ EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp
             "skinny_config_supported", "skinny_read_probe", "nvfp4_pack_swiglu", "nvfp4_gemm_swiglu",
             "nvfp4_gemm_swiglu_config", "lm_head_verify_greedy", "lm_head_verify_greedy_config",
             "skinny_layers_workspace_bytes", "skinny_layers_run", "fp8_pack", "fp8_gemm_packed",
-            "fp8_gemm_packed_config")
+            "fp8_gemm_packed_config", "skinny_default_config")

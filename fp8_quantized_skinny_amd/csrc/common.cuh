@@ -118,8 +118,12 @@ __device__ __forceinline__ void zero_x_tail(_Float16* xs, int M, int RS, int fro
 
 // Ordered argmax key of logit v at column n: the top 32 bits order like the
 // fp32 value (+0 and -0 made equal), the low 32 bits are the inverted column,
-// so the larger key is the larger logit or, on a tie, the lower column.
+// so the larger key is the larger logit or, on a tie, the lower column.  A
+// NaN logit is no score: it gets key 0, the "no candidate" key, which every
+// number (even -inf, whose key is 0x007FFFFF...) beats, so a NaN never wins
+// and a row of NaN alone leaves the index at 0xFFFFFFFF - 0 = -1.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
+  if (v != v) return 0ull;
   if (v == 0.0f) v = 0.0f;
   const uint32_t b = __builtin_bit_cast(uint32_t, v);
   const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);

@@ -321,6 +321,20 @@ int skinny_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t
   return launch_status(launch_read_probe(buf, bytes, sink, stream));
 }
 
+int skinny_default_config(int op, int M, int K, int N, int* engine, int* ct, int* nw, int* ksplit) {
+  if (!engine || !ct || !nw || !ksplit) return SKINNY_EINVAL;
+  if (op < 0 || op > 3) return SKINNY_EINVAL;
+  if (op == 3 ? swiglu_shape(M, K, N) : check_shape(M, K, N)) return SKINNY_ESHAPE;
+  const LaunchCfg c = op == 1   ? default_fp8_cfg(M, K, N)
+                      : op == 3 ? default_nvfp4_cfg(M, K, swiglu_packed_cols(N), false)
+                                : default_nvfp4_cfg(M, K, N, op == 2);
+  *engine = c.engine;
+  *ct = c.ct;
+  *nw = c.nw;
+  *ksplit = c.ksplit;
+  return SKINNY_OK;
+}
+
 size_t skinny_workspace_bytes(int op, int M, int K, int N) {
   if (check_shape(M, K, N)) return 0;
   switch (op) {

@@ -102,7 +102,7 @@ static_assert(sizeof(Fp8Header) <= kHeaderBytes, "header too large");
 
 // Launch parameters picked by the host for one call.
 struct LaunchCfg {
-  int engine;  // 0 = VALU dot2 (M = 1 only), 1 = MFMA 16x16x32 f16, 2 = streaming MFMA
+  int engine;  // 0 = VALU dot2 (NVFP4 M <= 2, FP8 M <= 4), 1 = MFMA 16x16x32 f16, 2 = streaming MFMA
   int ct;      // engines 0, 1: column tiles (of 16) per workgroup; engine 2: workgroups per CU
   int nw;      // wavefronts per workgroup (1..16); engines 0, 1: ct * K spans per workgroup
   int ksplit;  // workgroups that split K (1 = no split; engine 2 never splits)

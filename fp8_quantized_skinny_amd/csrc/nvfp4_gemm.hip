@@ -103,6 +103,9 @@ struct Plan {
   }
 };
 
+// Read in place of activation pairs past K by the VALU engine.
+__device__ const uint32_t kZeroPair = 0u;
+
 __device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -210,19 +213,21 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu(Nvfp4Args a) {
     u32x4 c[kChunksPerUnit];
     uint32_t xv[MR][kChunksPerUnit];
     const int kx = (P.s0 + P.s) * kUnitK + 2 * P.lane;
-    // A pair past K reads the last pair of its row instead (index in
-    // [0, K-2], even, so the 4-byte load stays in the row): the packed codes
-    // and scales there are zero, so it adds exact zeros for finite x.
-    // Clamping the address rather than selecting zero after the load keeps
-    // the loads independent; a select on loaded data made the first chunk
-    // wait for half of the unit's loads.
+    // A pair past K (k even and K % 16 == 0, so a pair is all in or all out)
+    // reads a zero word instead: the packed weights there are zero too, and
+    // 0 * 0 adds nothing whatever the row's real activations hold (a clamped
+    // real pair would turn an inf or NaN at the end of the row into NaN for
+    // every column).  Choosing the address rather than selecting zero after
+    // the load keeps the loads independent; a select on loaded data made the
+    // first chunk wait for half of the unit's loads.
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
       c[j] = load16(p + j * kChunkBytes);
+      const int k = kx + j * kChunkK;
 #pragma unroll
       for (int r = 0; r < MR; ++r)
-        xv[r][j] = *reinterpret_cast<const uint32_t*>(a.x + static_cast<size_t>(r) * a.K +
-                                                      min(kx + j * kChunkK, a.K - 2));
+        xv[r][j] = *(k < a.K ? reinterpret_cast<const uint32_t*>(a.x + static_cast<size_t>(r) * a.K + k)
+                             : &kZeroPair);
     }
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {

@@ -299,9 +299,9 @@ int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales);
 /* ---------------------------------------------------------------------------
  * The GEMM calls with an explicit kernel choice instead of the
  * library's pick (same arguments and results, used to compare kernels):
- *   engine : 0 = VALU dot2 engine (nvfp4_gemm, lm_head_gemm_argmax and
- *                lm_head_verify_greedy with M == 1; fp8_gemm and
- *                fp8_gemm_packed with M <= 4),
+ *   engine : 0 = VALU dot2 engine (nvfp4_gemm, nvfp4_gemm_swiglu,
+ *                lm_head_gemm_argmax and lm_head_verify_greedy with M <= 2;
+ *                fp8_gemm and fp8_gemm_packed with M <= 4),
  *            1 = MFMA 16x16x32 f16 engine (all calls, M = 1..8),
  *            2 = streaming MFMA engine (nvfp4_gemm and lm_head_gemm_argmax,
  *                K <= 9216): each workgroup keeps all of x in LDS and each
@@ -348,7 +348,7 @@ int lm_head_verify_greedy_config(const void* w_packed, const uint16_t* x,
                                  hipStream_t stream, int engine, int ct, int nw,
                                  int ksplit);
 /* For nvfp4_gemm_swiglu the choice applies to the packed blob's
- * 16 * ceil(F / 8) columns (engine 0 is available for M == 1). */
+ * 16 * ceil(F / 8) columns (engine 0 is available for M <= 2). */
 int nvfp4_gemm_swiglu_config(const void* w_packed, const uint16_t* x,
                              uint16_t* h, int M, int K, int F, void* workspace,
                              size_t workspace_bytes, hipStream_t stream,
@@ -358,6 +358,15 @@ int nvfp4_gemm_swiglu_config(const void* w_packed, const uint16_t* x,
  * below), else 0. */
 int skinny_config_supported(int op, int M, int K, int N, int engine, int ct,
                             int nw, int ksplit);
+
+/* The kernel choice the library makes for a call of this op and shape (op
+ * as below), written to *engine, *ct, *nw, *ksplit (host pointers, all
+ * non-NULL).  Returns SKINNY_OK, SKINNY_ESHAPE for an unsupported shape or
+ * SKINNY_EINVAL for a bad op or NULL pointer.  The choice can be passed to
+ * the *_config calls; it is always supported for that op, M and K (the N of
+ * another call may make the library choose differently). */
+int skinny_default_config(int op, int M, int K, int N, int* engine, int* ct,
+                          int* nw, int* ksplit);
 
 /* Workspace bytes of a call made with an explicit kernel choice (op as
  * below); 0 for an unsupported choice or when none is needed. */

@@ -15,7 +15,7 @@ tables, library routines, brute force and closed-form cases.
 """
 
 from .formats import e2m1_decode, e4m3_decode, e2m1_encode, e4m3_encode, E2M1_MAX, E4M3_MAX
-from .quantize import nvfp4_quantize, fp8_quantize
+from .quantize import nvfp4_quantize, nvfp4_global_scale, fp8_quantize
 from .speculative import verify_greedy
 from .gemm import (nvfp4_unpack_codes, nvfp4_dequant_unscaled, nvfp4_gemm, fp8_dequant, fp8_gemm,
                    silu, nvfp4_swiglu, argmax_rows, compare)

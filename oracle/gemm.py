@@ -12,9 +12,11 @@ token plus k=7 drafts, post section on why M=8 matters):
   y[m, n]  = sum_k x[m, k] * W~[k, n]                 (float64 here)
   NVFP4:  W~[k, n] = E2M1(q[n, k]) * E4M3(s[n, k//16]) * g
   FP8:    W~[k, n] = E4M3(c[n, k]) * S[n//128, k//128]
-  argmax: idx[m] = smallest n with y[m, n] == max_n' y[m, n']
+  argmax: idx[m] = smallest n with y[m, n] == max over the non-NaN y[m, n'],
+          -1 if every y[m, n] is NaN
           (the drafter should propose greedy / local-argmax tokens: post,
-           section "This is a server, not a GEMM screenshot")
+           section "This is a server, not a GEMM screenshot"; a NaN logit is
+           no token's score, so it never wins)
 
 The method reaches this exact result up to the order of floating-point sums,
 so the oracle is the definition: decode, widen to float64, one matmul.
@@ -117,16 +119,30 @@ def nvfp4_swiglu(x, gate, up, cols=None, chunk=1024):
 
 
 def argmax_rows(y):
-    """Per-row index of the maximum, ties to the lowest index; plus the normalised margin.
+    """Per-row greedy token: the lowest index holding the largest logit; plus the normalised margin.
 
-    margin[m] = (top1 - top2) / RMS(y[m, :]) -- how far the winner is ahead."""
+    NaN logits never win: the maximum is taken over the logits that are
+    numbers (+-inf included), and the index is the first column equal to it.
+    A row with no number at all (every logit NaN) has no greedy token: -1.
+
+    margin[m] = (top1 - top2) / RMS of row m, both over its non-NaN logits --
+    how far the winner is ahead (NaN where fewer than two logits are numbers)."""
     y = np.asarray(y, dtype=np.float64)
-    idx = np.argmax(y, axis=1)              # numpy returns the first maximum
-    top2 = np.partition(y, -2, axis=1)[:, -2:] if y.shape[1] > 1 else np.repeat(y, 2, axis=1)
-    rms = np.sqrt(np.mean(y * y, axis=1))
-    with np.errstate(divide="ignore", invalid="ignore"):
-        margin = (top2[:, 1] - top2[:, 0]) / rms
-    return idx.astype(np.int64), margin
+    M = y.shape[0]
+    idx = np.full(M, -1, np.int64)
+    margin = np.full(M, np.nan)
+    for m in range(M):
+        row = y[m]
+        numbers = row[~np.isnan(row)]
+        if numbers.size == 0:
+            continue
+        top = numbers.max()
+        idx[m] = np.flatnonzero(row == top)[0]
+        if numbers.size > 1:
+            second = np.partition(numbers, -2)[-2]
+            with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+                margin[m] = (top - second) / np.sqrt(np.mean(numbers * numbers))
+    return idx, margin
 
 
 def compare(y_test, y_ref):

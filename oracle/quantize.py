@@ -35,15 +35,26 @@ import numpy as np
 from .formats import e2m1_encode, e4m3_encode, e4m3_decode, E2M1_MAX, E4M3_MAX
 
 
-def nvfp4_quantize(w):
-    """w: float32 [K, N] (K % 16 == 0) -> (codes [N][K/2] u8, scales [N][K/16] u8, g float32)."""
+def nvfp4_global_scale(w):
+    """The per-tensor scale g = fp32(amax(|W|) / (6 * 448)) of float32 W."""
+    w = np.asarray(w, dtype=np.float32)
+    amax = float(np.abs(w).max()) if w.size else 0.0      # |float32| is exact in float64
+    return np.float32(amax / (E2M1_MAX * E4M3_MAX))
+
+
+def nvfp4_quantize(w, g=None):
+    """w: float32 [K, N] (K % 16 == 0) -> (codes [N][K/2] u8, scales [N][K/16] u8, g float32).
+
+    g: the per-tensor scale to quantize with; None computes it from w.  Every
+    block depends only on its own 16 values and g, so a column slice of a
+    tensor quantized with the whole tensor's g gives that slice of the whole
+    tensor's codes and scales."""
     w = np.asarray(w, dtype=np.float32)
     K, N = w.shape
     if K % 16:
         raise ValueError("K must be a multiple of 16")
     wt = w.T.astype(np.float64)                      # [N][K], exact widening
-    amax = np.abs(wt).max() if wt.size else 0.0
-    g = np.float32(amax / (E2M1_MAX * E4M3_MAX))
+    g = nvfp4_global_scale(w) if g is None else np.float32(g)
     if g == 0:
         return (np.zeros((N, K // 2), np.uint8), np.zeros((N, K // 16), np.uint8), np.float32(0.0))
     blocks = wt.reshape(N, K // 16, 16)

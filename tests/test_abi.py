@@ -489,3 +489,21 @@ def test_default_kernel_choice_is_always_supported():
                 assert L.fp8_gemm(A, A, A, A, M, K, N, A, big, None) == sk.EHIP, (M, K, N)
                 assert L.lm_head_gemm_argmax(A, A, A, None, M, K, N, A, big, None) == sk.EHIP, (M, K, N)
                 assert L.nvfp4_gemm_swiglu(A, A, A, M, K, N, A, big, None) == sk.EHIP, (M, K, N)
+
+
+def test_default_config_query():
+    """skinny_default_config returns a choice the library supports for the same op, M and K,
+    and rejects bad ops, shapes and NULL outputs before touching them."""
+    for op in (sk.OP_NVFP4, sk.OP_FP8, sk.OP_LM_HEAD, sk.OP_SWIGLU):
+        for M in (1, 2, 4, 8):
+            for K, N in ((256, 512), (5120, 17408), (17408, 5120), (5120, 151936), (1040, 40)):
+                cfg = sk.default_config(op, M, K, N)
+                assert sk.config_supported(op, M, K, N, cfg), (op, M, K, N, cfg)
+                assert sk.workspace_bytes(op, M, K, N, cfg) == sk.workspace_bytes(op, M, K, N)
+    L = lib()
+    v = [ctypes.c_int() for _ in range(4)]
+    refs = [ctypes.byref(c) for c in v]
+    assert L.skinny_default_config(4, 1, 256, 512, *refs) == sk.EINVAL
+    assert L.skinny_default_config(0, 9, 256, 512, *refs) == sk.ESHAPE
+    assert L.skinny_default_config(0, 1, 250, 512, *refs) == sk.ESHAPE
+    assert L.skinny_default_config(0, 1, 256, 512, None, *refs[1:]) == sk.EINVAL

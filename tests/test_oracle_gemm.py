@@ -199,3 +199,92 @@ def test_nvfp4_swiglu_zero_halves():
     zero = oracle.nvfp4_quantize(np.zeros((K, F), np.float32))
     assert np.all(oracle.nvfp4_swiglu(x, zero, up) == 0.0)
     assert np.all(oracle.nvfp4_swiglu(x, gate, zero) == 0.0)
+
+
+def _scan_argmax(row):
+    """Greedy token by a plain scan: skip NaN, keep the first strictly larger logit; -1 if none."""
+    best = -1
+    for n, v in enumerate(row):
+        if v != v:
+            continue
+        if best < 0 or v > row[best]:
+            best = n
+    return best
+
+
+def test_argmax_nan_never_wins():
+    """A NaN logit, whatever its sign bit, is no score: the greedy token is the
+    first maximum of the numbers in the row (+-inf count), and a row with no
+    number at all gives -1."""
+    nan, inf = np.nan, np.inf
+    neg_nan = np.copysign(np.nan, -1.0)
+    assert np.signbit(neg_nan) and not np.signbit(nan)
+    rows = [
+        ([nan, 1.0, neg_nan, 2.0, 2.0], 3),
+        ([nan, nan, nan], -1),
+        ([neg_nan, neg_nan], -1),
+        ([nan, neg_nan, nan, neg_nan], -1),
+        ([nan, -inf, neg_nan], 1),
+        ([inf, nan, inf], 0),
+        ([neg_nan, -inf, -inf], 1),
+        ([nan, -inf, inf, neg_nan, inf], 2),
+        ([-0.0, 0.0, nan], 0),
+        ([neg_nan, -5.0, 7.0, nan, 7.0], 2),
+    ]
+    for row, want in rows:
+        idx, _ = oracle.argmax_rows(np.array([row]))
+        assert idx[0] == want, (row, idx[0], want)
+        assert _scan_argmax(row) == want, row
+
+
+def test_argmax_with_nan_and_inf_matches_scan():
+    """Random rows with NaN of both signs, +-inf and exact ties planted, some
+    rows all NaN: the oracle equals the plain scan in every row."""
+    rng = np.random.default_rng(61)
+    specials = np.array([np.nan, np.copysign(np.nan, -1.0), np.inf, -np.inf])
+    for trial in range(200):
+        M, N = int(rng.integers(1, 9)), int(rng.integers(1, 40))
+        y = rng.integers(-3, 4, size=(M, N)).astype(np.float64)
+        plant = rng.random((M, N)) < rng.random()
+        y[plant] = specials[rng.integers(0, 4, size=int(plant.sum()))]
+        if trial % 7 == 0:
+            y[int(rng.integers(M))] = specials[rng.integers(0, 2, size=N)]   # an all-NaN row
+        idx, margin = oracle.argmax_rows(y)
+        for m in range(M):
+            assert idx[m] == _scan_argmax(list(y[m])), (y[m], idx[m])
+        finite_rows = np.isfinite(y).all(axis=1) & (N > 1)
+        assert np.all(margin[finite_rows] >= 0)
+
+
+def test_gemm_with_non_finite_activations_follows_ieee():
+    """Activations holding +-inf and NaN: the oracle's sums equal a plain
+    Python loop over IEEE doubles (inf * 0 is NaN, inf plus a finite value
+    stays inf, NaN spreads), element by element, NaN where NaN."""
+    K, N = 48, 9
+    w, _ = synth.draw(1, K, N, seed=62)
+    codes, scales, g = oracle.nvfp4_quantize(w)
+    q = oracle.nvfp4_unpack_codes(codes, K)
+    q[::2, 5] = 0                                   # zero codes under the inf of row 0
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    x = np.zeros((4, K), np.float16)
+    x[:] = np.random.default_rng(63).standard_normal((4, K)).astype(np.float16)
+    x[0, 5] = np.inf
+    x[1, K - 1] = -np.inf
+    x[2, 7] = np.nan
+    x[3, 3], x[3, 40] = np.inf, -np.inf
+    y = oracle.nvfp4_gemm(x, codes, scales, g)
+    deq = oracle.nvfp4_dequant_unscaled(codes, scales, K)
+    for m in range(4):
+        for n in range(N):
+            s = 0.0
+            for k in range(K):
+                s += float(x[m, k]) * float(deq[k, n])
+            want = s * float(g)
+            if want != want:
+                assert np.isnan(y[m, n]), (m, n, y[m, n])
+            elif abs(want) == float("inf"):
+                assert y[m, n] == want, (m, n, y[m, n], want)
+            else:
+                assert abs(y[m, n] - want) <= 1e-12 * max(1.0, abs(want)), (m, n)
+    assert np.isnan(y[2]).all()
+    assert np.isnan(y[0, ::2]).all() and np.isinf(y[0, 1::2]).all()

@@ -104,3 +104,18 @@ def test_chunked_draw_equals_one_shot():
     b = synth.draw_weights(rng2, 100, 37, chunk_rows=7)
     xb = synth.draw_activations(rng2, 3, 100)
     assert np.array_equal(a, b) and np.array_equal(xa, xb)
+
+
+def test_nvfp4_column_slices_with_the_whole_tensors_scale():
+    """Blocks depend only on their own 16 values and g: quantizing column
+    slices with the whole tensor's g gives the whole tensor's codes and
+    scales, slice by slice; the slice's own g would differ."""
+    w, _ = synth.draw(1, 256, 300, seed=64)
+    codes, scales, g = oracle.nvfp4_quantize(w)
+    assert g == oracle.nvfp4_global_scale(w)
+    for c0, c1 in ((0, 7), (7, 130), (130, 300)):
+        c, s, g2 = oracle.nvfp4_quantize(np.ascontiguousarray(w[:, c0:c1]), g=g)
+        assert g2 == g
+        assert np.array_equal(c, codes[c0:c1]) and np.array_equal(s, scales[c0:c1])
+    own = oracle.nvfp4_quantize(np.ascontiguousarray(w[:, :7]))
+    assert own[2] != g
