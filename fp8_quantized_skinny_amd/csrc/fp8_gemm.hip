@@ -44,7 +44,7 @@ constexpr int kFp8UnitK = kFp8UnitChunks * kChunkK;  // 512
 static_assert(kFp8UnitK == kFp8PackK && 2 * kFp8UnitChunks * 1024 == kFp8UnitBytes, "FP8 packed unit");
 
 // Read in place of activation pairs past K by the packed VALU engine.
-__device__ const uint32_t kFp8ZeroPair = 0u;
+__device__ uint32_t kFp8ZeroPair = 0u;
 
 struct Fp8Args {
   const uint8_t* w;  // canonical codes [N][K], or the packed units (fp8_pack) of the blob

@@ -104,7 +104,7 @@ struct Plan {
 };
 
 // Read in place of activation pairs past K by the VALU engine.
-__device__ const uint32_t kZeroPair = 0u;
+__device__ uint32_t kZeroPair = 0u;
 
 __device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
