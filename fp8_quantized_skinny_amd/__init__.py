@@ -196,6 +196,27 @@ def nvfp4_gemm(w_packed, x, y, K=None, N=None, workspace=None, stream=None, conf
     return y
 
 
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def nvfp4_gemm_noalloc(w_packed, x, y, K=None, N=None, stream=None):
+    """nvfp4_gemm without a workspace, for callers that cannot allocate: a K split's
+    partial sums go to the library's own device array (NOALLOC_SCRATCH_BYTES per GPU).
+    Calls that overlap in time on one GPU race.  Shapes whose kernel choice needs more
+    scratch raise SkinnyError (ESIZE)."""
+    import torch
+    M, Kx = x.shape
+    K = Kx if K is None else K
+    N = y.shape[-1] if N is None else N
+    _shape_checks(x, M, K, y, N, "y")
+    if w_packed.numel() < packed_bytes(K, N):
+        raise ValueError("w_packed is smaller than the blob for this K, N")
+    wp = _dev(w_packed, torch.uint8, "w_packed")
+    xp, yp = _dev(x, torch.float16, "x"), _dev(y, torch.float16, "y")
+    _check(lib().nvfp4_gemm_noalloc(wp, xp, yp, M, K, N, _stream(stream)), "nvfp4_gemm_noalloc")
+    return y
+
+
 def nvfp4_gemm_swiglu(w_packed, x, h, workspace=None, stream=None, config=None):
     """h[M, F] fp16 = silu(x . Wg~) * (x . Wu~); w_packed: CUDA uint8 blob from nvfp4_pack_swiglu.
 

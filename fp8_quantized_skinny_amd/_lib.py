@@ -22,6 +22,7 @@ def _declare(lib):
         "nvfp4_pack": (c_int, [P, P, c_float, c_int, c_int, P, ctypes.POINTER(c_size_t)]),
         "nvfp4_gemm": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
         "nvfp4_gemm_config": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P, c_int, c_int, c_int, c_int]),
+        "nvfp4_gemm_noalloc": (c_int, [P, P, P, c_int, c_int, c_int, P]),
         "nvfp4_pack_swiglu": (c_int, [P, P, c_float, P, P, c_float, c_int, c_int, P, ctypes.POINTER(c_size_t)]),
         "nvfp4_gemm_swiglu": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P]),
         "nvfp4_gemm_swiglu_config": (c_int, [P, P, P, c_int, c_int, c_int, P, c_size_t, P,
@@ -73,4 +74,4 @@ EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp
             "skinny_config_supported", "skinny_read_probe", "nvfp4_pack_swiglu", "nvfp4_gemm_swiglu",
             "nvfp4_gemm_swiglu_config", "lm_head_verify_greedy", "lm_head_verify_greedy_config",
             "skinny_layers_workspace_bytes", "skinny_layers_run", "fp8_pack", "fp8_gemm_packed",
-            "fp8_gemm_packed_config", "skinny_default_config")
+            "fp8_gemm_packed_config", "skinny_default_config", "nvfp4_gemm_noalloc")

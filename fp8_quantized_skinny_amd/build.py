@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libskinny.so")
-SOURCES = ["host.cpp", "nvfp4_gemm.hip", "fp8_gemm.hip", "reduce.hip", "probe.hip"]
+SOURCES = ["host.cpp", "nvfp4_gemm.hip", "fp8_gemm.hip", "reduce.hip", "probe.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -615,6 +615,23 @@ int nvfp4_gemm_config(const void* w_packed, const uint16_t* x, uint16_t* y, int 
                                     nullptr, workspace, stream));
 }
 
+}  // extern "C"
+
+namespace skinny {
+
+int nvfp4_gemm_host_checks(const void* w_packed, const uint16_t* x, const uint16_t* y, int M, int K, int N,
+                           size_t* workspace_need) {
+  int s = nvfp4_common_checks(w_packed, x, y, M, K, N);
+  if (s) return s;
+  if (!aligned(y, 16)) return SKINNY_EALIGN;
+  *workspace_need = nvfp4_workspace_layout(default_nvfp4_cfg(M, K, N, false), M, K, N, false).total;
+  return SKINNY_OK;
+}
+
+}  // namespace skinny
+
+extern "C" {
+
 int nvfp4_gemm(const void* w_packed, const uint16_t* x, uint16_t* y, int M, int K, int N,
                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int s = check_shape(M, K, N);

@@ -170,6 +170,11 @@ hipError_t launch_finalize_swiglu(const float* part, int ksplit, int M, int N, i
 // Largest row count (the target token plus seven drafts).
 constexpr int kMaxRows = 8;
 
+// Every host-side check of nvfp4_gemm except the workspace's, and the
+// workspace bytes its default kernel choice needs (host.cpp).
+int nvfp4_gemm_host_checks(const void* w_packed, const uint16_t* x, const uint16_t* y, int M, int K, int N,
+                           size_t* workspace_need);
+
 }  // namespace skinny
 
 #endif

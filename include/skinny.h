@@ -137,6 +137,29 @@ int nvfp4_gemm(const void* w_packed, const uint16_t* x, uint16_t* y,
                hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * nvfp4_gemm_noalloc -- nvfp4_gemm for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ *
+ * Same arguments, layouts, kernel choice and results as nvfp4_gemm (bit for
+ * bit), but no workspace: the fp32 partial sums of a K split go to a device
+ * array inside the library of SKINNY_NOALLOC_SCRATCH_BYTES (8 MiB), one per
+ * GPU, held from the first call on that GPU until the process ends.  The call
+ * itself allocates nothing (no hipMalloc, no allocating library routine); the
+ * first call on a device looks the array's address up once.
+ *   Returns SKINNY_ESIZE, before any HIP call, when the library's kernel
+ *   choice for (M, K, N) needs more scratch than that (skinny_workspace_bytes
+ *   (0, M, K, N) > SKINNY_NOALLOC_SCRATCH_BYTES); use nvfp4_gemm with a
+ *   workspace there.  Other errors as nvfp4_gemm.
+ *   Calls that overlap in time on one GPU (two streams, two host threads)
+ *   share the array and race; serialize them.  No byte of the array has to
+ *   start at any value: every call writes the scratch it reads.
+ * ------------------------------------------------------------------------- */
+#define SKINNY_NOALLOC_SCRATCH_BYTES (8u << 20)
+int nvfp4_gemm_noalloc(const void* w_packed, const uint16_t* x, uint16_t* y,
+                       int M, int K, int N, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * nvfp4_gemm_swiglu -- h = silu(x . Wg~) * (x . Wu~), fp16 out.
  *
  *   w_packed  : device, blob from nvfp4_pack_swiglu for exactly this K and F

@@ -507,3 +507,21 @@ def test_default_config_query():
     assert L.skinny_default_config(0, 9, 256, 512, *refs) == sk.ESHAPE
     assert L.skinny_default_config(0, 1, 250, 512, *refs) == sk.ESHAPE
     assert L.skinny_default_config(0, 1, 256, 512, None, *refs[1:]) == sk.EINVAL
+
+
+def test_noalloc_argument_errors_before_any_hip_call():
+    """nvfp4_gemm_noalloc rejects bad arguments, and shapes whose kernel choice
+    needs more scratch than its device array holds, on the host (no GPU here)."""
+    L = lib()
+    assert L.nvfp4_gemm_noalloc(None, A, A, 1, 256, 512, None) == sk.EINVAL
+    assert L.nvfp4_gemm_noalloc(A, A, A, 9, 256, 512, None) == sk.ESHAPE
+    assert L.nvfp4_gemm_noalloc(A, A, A, 1, 250, 512, None) == sk.ESHAPE
+    assert L.nvfp4_gemm_noalloc(A + 8, A, A, 1, 256, 512, None) == sk.EALIGN
+    assert L.nvfp4_gemm_noalloc(A, A, A + 2, 1, 256, 512, None) == sk.EALIGN
+    big = (8, 1 << 20, 4096)
+    assert sk.workspace_bytes(sk.OP_NVFP4, *big) > sk.NOALLOC_SCRATCH_BYTES
+    assert L.nvfp4_gemm_noalloc(A, A, A, *big, None) == sk.ESIZE
+    # the down projection at M = 8 (a nine-way K split) fits
+    assert 0 < sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120) <= sk.NOALLOC_SCRATCH_BYTES
+    if not _has_gpu():      # with a GPU the fake pointers would reach a kernel
+        assert L.nvfp4_gemm_noalloc(A, A, A, 8, 17408, 5120, None) == sk.EHIP
