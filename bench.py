@@ -6,16 +6,21 @@ Metric: effective weight-read bandwidth in GB/s, i.e. compressed weight bytes
 scales) per step divided by the time per step, with every input already
 resident in HBM.  The headline workload is the NVFP4 GEMV at M = 1,
 K = 5120, N = 17408 (an MLP up-projection at decode): one step is one
-nvfp4_gemm call.  The same line also carries the two NVFP4 M = 8 shapes (fused
-gate+up 5120 x 34816 and down 17408 x 5120), the gate+up shape with the
-fused SwiGLU epilogue (nvfp4_gemm_swiglu, h[8, 17408]) and one decoder block's
-four GEMMs in the published FP8/FP4 mix (skinny_layers_run) at M = 8, timed
-the same way.  For the headline and the two plain M = 8 shapes it also reports
-the measured read ceiling: the library's read probe (skinny_read_probe, one
-9 KiB block per wavefront like one packed unit) over the same rotating copies,
-plus the probe over a 2 GiB buffer.
+nvfp4_gemm call.  The same line also carries, timed the same way:
+  * the NVFP4 M = 8 shapes: fused gate+up 5120 x 34816, down 17408 x 5120,
+    and gate+up with the fused SwiGLU epilogue (nvfp4_gemm_swiglu, h[8, 17408]);
+  * the FP8 shapes qkv 5120 x 7168 and o_proj 6144 x 5120 at M = 1, 2 and 4,
+    with canonical codes (fp8_gemm) and packed codes (fp8_gemm_packed);
+  * the 151936-column NVFP4 lm_head with its fused argmax at M = 1 and 8;
+  * one decoder block's four GEMMs in the published FP8/FP4 mix
+    (skinny_layers_run) at M = 8.
+Each shape reports the measured read ceiling at its weight size: the
+library's read probe (skinny_read_probe, one 9 KiB block per single-wavefront
+workgroup, the fastest pattern of the read sweep) over the same rotating
+copies; the headline adds the probe over a 2 GiB buffer.
 
     python bench.py [--steps K] [--warmup W] [--workload up|gate_up|down|qkv|o_proj|lm_head|gate_up_swiglu|lm_head_verify|block|qkv_packed|o_proj_packed] [--M m]
+    python bench.py --read-sweep [--workload up]     every read pattern of skinny_read_probe_pattern
 
 Each step reads a different one of R byte-identical copies of the weights
 (R copies exceed 600 MB) so that the 256 MB Infinity Cache cannot serve them.
@@ -23,10 +28,11 @@ Timing: W eager warm-up steps, then the K steps are captured once into a HIP
 graph, which is replayed untimed for about 0.1 s (GPU clocks settle only
 after tens of milliseconds of work); the timed region is one more replay,
 bracketed by device synchronisation, with a HIP event pair recorded on the
-replay stream.  The
-kernels of a replay run back to back, so the per-launch kernel duration is the
-event time divided by K.  The CPU oracle is timed beside it on the host, on a
-bounded sample of the headline workload.
+replay stream.  The kernels of a replay run back to back, so the per-launch
+kernel duration is the event time divided by K.  Six more replays, timed the
+same way after the timed region, give the spread (p10 / median / p90 of the
+per-step time over the seven replays).  The CPU oracle is timed beside it on
+the host, on a bounded sample of the headline workload.
 """
 
 import argparse
@@ -55,6 +61,8 @@ def parse():
     ap.add_argument("--config", default=None, help="explicit kernel choice engine,ct,nw,ksplit")
     ap.add_argument("--headline-only", action="store_true", help="skip the M = 8 companion shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--read-sweep", action="store_true",
+                    help="only time every read pattern of skinny_read_probe_pattern at the workload's weight size")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run five device-to-device copies of MB megabytes (the known-size "
                          "kernel that scales the HBM byte counters)")
@@ -136,10 +144,12 @@ def recorded_traffic(name, M):
     return None
 
 
-def time_graph(step, steps, stream):
+def time_graph(step, steps, stream, extra=0):
     """Capture `steps` launches of step(i, stream_handle) in a HIP graph, replay it untimed for
     about 0.1 s (clocks and power state settle only after tens of milliseconds of back-to-back
-    kernels), then time one replay with HIP events on `stream`; returns ms for that replay."""
+    kernels), then time one replay with HIP events on `stream` (the timed region).  `extra` more
+    replays are timed the same way afterwards, for the spread.  Returns (ms of the timed replay,
+    [ms of each extra replay])."""
     import torch
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
@@ -153,15 +163,25 @@ def time_graph(step, steps, stream):
         torch.cuda.synchronize()
         if time.perf_counter() - t_warm > 0.1:
             break
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
+    times = []
+    for _ in range(1 + extra):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
     del g
-    return ms
+    return times[0], times[1:]
+
+
+def spread(us_list):
+    """p10 / median / p90 of per-step times (us) over graph replays."""
+    import numpy as np
+    a = np.asarray(us_list, dtype=np.float64)
+    return {"replays": int(a.size), "us_p10": round(float(np.percentile(a, 10)), 3),
+            "us_median": round(float(np.median(a)), 3), "us_p90": round(float(np.percentile(a, 90)), 3)}
 
 
 def probe_size(nbytes, buffers):
@@ -191,10 +211,11 @@ def read_ceiling(copies, nbytes, steps, large=True):
         st = L.skinny_read_probe(copies[i % len(copies)].data_ptr(), probe_bytes, sink.data_ptr(), s)
         if st != 0:
             raise RuntimeError(f"read probe failed: {sk.strerror(st)}")
-    ms = time_graph(step_same, steps, stream)
+    ms, _ = time_graph(step_same, steps, stream)
     same = probe_bytes * steps / (ms * 1e-3) / 1e9
     out = {"same_size_GBs": round(same, 1),
-           "probe": "skinny_read_probe: one 9 KiB block per wavefront, nine 16-byte loads per lane; "
+           "probe": "skinny_read_probe: one 9 KiB block per single-wavefront workgroup, nine 16-byte "
+                    "non-temporal loads per lane (the fastest read pattern of bench.py --read-sweep); "
                     "same rotation of weight copies as the GEMM, HIP-graph replay"}
     log(f"read probe: {same:.1f} GB/s at {nbytes / 1e6:.1f} MB")
     if not large:
@@ -206,7 +227,7 @@ def read_ceiling(copies, nbytes, steps, large=True):
         st = L.skinny_read_probe(big.data_ptr(), big_bytes, sink.data_ptr(), s)
         if st != 0:
             raise RuntimeError(f"read probe failed: {sk.strerror(st)}")
-    ms_big = time_graph(step_big, 20, stream)
+    ms_big, _ = time_graph(step_big, 20, stream)
     large_gbs = big_bytes * 20 / (ms_big * 1e-3) / 1e9
     del big
     log(f"read probe: {large_gbs:.1f} GB/s at 2 GiB")
@@ -214,26 +235,39 @@ def read_ceiling(copies, nbytes, steps, large=True):
     return out
 
 
-def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_probe=False):
-    """Time `steps` launches of one workload; returns (result dict, case or None)."""
-    import numpy as np
-    import torch
-    import fp8_quantized_skinny_amd as sk
+def prepare(name, M=None):
+    """The host case of a workload (seeded draw, library quantizer, packed blob) at its largest M."""
     from fp8_quantized_skinny_amd import workload, synth
-    from fp8_quantized_skinny_amd._lib import lib
-
     fmt, ms, K, N = synth.WORKLOADS[name]
     M = M or max(ms)
     t = time.perf_counter()
     case = (workload.nvfp4_case(M, K, N) if fmt == "nvfp4" else
             workload.swiglu_case(M, K, N) if fmt == "swiglu" else workload.fp8_case(M, K, N))
+    log(f"prepared {name} (M up to {M}, K={K}, N={N}) in {time.perf_counter() - t:.1f} s")
+    return case
+
+
+def measure(name, M, cfg, steps, warmup, case=None, ceiling=False, large_probe=False, extra=6):
+    """Time `steps` launches of one workload at M rows; returns the result dict.
+
+    case: a prepared case of the same workload with at least M rows of x (its
+    leading M rows are used; the weights do not depend on M)."""
+    import numpy as np
+    import torch
+    import fp8_quantized_skinny_amd as sk
+    from fp8_quantized_skinny_amd import synth
+    from fp8_quantized_skinny_amd._lib import lib
+
+    fmt, ms, K, N = synth.WORKLOADS[name]
+    M = M or max(ms)
+    case = case if case is not None else prepare(name, M)
+    assert case["x"].shape[0] >= M
     packed = fmt == "fp8p"
-    log(f"prepared {describe(case, name)} in {time.perf_counter() - t:.1f} s")
     wbytes = case["weight_bytes"]
     R = max(2, math.ceil(MIN_ROTATION_BYTES / wbytes))
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     L = lib()
-    x = dev(case["x"])
+    x = dev(case["x"][:M])
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     idx = torch.empty((M,), dtype=torch.int32, device="cuda")
     if fmt in ("nvfp4", "swiglu"):
@@ -283,19 +317,70 @@ def measure(name, M, cfg, steps, warmup, keep_case=False, ceiling=False, large_p
     torch.cuda.synchronize()
 
     # Timed region: one replay of the K-step graph on `stream`, after untimed replays.
-    gpu_ms = time_graph(step, steps, stream)
+    gpu_ms, more = time_graph(step, steps, stream, extra=extra)
     log(f"{name} M={M}: graph replay {gpu_ms:.3f} ms GPU for {steps} steps")
     us = gpu_ms * 1e3 / steps
     gbs = wbytes / (us * 1e-6) / 1e9
-    res = {"workload": describe(case, name), "M": M, "K": K, "N": N, "weight_bytes": wbytes, "weight_copies": R,
-           "kernel_choice": list(cfg) if cfg else "default", "us_per_step": round(us, 3),
-           "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    res = {"workload": describe(dict(case, M=M), name), "M": M, "K": K, "N": N, "weight_bytes": wbytes,
+           "weight_copies": R, "kernel_choice": list(cfg) if cfg else list(sk.default_config(op, M, K, N)),
+           "us_per_step": round(us, 3), "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    if extra:
+        res["spread"] = spread([t * 1e3 / steps for t in [gpu_ms] + more])
     if ceiling:
         res["read_ceiling"] = read_ceiling(copies, wbytes, steps, large=large_probe)
         res["frac_of_read_ceiling"] = round(gbs / res["read_ceiling"]["same_size_GBs"], 4)
     del copies
     torch.cuda.synchronize()
-    return res, (case if keep_case else None)
+    return res
+
+
+def read_sweep(name, steps):
+    """HBM read rate of each read pattern of skinny_read_probe_pattern at the workload's weight size,
+    over the same rotation of copies as the GEMM (bench.py --read-sweep)."""
+    import ctypes
+    import torch
+    import fp8_quantized_skinny_amd as sk
+    from fp8_quantized_skinny_amd import synth
+    from fp8_quantized_skinny_amd._lib import lib
+    L = lib()
+    fmt, ms, K, N = synth.WORKLOADS[name]
+    ku, nt = -(-K // 1024), -(-N // 16)
+    nbytes = ku * nt * 9216 if fmt == "nvfp4" else K * N
+    R = max(2, math.ceil(MIN_ROTATION_BYTES / nbytes))
+    copies = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    patterns = [("blocks 9 KiB, 1 wavefront per workgroup (skinny_read_probe)", 0, 1, 0),
+                ("blocks 9 KiB, 2 wavefronts per workgroup", 0, 2, 0),
+                ("blocks 9 KiB, 4 wavefronts per workgroup", 0, 4, 0),
+                ("blocks 9 KiB, 8 wavefronts per workgroup", 0, 8, 0),
+                ("blocks 9 KiB, 16 wavefronts per workgroup", 0, 16, 0),
+                ("blocks 4 KiB, 4 wavefronts per workgroup", 1, 4, 0),
+                ("blocks 18 KiB, 2 wavefronts per workgroup", 2, 2, 0),
+                ("blocks 18 KiB, 4 wavefronts per workgroup", 2, 4, 0),
+                (f"tiles of {ku} spans, one workgroup per tile (the NVFP4 GEMV's shape)", 3, ku, 0),
+                ("persistent, 256 workgroups x 4 wavefronts, 2 blocks in flight", 4, 256, 4),
+                ("persistent, 256 workgroups x 8 wavefronts, 2 blocks in flight", 4, 256, 8),
+                ("persistent, 1024 workgroups x 4 wavefronts, 2 blocks in flight", 4, 1024, 4)]
+    out = []
+    for label, pattern, a, b in patterns:
+        if pattern == 3 and not 1 <= a <= 16:
+            continue
+        got = ctypes.c_size_t(0)
+
+        def step(i, s, pattern=pattern, a=a, b=b, got=got):
+            st = L.skinny_read_probe_pattern(copies[i % R].data_ptr(), nbytes, pattern, a, b, sink.data_ptr(),
+                                             ctypes.byref(got), s)
+            if st != 0:
+                raise RuntimeError(f"read probe failed: {sk.strerror(st)}")
+        ms_, more = time_graph(step, steps, stream, extra=4)
+        per = [t * 1e3 / steps for t in [ms_] + more]
+        us = sorted(per)[len(per) // 2]
+        out.append({"pattern": label, "bytes": got.value, "us_median": round(us, 3),
+                    "GB/s": round(got.value / (us * 1e-6) / 1e9, 1)})
+        log(f"read sweep {label}: {us:.3f} us, {out[-1]['GB/s']} GB/s")
+    del copies
+    return {"workload": name, "weight_bytes_per_copy": nbytes, "copies": R, "patterns": out}
 
 
 def measure_block(M, steps, warmup):
@@ -337,14 +422,39 @@ def measure_block(M, steps, warmup):
     for i in range(warmup):
         step(i, stream.cuda_stream)
     torch.cuda.synchronize()
-    gpu_ms = time_graph(step, steps, stream)
+    gpu_ms, more = time_graph(step, steps, stream, extra=6)
     us = gpu_ms * 1e3 / steps
     gbs = wbytes / (us * 1e-6) / 1e9
     log(f"block M={M}: {us:.2f} us per step")
     return {"workload": f"decoder block M={M}: qkv FP8 {Kq}x{Nq}, o_proj FP8 {Ko}x{No} (packed), "
                         f"gate+up NVFP4 SwiGLU {Kg}x2x{F}, down NVFP4 {Kd}x{Nd}",
             "M": M, "weight_bytes": wbytes, "weight_copies": R, "us_per_step": round(us, 3),
-            "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "spread": spread([t * 1e3 / steps for t in [gpu_ms] + more])}
+
+
+def companions(steps, warmup):
+    """The other configurations of the benchmark, timed like the headline: the NVFP4 M = 8
+    shapes, the FP8 shapes at M = 1, 2, 4 (canonical and packed codes) and the lm_head at M = 1
+    and 8, each with the read ceiling at its weight size."""
+    m8 = []
+    for name in ("gate_up", "down", "gate_up_swiglu"):
+        m8.append(measure(name, 8, None, steps, warmup, ceiling=name != "gate_up_swiglu"))
+    fp8 = []
+    for name in ("qkv", "o_proj"):
+        case = prepare(name)
+        for M in (1, 2, 4):
+            for variant in (name, name + "_packed"):
+                fp8.append(measure(variant, M, None, steps, warmup, case=case,
+                                   ceiling=(M == 1 and variant == name)))
+        del case
+    lm = []
+    case = prepare("lm_head")
+    for M in (1, 8):
+        lm.append(measure("lm_head", M, None, max(20, steps // 10), max(2, warmup // 10), case=case,
+                          ceiling=M == 1))
+    del case
+    return m8, fp8, lm
 
 
 def main():
@@ -363,6 +473,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes, "copies": 5}), flush=True)
         return
+    if args.read_sweep:
+        print(json.dumps({"read_sweep": read_sweep(args.workload, args.steps)}), flush=True)
+        return
     if args.workload == "block":
         res = measure_block(args.M or 8, args.steps, args.warmup)
         print(json.dumps({"metric": METRIC, "value": res["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -371,15 +484,12 @@ def main():
                           "data": "synthetic", "config": res}), flush=True)
         return
     cfg = tuple(int(v) for v in args.config.split(",")) if args.config else None
-    head, case = measure(args.workload, args.M, cfg, args.steps, args.warmup,
-                         keep_case=not args.no_cpu_baseline, ceiling=not args.headline_only,
-                         large_probe=True)
-    companions = []
-    block = None
+    case = prepare(args.workload, args.M)
+    head = measure(args.workload, args.M, cfg, args.steps, args.warmup, case=case,
+                   ceiling=not args.headline_only, large_probe=True)
+    m8, fp8, lm, block = [], [], [], None
     if not args.headline_only and args.workload == "up" and cfg is None:
-        for name in ("gate_up", "down", "gate_up_swiglu"):
-            r, _ = measure(name, 8, None, args.steps, args.warmup, ceiling=name != "gate_up_swiglu")
-            companions.append(r)
+        m8, fp8, lm = companions(args.steps, args.warmup)
         block = measure_block(8, args.steps, args.warmup)
     value = head["GB/s"]
     out = {
@@ -395,16 +505,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {**head, "timed": "one HIP-graph replay of K steps, weights rotated over R copies",
-                   "m8_shapes": companions, "decoder_block_m8": block},
+        "config": {**head, "timed": "one HIP-graph replay of K steps, weights rotated over R copies; "
+                                    "spread: that replay and 6 more",
+                   "m8_shapes": m8, "fp8_shapes": fp8, "lm_head_shapes": lm, "decoder_block_m8": block},
         "roofline": {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4),
                      "traffic": None if cfg else recorded_traffic(args.workload, head["M"]),
                      "kernel_us": head["us_per_step"]},
     }
-    if case is not None:
+    if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(case)
+        out["cpu_baseline"] = cpu_baseline(dict(case, x=case["x"][:head["M"]]))
     print(json.dumps(out), flush=True)
 
 

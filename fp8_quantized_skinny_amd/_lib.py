@@ -43,6 +43,7 @@ def _declare(lib):
         "skinny_config_supported": (c_int, [c_int] * 8),
         "skinny_default_config": (c_int, [c_int] * 4 + [ctypes.POINTER(c_int)] * 4),
         "skinny_read_probe": (c_int, [P, c_size_t, P, P]),
+        "skinny_read_probe_pattern": (c_int, [P, c_size_t, c_int, c_int, c_int, P, ctypes.POINTER(c_size_t), P]),
         "nvfp4_quantize": (c_int, [P, c_int, c_int, P, P, ctypes.POINTER(c_float)]),
         "fp8_quantize": (c_int, [P, c_int, c_int, P, P]),
         "skinny_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
@@ -59,9 +60,19 @@ def _declare(lib):
 
 
 def lib():
-    """The loaded library; it is built first only if no built copy exists."""
+    """The loaded library; it is built first only if no built copy exists.
+
+    torch is imported first: PyTorch for ROCm ships its own HIP runtime
+    (libamdhip64), and the library must bind to that same runtime, whose
+    streams and device buffers the binding passes in.  Loaded before torch,
+    the library would pull in the system's runtime, and its launches on
+    torch's streams fail."""
     global _LIB
     if _LIB is None:
+        try:
+            import torch  # noqa: F401
+        except ImportError:       # host-only use (packing, quantizing) without torch
+            pass
         if not os.path.exists(_build.LIB):
             _build.build()
         _LIB = _declare(ctypes.CDLL(_build.LIB))
@@ -74,4 +85,5 @@ EXPORTED = ("nvfp4_pack", "nvfp4_gemm", "fp8_gemm", "lm_head_gemm_argmax", "nvfp
             "skinny_config_supported", "skinny_read_probe", "nvfp4_pack_swiglu", "nvfp4_gemm_swiglu",
             "nvfp4_gemm_swiglu_config", "lm_head_verify_greedy", "lm_head_verify_greedy_config",
             "skinny_layers_workspace_bytes", "skinny_layers_run", "fp8_pack", "fp8_gemm_packed",
-            "fp8_gemm_packed_config", "skinny_default_config", "nvfp4_gemm_noalloc")
+            "fp8_gemm_packed_config", "skinny_default_config", "nvfp4_gemm_noalloc",
+            "skinny_read_probe_pattern")

@@ -43,9 +43,6 @@ constexpr int kFp8UnitChunks = 4;
 constexpr int kFp8UnitK = kFp8UnitChunks * kChunkK;  // 512
 static_assert(kFp8UnitK == kFp8PackK && 2 * kFp8UnitChunks * 1024 == kFp8UnitBytes, "FP8 packed unit");
 
-// Read in place of activation pairs past K by the packed VALU engine.
-__device__ uint32_t kFp8ZeroPair = 0u;
-
 struct Fp8Args {
   const uint8_t* w;  // canonical codes [N][K], or the packed units (fp8_pack) of the blob
   const float* scales;
@@ -456,20 +453,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
   const _Float16* xr[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) xr[m] = a.x + static_cast<size_t>(min(m, a.M - 1)) * a.K;
-  // Activation pairs past K (k even, K % 16 == 0: a pair is all in or all
-  // out) read a zero word, so they add nothing whatever the codes there
-  // (packed: zero; canonical: the row start's) and whatever the row's real
-  // activations hold.
+  // A pair past K reads the last pair of its row (index in [0, K-2], even,
+  // so the 4-byte load stays in the row); below, it is replaced by zero
+  // where that matters.
   if (PACKED) {
     const uint8_t* up = a.w + (static_cast<size_t>(u) * a.nt + tt) * kFp8UnitBytes + P.lane * 16;
 #pragma unroll
     for (int j = 0; j < kFp8UnitChunks; ++j) {
       w[j][0] = load16(up + (2 * j) * 1024);
       w[j][1] = load16(up + (2 * j + 1) * 1024);
-      const int k = kx + j * kChunkK;
 #pragma unroll
       for (int m = 0; m < MR; ++m)
-        xv[j][m] = *(k < a.K ? reinterpret_cast<const uint32_t*>(xr[m] + k) : &kFp8ZeroPair);
+        xv[j][m] = *reinterpret_cast<const uint32_t*>(xr[m] + min(kx + j * kChunkK, a.K - 2));
     }
   } else {
     const int cl = P.lane & 15, grp = P.lane >> 4;
@@ -482,23 +477,33 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
         const int k = k0 + j * kChunkK + 64 * h;
         w[j][h] = load16_shared_line(row + (k + 16 <= a.K ? k : 0));
       }
-      const int k = kx + j * kChunkK;
 #pragma unroll
       for (int m = 0; m < MR; ++m)
-        xv[j][m] = *(k < a.K ? reinterpret_cast<const uint32_t*>(xr[m] + k) : &kFp8ZeroPair);
+        xv[j][m] = *reinterpret_cast<const uint32_t*>(xr[m] + min(kx + j * kChunkK, a.K - 2));
     }
   }
   float acc[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+  const bool straddles = (u + 1) * kFp8UnitK > a.K;
   if (P.active) {
 #pragma unroll
     for (int j = 0; j < kFp8UnitChunks; ++j) {
+      // Canonical codes past K are real codes of the row start: their x pairs
+      // must be zero; selected here, where these x words are needed anyway.
+      // Packed codes past K are zero, but a clamped pair holding inf or NaN
+      // would still give 0 * x = NaN: a unit that straddles K (wave-uniform)
+      // selects too, which no full unit does.
+      const bool in = (!PACKED || straddles) ? kx + j * kChunkK < a.K : true;
+      uint32_t x[MR];
       float p[MR];
 #pragma unroll
-      for (int m = 0; m < MR; ++m) p[m] = 0.0f;
-      fp8_half_dot<MR>(p, xv[j], w[j][0], false);
-      fp8_half_dot<MR>(p, xv[j], w[j][1], true);
+      for (int m = 0; m < MR; ++m) {
+        x[m] = in ? xv[j][m] : 0u;
+        p[m] = 0.0f;
+      }
+      fp8_half_dot<MR>(p, x, w[j][0], false);
+      fp8_half_dot<MR>(p, x, w[j][1], true);
 #pragma unroll
       for (int m = 0; m < MR; ++m) acc[m] = __builtin_fmaf(p[m], sc[j], acc[m]);
     }

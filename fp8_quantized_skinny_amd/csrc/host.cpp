@@ -317,8 +317,40 @@ int skinny_config_supported(int op, int M, int K, int N, int engine, int ct, int
 int skinny_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
   if (!buf || !sink) return SKINNY_EINVAL;
   if (!aligned(buf, 16) || !aligned(sink, 4)) return SKINNY_EALIGN;
-  if (bytes < 9216 || bytes / 9216 > (static_cast<size_t>(1) << 31) * 4) return SKINNY_ESIZE;
+  if (bytes < 9216 || bytes / 9216 >= (static_cast<size_t>(1) << 31)) return SKINNY_ESIZE;
   return launch_status(launch_read_probe(buf, bytes, sink, stream));
+}
+
+int skinny_read_probe_pattern(const void* buf, size_t bytes, int pattern, int a, int b, uint32_t* sink,
+                              size_t* bytes_read, hipStream_t stream) {
+  if (!buf || !sink) return SKINNY_EINVAL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return SKINNY_EALIGN;
+  size_t block = 0, groups = 0, read = 0;
+  switch (pattern) {
+    case 0: case 1: case 2:
+      if (a < 1 || a > kMaxWaves) return SKINNY_EINVAL;
+      block = pattern == 0 ? 9216 : pattern == 1 ? 4096 : 18432;
+      read = bytes / block * block;
+      groups = (bytes / block + a - 1) / a;
+      break;
+    case 3:
+      if (a < 1 || a > kMaxWaves) return SKINNY_EINVAL;
+      block = static_cast<size_t>(a) * kUnitBytes;   // one tile of a spans
+      read = bytes / block * block;
+      groups = bytes / block;
+      break;
+    case 4:
+      if (a < 1 || a > 65535 || b < 1 || b > kMaxWaves) return SKINNY_EINVAL;
+      block = kUnitBytes;
+      read = bytes / block * block;
+      groups = static_cast<size_t>(a);
+      break;
+    default:
+      return SKINNY_EINVAL;
+  }
+  if (read == 0 || groups >= (static_cast<size_t>(1) << 31)) return SKINNY_ESIZE;
+  if (bytes_read) *bytes_read = read;
+  return launch_status(launch_read_probe_pattern(buf, bytes, pattern, a, b, sink, stream));
 }
 
 int skinny_default_config(int op, int M, int K, int N, int* engine, int* ct, int* nw, int* ksplit) {

@@ -142,8 +142,13 @@ constexpr int kMaxStreamSpans = 9;
 size_t nvfp4_stream_lds_bytes(int M, int K, int nw);
 int nvfp4_stream_groups(const LaunchCfg& cfg, int N);
 
-// Read-bandwidth probe (probe.hip): reads bytes / 9216 blocks of 9216 bytes.
+// Read-bandwidth probes (probe.hip).  launch_read_probe reads bytes / 9216
+// blocks of 9216 bytes, one per single-wavefront workgroup; the patterns of
+// launch_read_probe_pattern are those of skinny_read_probe_pattern (skinny.h),
+// with arguments already checked.
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_read_probe_pattern(const void* buf, size_t bytes, int pattern, int a, int b, uint32_t* sink,
+                                     hipStream_t stream);
 
 // Compute units of the current device (256 if it cannot be queried).
 int device_cu_count();

@@ -103,7 +103,8 @@ struct Plan {
   }
 };
 
-// Read in place of activation pairs past K by the VALU engine.
+// Read in place of activation pairs past K by the VALU engine (a global,
+// not a constant, so that both choices of address are global loads).
 __device__ uint32_t kZeroPair = 0u;
 
 __device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
@@ -219,7 +220,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu(Nvfp4Args a) {
     // real pair would turn an inf or NaN at the end of the row into NaN for
     // every column).  Choosing the address rather than selecting zero after
     // the load keeps the loads independent; a select on loaded data made the
-    // first chunk wait for half of the unit's loads.
+    // first chunk wait for half of the unit's loads.  With two rows a
+    // scheduling barrier keeps every load of the unit ahead of the first
+    // conversion (the compiler otherwise held back 9 of the 25 loads, which
+    // cost 0.3 us on a 17408 x 5120 weight); with one row it issues all 17
+    // first by itself, and the barrier measured 0.25 us slower there.
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
       c[j] = load16(p + j * kChunkBytes);
@@ -229,6 +234,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu(Nvfp4Args a) {
         xv[r][j] = *(k < a.K ? reinterpret_cast<const uint32_t*>(a.x + static_cast<size_t>(r) * a.K + k)
                              : &kZeroPair);
     }
+    if constexpr (MR == 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kChunksPerUnit; ++j) {
       const uint32_t sd = dword(sv, j >> 1);

@@ -1,12 +1,22 @@
-// Read-bandwidth probe: the measured HBM read ceiling that the GEMM kernels
+// Read-bandwidth probes: the measured HBM read ceiling that the GEMM kernels
 // are compared with (the author's post rates its kernels against a measured
 // read-only ceiling of its cards, section "What I actually built").
 //
-// Every wavefront reads one 9 KiB block with nine 16-byte loads per lane,
-// issued together, exactly like one NVFP4 unit of the GEMM kernels, and
-// folds the data into one value so that no load can be dropped.  Nothing is
-// written unless the folded value hits a 2^-64 chance, so the probe moves
-// the block bytes and nothing else.
+// Every probe reads whole blocks of 1 KiB per wavefront instruction (one
+// 16-byte non-temporal load per lane, the weight loads of the GEMM kernels)
+// and folds the data into one value so that no load can be dropped.  Nothing
+// is written unless the folded value hits a 2^-64 chance, so a probe moves the
+// bytes it reads and nothing else.  Patterns:
+//   * blocks: every wavefront reads one block of B KiB with B loads issued
+//     together, W wavefronts per workgroup, block order = wavefront order.
+//     B = 9, W = 1 is the default probe: the fastest pattern measured at the
+//     decode sizes (50 MB on MI355X: 8.26 us against 8.43 us for W = 4 and
+//     8.67 us for the GEMV's own shape below).
+//   * tiles: the NVFP4 GEMV's shape: 9 KiB units in span-major order, one
+//     workgroup per 16-column tile with one wavefront per K span.
+//   * persistent: G workgroups of W wavefronts walk the blocks (wavefront w
+//     reads blocks w, w + all wavefronts, ...) with two 9 KiB blocks in
+//     flight each.
 #include <hip/hip_runtime.h>
 
 #include "common.cuh"
@@ -15,30 +25,96 @@
 namespace skinny {
 namespace {
 
-constexpr int kProbeBlock = 9216;
+__device__ __forceinline__ void fold_and_sink(u32x4 h, uint32_t* sink) {
+  const uint64_t lo = static_cast<uint64_t>(h.x) | (static_cast<uint64_t>(h.y) << 32);
+  const uint64_t hi = static_cast<uint64_t>(h.z) | (static_cast<uint64_t>(h.w) << 32);
+  if ((lo ^ hi) == 0x9E3779B97F4A7C15ull) sink[0] = h.x;
+}
 
-__global__ __launch_bounds__(256) void read_probe(const uint8_t* buf, size_t blocks, uint32_t* sink) {
+template <int B>
+__global__ __launch_bounds__(1024) void read_blocks(const uint8_t* buf, size_t blocks, uint32_t* sink) {
   const size_t wave = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   if (wave >= blocks) return;
-  const uint8_t* p = buf + wave * kProbeBlock + (threadIdx.x & 63) * 16;
+  const uint8_t* p = buf + wave * (B * 1024) + (threadIdx.x & 63) * 16;
+  u32x4 v[B];
+#pragma unroll
+  for (int j = 0; j < B; ++j) v[j] = load16(p + j * 1024);
+  u32x4 h = v[0];
+#pragma unroll
+  for (int j = 1; j < B; ++j) h ^= v[j];
+  fold_and_sink(h, sink);
+}
+
+// Tile t of nt, span s = wavefront index: unit (s, t) at (s * nt + t) * 9216.
+__global__ __launch_bounds__(1024) void read_tiles(const uint8_t* buf, int nt, uint32_t* sink) {
+  const uint8_t* p = buf + (static_cast<size_t>(threadIdx.x >> 6) * nt + blockIdx.x) * kUnitBytes +
+                     (threadIdx.x & 63) * 16;
   u32x4 v[9];
 #pragma unroll
   for (int j = 0; j < 9; ++j) v[j] = load16(p + j * 1024);
   u32x4 h = v[0];
 #pragma unroll
   for (int j = 1; j < 9; ++j) h ^= v[j];
-  const uint64_t lo = static_cast<uint64_t>(h.x) | (static_cast<uint64_t>(h.y) << 32);
-  const uint64_t hi = static_cast<uint64_t>(h.z) | (static_cast<uint64_t>(h.w) << 32);
-  if ((lo ^ hi) == 0x9E3779B97F4A7C15ull) sink[0] = h.x;
+  fold_and_sink(h, sink);
+}
+
+// Two blocks in flight per wavefront; past the end a wavefront re-reads its
+// current block (never used), so every address stays inside the blocks.
+__global__ __launch_bounds__(1024) void read_persistent(const uint8_t* buf, size_t blocks, uint32_t* sink) {
+  const size_t W = (static_cast<size_t>(gridDim.x) * blockDim.x) >> 6;
+  const size_t w = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  if (w >= blocks) return;
+  const uint8_t* base = buf + (threadIdx.x & 63) * 16;
+  u32x4 a[9], c[9], h = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 9; ++j) a[j] = load16(base + w * kUnitBytes + j * 1024);
+  for (size_t b = w; b < blocks; b += 2 * W) {
+    const size_t b1 = b + W < blocks ? b + W : b;
+#pragma unroll
+    for (int j = 0; j < 9; ++j) c[j] = load16(base + b1 * kUnitBytes + j * 1024);
+#pragma unroll
+    for (int j = 0; j < 9; ++j) h ^= a[j];
+    const size_t b2 = b + 2 * W < blocks ? b + 2 * W : b;
+#pragma unroll
+    for (int j = 0; j < 9; ++j) a[j] = load16(base + b2 * kUnitBytes + j * 1024);
+#pragma unroll
+    for (int j = 0; j < 9; ++j) h ^= c[j];
+  }
+  fold_and_sink(h, sink);
+}
+
+template <int B>
+void launch_blocks(const uint8_t* buf, size_t bytes, int waves, uint32_t* sink, hipStream_t stream) {
+  const size_t blocks = bytes / (B * 1024);
+  const size_t groups = (blocks + waves - 1) / waves;
+  hipLaunchKernelGGL(read_blocks<B>, dim3(static_cast<unsigned>(groups)), dim3(64 * waves), 0, stream, buf, blocks,
+                     sink);
 }
 
 }  // namespace
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
-  const size_t blocks = bytes / kProbeBlock;
-  const size_t groups = (blocks + 3) / 4;
-  hipLaunchKernelGGL(read_probe, dim3(static_cast<unsigned>(groups)), dim3(256), 0, stream,
-                     static_cast<const uint8_t*>(buf), blocks, sink);
+  launch_blocks<9>(static_cast<const uint8_t*>(buf), bytes, 1, sink, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe_pattern(const void* buf, size_t bytes, int pattern, int a, int b, uint32_t* sink,
+                                     hipStream_t stream) {
+  const uint8_t* p = static_cast<const uint8_t*>(buf);
+  switch (pattern) {
+    case 0: launch_blocks<9>(p, bytes, a, sink, stream); break;
+    case 1: launch_blocks<4>(p, bytes, a, sink, stream); break;
+    case 2: launch_blocks<18>(p, bytes, a, sink, stream); break;
+    case 3: {
+      const int nt = static_cast<int>(bytes / (static_cast<size_t>(a) * kUnitBytes));
+      hipLaunchKernelGGL(read_tiles, dim3(nt), dim3(64 * a), 0, stream, p, nt, sink);
+      break;
+    }
+    case 4:
+      hipLaunchKernelGGL(read_persistent, dim3(a), dim3(64 * b), 0, stream, p, bytes / kUnitBytes, sink);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

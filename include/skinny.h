@@ -405,16 +405,34 @@ size_t skinny_workspace_bytes(int op, int M, int K, int N);
  * skinny_read_probe -- measurement helper, not part of the GEMM path.
  *
  * Reads floor(bytes / 9216) blocks of 9216 bytes of the device buffer `buf`,
- * each by one wavefront with nine 16-byte non-temporal loads per lane (the
- * access shape and cache policy of one NVFP4 unit's loads in the GEMM
- * kernels), and writes nothing else but possibly one word to `sink`
+ * each by one single-wavefront workgroup with nine 16-byte non-temporal loads
+ * per lane (the access shape and cache policy of one NVFP4 unit's loads in
+ * the GEMM kernels), and writes nothing else but possibly one word to `sink`
  * (device, 4 bytes).  Timing it gives the HBM read ceiling that the GEMM
  * kernels are rated against (the post, section "What I actually built",
- * rates its kernels against a measured read-only ceiling).  Asynchronous on
- * `stream`.  SKINNY_ESIZE if bytes < 9216.
+ * rates its kernels against a measured read-only ceiling); of the patterns
+ * below it was the fastest at the decode sizes.  Asynchronous on `stream`.
+ * SKINNY_ESIZE if bytes < 9216 or the buffer holds 2^31 blocks or more.
  * ------------------------------------------------------------------------- */
 int skinny_read_probe(const void* buf, size_t bytes, uint32_t* sink,
                       hipStream_t stream);
+
+/* skinny_read_probe_pattern -- the same probe in other read patterns, to
+ * measure which read shape the memory system serves fastest (measurement
+ * only).  Reads whole blocks inside [buf, buf + bytes) and writes the number
+ * of bytes read to *bytes_read (host pointer, may be NULL).
+ *   pattern 0, 1, 2: blocks of 9, 4 or 18 KiB, one per wavefront, all its
+ *                    loads issued together; a = wavefronts per workgroup
+ *                    (1..16); b unused
+ *   pattern 3: the NVFP4 GEMV's shape: 9 KiB units in span-major order of
+ *              a K spans (1..16), one workgroup of a wavefronts per tile
+ *   pattern 4: a workgroups (1..65535) of b wavefronts (1..16) walk the
+ *              9 KiB blocks, two blocks in flight per wavefront
+ * SKINNY_EINVAL for a bad pattern, a or b; SKINNY_ESIZE if not one block
+ * fits. */
+int skinny_read_probe_pattern(const void* buf, size_t bytes, int pattern,
+                              int a, int b, uint32_t* sink, size_t* bytes_read,
+                              hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* skinny_strerror(int status);
