@@ -414,7 +414,7 @@ def measure_block(M, steps, warmup):
     xs = [dev(c["x"]) for c in (qkv, o, gu, dn)]
     ys = [torch.empty((M, n), dtype=torch.float16, device="cuda") for n in (Nq, No, F, Nd)]
     n = sk.layers_workspace_bytes(tables[0], M)
-    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(i, s):

@@ -89,6 +89,21 @@ def _workspace(workspace, need, where):
     return _dev(workspace, torch.uint8, "workspace"), workspace.numel()
 
 
+def new_workspace(nbytes, fill=None, device=None):
+    """A device workspace of nbytes (None if nbytes is 0), ready for its first call: its leading
+    WORKSPACE_SYNC_BYTES are zero (the arrival counters of the in-kernel K-split reduction, which
+    every call leaves zero).  fill: byte value for the rest (default zero); calls write every other
+    byte they read, so any value works there."""
+    import torch
+    if not nbytes:
+        return None
+    if fill is None:
+        return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")
+    ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=device or "cuda")
+    ws[:WORKSPACE_SYNC_BYTES].zero_()
+    return ws
+
+
 def strerror(status):
     return lib().skinny_strerror(status).decode()
 
@@ -197,6 +212,7 @@ def nvfp4_gemm(w_packed, x, y, K=None, N=None, workspace=None, stream=None, conf
 
 
 NOALLOC_SCRATCH_BYTES = 8 << 20
+WORKSPACE_SYNC_BYTES = 128 << 10   # the leading bytes of a workspace that must be zero before its first use
 
 
 def nvfp4_gemm_noalloc(w_packed, x, y, K=None, N=None, stream=None):

@@ -234,13 +234,27 @@ Geometry nvfp4_geometry(int K, int N) {
   return g;
 }
 
-// Partial sums of a K split: fp32 part[split][m][n] for the M real rows.
-// Argmax candidates: one 64-bit key per row for each workgroup of the GEMM
-// kernel (no split) or each column block of the split reduction.
+bool nvfp4_uses_xsplit(const LaunchCfg& cfg, int N, bool plain_epilogue) {
+  const int nt = (N + kTileCols - 1) / kTileCols;
+  // The reduction's buffer offsets, up to (ksplit + 16) blocks of at most
+  // 8 rows x ct tiles of fp32, stay far inside an int.
+  const int64_t reach = static_cast<int64_t>(cfg.ksplit + 16) * 8 * cfg.ct * kTileCols * 4;
+  return cfg.engine == 1 && cfg.ksplit > 1 && plain_epilogue && (nt + cfg.ct - 1) / cfg.ct <= kMaxSyncGroups &&
+         reach < (int64_t{1} << 30);
+}
+
+// Partial sums of a K split: fp32, ksplit x M x (the tiles' columns) for the
+// M real rows, laid out [split][m][n] for the split reduction kernel or in one
+// [m][column] block per (tile group, split) for the in-kernel reduction; the
+// size covers both.  Argmax candidates: one 64-bit key per row for each
+// workgroup of the GEMM kernel (no split) or each column block of the split
+// reduction.
 WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N, bool argmax) {
   const Geometry g = nvfp4_geometry(K, N);
   WorkspaceLayout w{};
-  size_t off = 0;
+  if (!argmax && cfg.ksplit == 1) return w;
+  size_t off = kSyncBytes;
+  w.sync_bytes = kSyncBytes;
   if (argmax) {
     const size_t groups = cfg.engine == 2 ? kMaxStreamGroups
                           : cfg.ksplit > 1 ? finalize_groups(N) : (g.nt + cfg.ct - 1) / cfg.ct;
@@ -249,8 +263,10 @@ WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N
     off = align256(off + w.keys_bytes);
   }
   if (cfg.ksplit > 1) {
+    const size_t cols = std::max(static_cast<size_t>(N),
+                                 static_cast<size_t>((g.nt + cfg.ct - 1) / cfg.ct) * cfg.ct * kTileCols);
     w.part_off = off;
-    w.part_bytes = static_cast<size_t>(cfg.ksplit) * M * N * 4;
+    w.part_bytes = static_cast<size_t>(cfg.ksplit) * M * cols * 4;
     off = align256(off + w.part_bytes);
   }
   w.total = off;
@@ -260,12 +276,12 @@ WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N
 WorkspaceLayout fp8_workspace_layout(const LaunchCfg& cfg, int M, int K, int N) {
   (void)K;
   WorkspaceLayout w{};
-  size_t off = 0;
-  if (cfg.ksplit > 1) {
-    w.part_off = off;
-    w.part_bytes = static_cast<size_t>(cfg.ksplit) * M * N * 4;
-    off = align256(off + w.part_bytes);
-  }
+  if (cfg.ksplit == 1) return w;
+  size_t off = kSyncBytes;
+  w.sync_bytes = kSyncBytes;
+  w.part_off = off;
+  w.part_bytes = static_cast<size_t>(cfg.ksplit) * M * N * 4;
+  off = align256(off + w.part_bytes);
   w.total = off;
   return w;
 }

@@ -110,14 +110,24 @@ struct LaunchCfg {
 constexpr int kMaxWaves = 16;
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 
-// Workspace of one call (offsets in bytes, 256-aligned): argmax candidate
-// keys (lm_head) and the fp32 partial sums part[split][m][n] of a K split.
-// Every byte is written by the call before it is read, so no initialisation
-// is needed.
+// Workspace of one call (offsets in bytes, 256-aligned).  Every workspace
+// that is not empty starts with the same kSyncBytes: arrival counters of the
+// in-kernel K-split reduction, one per tile group and 128 bytes apart (a
+// cache line each).  They must be zero before a workspace's first use, and
+// every call leaves them zero; no other data is ever placed there, so one
+// workspace can serve calls of every kind.  After them: argmax candidate
+// keys (lm_head) and the fp32 partial sums of a K split.  Those are written
+// by the call before they are read, so they need no initialisation.
+constexpr int kMaxSyncGroups = 1024;
+constexpr size_t kSyncLineBytes = 128;
+constexpr size_t kSyncBytes = kMaxSyncGroups * kSyncLineBytes;
 struct WorkspaceLayout {
-  size_t keys_off, keys_bytes, part_off, part_bytes, total;
+  size_t sync_off, sync_bytes, keys_off, keys_bytes, part_off, part_bytes, total;
 };
 WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N, bool argmax);
+// True when an NVFP4 call with this choice adds its K split inside the GEMM
+// kernel (the MFMA engine, plain epilogue, at most kMaxSyncGroups tile groups).
+bool nvfp4_uses_xsplit(const LaunchCfg& cfg, int N, bool plain_epilogue);
 WorkspaceLayout fp8_workspace_layout(const LaunchCfg& cfg, int M, int K, int N);
 
 // Kernel launchers (defined in the .hip files).  Arguments are validated.

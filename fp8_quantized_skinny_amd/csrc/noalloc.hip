@@ -9,8 +9,12 @@
 // host that name is only a stand-in): the first call on each device looks up
 // the device address with hipGetSymbolAddress, with that device current, and
 // every call on the device passes that address.  Calls that overlap in time
-// on one GPU share the array and race; the kernels write every scratch byte
-// they read within a call, so nothing has to start at zero.
+// on one GPU share the array and race.  The array's first
+// SKINNY_WORKSPACE_SYNC_BYTES hold the K split's arrival counters, which must
+// be zero when a call starts and are zero again when it ends; the first call
+// on each device clears them with a small kernel on its stream (static
+// storage starts zeroed as well).  The kernels write every other scratch byte
+// they read within a call.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -27,14 +31,26 @@ constexpr int kMaxDevices = 64;
 std::mutex g_mutex;
 void* g_scratch[kMaxDevices];  // device address of `scratch`, per device (null until looked up)
 
-// This device's address of `scratch` (looked up once per device).
-int scratch_address(void** out) {
+static_assert(SKINNY_WORKSPACE_SYNC_BYTES % 4 == 0 && SKINNY_WORKSPACE_SYNC_BYTES <= kScratchBytes, "sync region");
+
+__global__ void clear_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// This device's address of `scratch`, looked up (and its counters cleared on
+// `stream`) on the first call on the device.
+int scratch_address(void** out, hipStream_t stream) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SKINNY_EHIP;
   std::lock_guard<std::mutex> lock(g_mutex);
   if (!g_scratch[dev]) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SKINNY_EHIP;
+    constexpr int kWords = SKINNY_WORKSPACE_SYNC_BYTES / 4;
+    hipLaunchKernelGGL(clear_words, dim3((kWords + 255) / 256), dim3(256), 0, stream, static_cast<uint32_t*>(p),
+                       kWords);
+    if (hipGetLastError() != hipSuccess) return SKINNY_EHIP;
     g_scratch[dev] = p;
   }
   *out = g_scratch[dev];
@@ -51,7 +67,7 @@ extern "C" int nvfp4_gemm_noalloc(const void* w_packed, const uint16_t* x, uint1
   if (s) return s;
   if (need > kScratchBytes) return SKINNY_ESIZE;
   void* ws = nullptr;
-  s = scratch_address(&ws);
+  s = scratch_address(&ws, stream);
   if (s) return s;
   return nvfp4_gemm(w_packed, x, y, M, K, N, ws, kScratchBytes, stream);
 }

@@ -60,10 +60,14 @@ struct Nvfp4Args {
   _Float16* y;
   int M, K, N;
   int ku, nt, ksplit, S;     // S: K spans per workgroup
-  float* part;               // [ksplit][M][N] fp32 partial sums (ksplit > 1)
+  float* part;               // fp32 partial sums of a K split (ksplit > 1): [ksplit][M][N], or with
+                             // xsplit one block [M][ct * 16] per (tile group, split)
   unsigned long long* cand;  // [gridDim.x][M] argmax candidates (lm_head, ksplit == 1)
   const float* g2ptr;        // SwiGLU pair: the up projection's scale
   int F;                     // SwiGLU pair: output columns (y is h[M][F])
+  int xsplit;                // 1: the K split is added inside the kernel on each tile group's XCD
+  int ntg;                   // tile groups (xsplit)
+  unsigned* sync;            // xsplit: one arrival counter per tile group, 128 bytes apart (zero at rest)
 };
 
 // What a kernel does with its finished fp32 tile sums.
@@ -79,17 +83,35 @@ __device__ __forceinline__ float swiglu_pair(float sum, float g, float g2) {
 }
 
 // This wavefront's unit and its workgroup's geometry (wave-uniform values).
+// Workgroup b of an xsplit grid (1-D, 8 * ceil(ntg / 8) * ksplit workgroups)
+// takes tile group 8 * (b / (8 * ksplit)) + b % 8 and split (b % (8 * ksplit))
+// / 8: the splits of a tile group are workgroups congruent mod 8, which the
+// hardware dispatches to one XCD (it deals the workgroups of a kernel to the
+// 8 XCDs in turn), so they share that XCD's L2.
+__device__ __forceinline__ void xsplit_place(int b, int ksplit, int& group, int& split) {
+  const int per = 8 * ksplit;
+  group = (b / per) * 8 + (b & 7);
+  split = (b % per) >> 3;
+}
+
 struct Plan {
   int lane, wave, nw, S, tile0, s0, sw;  // sw: spans in this split
   int t, s;                              // local tile and span of this wavefront's unit
+  int group, split;                      // tile group and K split of this workgroup
   bool active;
   __device__ Plan(const Nvfp4Args& a, int ct) {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     nw = blockDim.x >> 6;
     S = a.S;
-    tile0 = blockIdx.x * ct;
-    s0 = blockIdx.y * S;
+    if (a.xsplit) {
+      xsplit_place(blockIdx.x, a.ksplit, group, split);
+    } else {
+      group = blockIdx.x;
+      split = blockIdx.y;
+    }
+    tile0 = group * ct;
+    s0 = split * S;
     sw = min(S, a.ku - s0);
     t = wave / S;
     s = wave % S;
@@ -102,6 +124,53 @@ struct Plan {
     return a.units + (static_cast<size_t>(s0 + s) * a.nt + tt) * kUnitBytes + lane * 16;
   }
 };
+
+// The end of an xsplit workgroup: its partial sums of tile group P.group,
+// already stored to the group's block for split P.split, are published with
+// an arrival count on the group's counter; the workgroup that arrives last
+// (all splits of the group run on one XCD, so plain stores, an atomic in that
+// XCD's L2 and loads that skip the CU's L1 see each other) adds the ksplit
+// blocks in split order, scales by g and writes y.  It then sets the counter
+// back to zero for the next call.  Nothing waits on another workgroup, and the
+// order of the sums does not depend on which split arrives last.
+// Every thread of the workgroup must call this.
+template <int CT>
+__device__ void xsplit_finish(const Nvfp4Args& a, const Plan& P) {
+  constexpr int kCols = CT * kTileCols;
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have reached L2
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* cnt = a.sync + static_cast<size_t>(P.group) * 32;
+    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    last = old == static_cast<unsigned>(a.ksplit - 1);
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __syncthreads();
+  if (!last) return;
+  const size_t block = static_cast<size_t>(a.M) * kCols;
+  const float* base = a.part + static_cast<size_t>(P.group) * a.ksplit * block;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(base), 0, static_cast<int>(a.ksplit * block * sizeof(float)), 0x00020000);
+  const float g = *a.gptr;
+  for (int o = threadIdx.x; o < static_cast<int>(block); o += blockDim.x) {
+    const int m = o / kCols, n = P.tile0 * kTileCols + o % kCols;
+    // Sixteen splits per batch, all loads issued before the first add; a
+    // split past the last reads 0 (outside the buffer's range) and adds 0.
+    constexpr int kBatch = 16;
+    float sum = 0.0f;
+    for (int k0 = 0; k0 < a.ksplit; k0 += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)  // sc0: past this CU's L1, from the XCD's L2
+        v[i] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, static_cast<int>(((k0 + i) * block + o) * 4), 0, 1));
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) sum += v[i];
+    }
+    if (n < a.N) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(g * sum);
+  }
+}
 
 // Read in place of activation pairs past K by the VALU engine (a global,
 // not a constant, so that both choices of address are global loads).
@@ -284,7 +353,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu(Nvfp4Args a) {
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
         if (a.ksplit > 1)
-          a.part[(static_cast<size_t>(blockIdx.y) * MR + r) * a.N + n] = tot[r];
+          a.part[(static_cast<size_t>(P.split) * MR + r) * a.N + n] = tot[r];
         else if (EPI != kEpiArgmax || a.y)  // the lm_head's logits are optional
           a.y[static_cast<size_t>(r) * a.N + n] = static_cast<_Float16>(*a.gptr * tot[r]);
       }
@@ -377,6 +446,7 @@ template <int CT, int EPI>
 __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const Plan P(a, CT);
+  if (a.xsplit && P.group >= a.ntg) return;  // grid rounding to whole groups of 8 (uniform)
   _Float16* xs = reinterpret_cast<_Float16*>(lds);
   f32x4* red = reinterpret_cast<f32x4*>(lds + ((a.M * xs_stride(P.S) * 2 + 15) & ~15));  // [nw][32]
 
@@ -414,12 +484,24 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
   f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
   if (fin)
     for (int s = 0; s < P.sw; ++s) tot += red[(P.wave * P.S + s) * 32 + P.lane];
+  if (a.ksplit > 1 && a.xsplit) {  // this split's block of the group; the last split adds them
+    if (fin) {
+      float* blk = a.part + (static_cast<size_t>(P.group) * a.ksplit + P.split) * a.M * (CT * kTileCols);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = grp * 4 + i;
+        if (m < a.M) blk[m * (CT * kTileCols) + P.wave * kTileCols + cl] = tot[i];
+      }
+    }
+    xsplit_finish<CT>(a, P);
+    return;
+  }
   if (a.ksplit > 1) {  // this split's partial sums; the split reduction finishes
     if (fin && n < a.N) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = grp * 4 + i;
-        if (m < a.M) a.part[(static_cast<size_t>(blockIdx.y) * a.M + m) * a.N + n] = tot[i];
+        if (m < a.M) a.part[(static_cast<size_t>(P.split) * a.M + m) * a.N + n] = tot[i];
       }
     }
     return;
@@ -735,7 +817,7 @@ hipError_t launch_gemm(const Nvfp4Args& a, const LaunchCfg& cfg, int epi, hipStr
         return hipErrorInvalidValue;
     }
   }
-  const dim3 grid((a.nt + cfg.ct - 1) / cfg.ct, cfg.ksplit);
+  const dim3 grid = a.xsplit ? dim3(8 * ((a.ntg + 7) / 8) * cfg.ksplit) : dim3((a.nt + cfg.ct - 1) / cfg.ct, cfg.ksplit);
   const size_t lds = nvfp4_mfma_lds_bytes(a.M, a.S, cfg.nw);
   SKINNY_NVFP4_DISPATCH(1)
   SKINNY_NVFP4_DISPATCH(2)
@@ -772,8 +854,11 @@ hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y, int
   a.g2ptr = reinterpret_cast<const float*>(blob + kG2Offset);
   a.F = swiglu_F;
   const bool swiglu = swiglu_F > 0;
+  a.xsplit = nvfp4_uses_xsplit(cfg, N, !argmax && !swiglu) ? 1 : 0;
+  a.ntg = (geo.nt + cfg.ct - 1) / cfg.ct;
+  a.sync = reinterpret_cast<unsigned*>(ws + wl.sync_off);
   hipError_t e = launch_gemm(a, cfg, argmax ? kEpiArgmax : swiglu ? kEpiSwiglu : kEpiPlain, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.xsplit) return e;
   int groups = cfg.engine == 2 ? nvfp4_stream_groups(cfg, N) : (geo.nt + cfg.ct - 1) / cfg.ct;
   if (cfg.ksplit > 1 && swiglu)
     return launch_finalize_swiglu(a.part, cfg.ksplit, M, N, swiglu_F, a.gptr, a.g2ptr, y, stream);

@@ -63,6 +63,17 @@ enum {
 /* Largest supported row count: the target token plus seven drafts. */
 #define SKINNY_MAX_M 8
 
+/* Workspaces.  A call that needs one (skinny_workspace_bytes > 0) takes a
+ * caller-owned device buffer.  Its first SKINNY_WORKSPACE_SYNC_BYTES bytes
+ * hold the arrival counters with which the GEMM kernel adds a K split on
+ * each tile group's XCD (the splits of a group run on one XCD and meet in
+ * its L2), so they must be zero before the workspace's first use
+ * (hipMemset once after allocating); every call leaves them zero, and no call
+ * stores anything else there, so one workspace may serve calls of every kind.
+ * The rest may hold anything: the call writes every other byte it reads.
+ * Calls that share one workspace must not overlap in time. */
+#define SKINNY_WORKSPACE_SYNC_BYTES (128u << 10)
+
 /* ---------------------------------------------------------------------------
  * nvfp4_pack -- lay NVFP4 codes and scales out for 128-bit coalesced loads.
  *
@@ -127,9 +138,10 @@ int nvfp4_pack_swiglu(const uint8_t* gate_codes, const uint8_t* gate_scales,
  *   y         : device, fp16 [M][N] row-major (written, never read).
  *   M         : 1..8.
  *   workspace : device scratch buffer of at least
- *               skinny_workspace_bytes(0, M, K, N) bytes (any contents; the
- *               call writes every byte it reads).  May be NULL when that size
- *               is 0.  Calls that share one workspace must not overlap in time.
+ *               skinny_workspace_bytes(0, M, K, N) bytes (see "Workspaces":
+ *               its first SKINNY_WORKSPACE_SYNC_BYTES zero at rest, the rest
+ *               any contents).  May be NULL when that size is 0.  Calls that
+ *               share one workspace must not overlap in time.
  *   stream    : HIP stream the kernel is enqueued on (0 = null stream).
  * ------------------------------------------------------------------------- */
 int nvfp4_gemm(const void* w_packed, const uint16_t* x, uint16_t* y,
@@ -168,7 +180,7 @@ int nvfp4_gemm_noalloc(const void* w_packed, const uint16_t* x, uint16_t* y,
  *   x, M      : as for nvfp4_gemm.
  *   h         : device, fp16 [M][F] row-major (written, never read).
  *   workspace : scratch of at least skinny_workspace_bytes(3, M, K, F) bytes
- *               (any contents; calls sharing one must not overlap in time).
+ *               (as for nvfp4_gemm).
  *
  * Both projections are accumulated in fp32 and scaled by their own g; the
  * activation is applied to those fp32 values in fp32, and only h is rounded
@@ -227,8 +239,7 @@ int fp8_gemm_packed(const void* w_packed, const float* block_scales,
  *               comparison uses the fp32 logits before any fp16 rounding.
  *   logits    : device fp16 [M][N] or NULL (then no logits are written).
  *   workspace : scratch of at least skinny_workspace_bytes(2, M, K, N) bytes
- *               (any contents).  Calls that share one workspace must not
- *               overlap in time.
+ *               (as for nvfp4_gemm).
  * ------------------------------------------------------------------------- */
 int lm_head_gemm_argmax(const void* w_packed, const uint16_t* x, int32_t* idx,
                         uint16_t* logits, int M, int K, int N, void* workspace,
@@ -342,7 +353,10 @@ int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales);
  *            (engine 2: always 1).
  *            With ksplit > 1 each workgroup stores fp32 partial sums in
  *            the workspace (size from skinny_workspace_bytes_config for the
- *            same choice) and a second kernel adds them in split order
+ *            same choice) and they are added in split order: by the last
+ *            split to arrive, on the tile group's XCD, for plain NVFP4 calls
+ *            on engine 1; by a second kernel otherwise (engine 0, FP8,
+ *            SwiGLU pairs, the lm_head).
  * A combination that is not built (or whose LDS need exceeds the CU)
  * returns SKINNY_EINVAL.
  * ------------------------------------------------------------------------- */

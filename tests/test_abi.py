@@ -215,11 +215,17 @@ def test_workspace_sizes():
     assert sk.workspace_bytes(sk.OP_FP8, 4, 5120, 7168, (1, 1, 10, 1)) == 0
     # argmax: one 64-bit candidate per workgroup and row
     assert sk.workspace_bytes(sk.OP_LM_HEAD, 8, 5120, 151936, (1, 1, 5, 1)) >= 9496 * 8 * 8
+    # every workspace that is not empty starts with the 128 KiB of arrival counters
+    SYNC = sk.WORKSPACE_SYNC_BYTES
+    assert SYNC == 1024 * 128
     # K split: fp32 partials of every split, row and column
-    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 2, 10, 4)) == 4 * 8 * 5120 * 4
-    assert sk.workspace_bytes(sk.OP_FP8, 3, 6144, 5120, (1, 1, 4, 3)) == 3 * 3 * 5120 * 4
+    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 2, 10, 4)) == SYNC + 4 * 8 * 5120 * 4
+    assert sk.workspace_bytes(sk.OP_FP8, 3, 6144, 5120, (1, 1, 4, 3)) == SYNC + 3 * 3 * 5120 * 4
+    # columns rounded up to whole tile groups for the in-kernel split (2 groups of 4 tiles for 100 columns)
+    assert sk.workspace_bytes(sk.OP_NVFP4, 8, 2048, 100, (1, 4, 4, 2)) == SYNC + 2 * 8 * 128 * 4
     # K split with argmax: candidates of each 256-column block of the split reduction, then the partials
-    assert sk.workspace_bytes(sk.OP_LM_HEAD, 2, 5120, 1000, (1, 1, 1, 5)) == 256 + 40192   # 40000 rounded up to 256
+    # (partials of 5 x 2 x 1008 columns: 63 whole tiles; 40320 rounded up to 256)
+    assert sk.workspace_bytes(sk.OP_LM_HEAD, 2, 5120, 1000, (1, 1, 1, 5)) == SYNC + 256 + 40448
     # spans that do not cover K, or a split that leaves a workgroup without spans, are unsupported
     assert sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 2, 4, 4)) == 0
     assert sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 1, 9, 2)) > 0

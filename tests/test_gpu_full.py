@@ -49,7 +49,7 @@ def _log(msg):
 def _ws(op, M, K, N, cfg=None):
     """Junk-filled workspace for a kernel choice (None if none is needed)."""
     n = sk.workspace_bytes(op, M, K, N, cfg)
-    return torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
+    return sk.new_workspace(n, fill=0xA5)
 
 
 def _whole(got, ref, what):

@@ -36,7 +36,7 @@ def dev(a):
 
 def _ws(op, M, K, N, config=None):
     n = sk.workspace_bytes(op, M, K, N, config)
-    return torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
+    return sk.new_workspace(n, fill=0xA5)
 
 
 def _check(got, ref, what):

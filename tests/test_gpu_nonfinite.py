@@ -97,11 +97,11 @@ def _lm_head(case, rows, cfg):
     idx = torch.full((M,), -7, dtype=torch.int32, device="cuda")
     lg = torch.empty((M, N), dtype=torch.float16, device="cuda")
     n = sk.workspace_bytes(sk.OP_LM_HEAD, M, K, N, cfg)
-    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
+    ws = sk.new_workspace(n, fill=0xA5)
     sk.lm_head_gemm_argmax(dev(case["blob"]), dev(case["x"][rows]), idx, N, logits=lg, workspace=ws, config=cfg)
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     n = sk.workspace_bytes(sk.OP_NVFP4, M, K, N, cfg)
-    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
+    ws = sk.new_workspace(n, fill=0xA5)
     sk.nvfp4_gemm(dev(case["blob"]), dev(case["x"][rows]), y, workspace=ws, config=cfg)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), lg.float().cpu().numpy(), y.float().cpu().numpy()

@@ -52,7 +52,7 @@ def stream_cfgs(op, M, K, N):
 def ws_for(op, M, K, N, config):
     """Workspace for a call, filled with junk: the library must not rely on its contents."""
     n = sk.workspace_bytes(op, M, K, N, config)
-    return torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
+    return sk.new_workspace(n, fill=0xA5)
 
 
 def dev(a):
@@ -451,7 +451,7 @@ def test_layer_table_mixed_allocation():
         xs = [dev(c["x"][:M]) for c in (nv, f8, sw, dn, f8b, f8b)]
         ys = [torch.full((M, l[4]), float("nan"), dtype=torch.float16, device="cuda") for l in layers]
         n = sk.layers_workspace_bytes(layers, M)
-        ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
+        ws = sk.new_workspace(n, fill=0xA5)
         sk.layers_run(layers, xs, ys, workspace=ws)
         torch.cuda.synchronize()
         for i, (y, ref) in enumerate(zip(ys, refs)):
@@ -465,7 +465,7 @@ def test_layer_table_mixed_allocation():
     out = torch.empty((4, 384), dtype=torch.float16, device="cuda")
     n = sk.layers_workspace_bytes(chain, 4)
     sk.layers_run(chain, [dev(a["x"]), mid], [mid, out],
-                  workspace=torch.empty(n, dtype=torch.uint8, device="cuda") if n else None)
+                  workspace=sk.new_workspace(n))
     torch.cuda.synchronize()
     _check(mid.float().cpu().numpy(), ref_nvfp4(a), "chain layer 0")
     _check(out.float().cpu().numpy(), oracle.fp8_gemm(mid.cpu().numpy(), b["codes"], b["scales"]), "chain layer 1")
@@ -508,7 +508,7 @@ def test_hip_graph_replays_match_eager():
         "sw_split": (sk.OP_SWIGLU, 8, 2064, 72, split), "lm": (sk.OP_LM_HEAD, 8, 1024, 3000, None),
         "lmv": (sk.OP_LM_HEAD, 8, 1024, 3000, None), "f8p": (sk.OP_FP8, 4, 1040, 640, f8split)}.items()}
     n_layers = sk.layers_workspace_bytes(layers, 4)
-    wss["layers"] = torch.empty(n_layers, dtype=torch.uint8, device="cuda") if n_layers else None
+    wss["layers"] = sk.new_workspace(n_layers)
     assert wss["nv_split"] is not None and wss["f8"] is not None and wss["sw_split"] is not None
     assert sk.config_supported(sk.OP_NVFP4, 8, 2064, 1000, split) and sk.config_supported(sk.OP_SWIGLU, 8, 2064, 72, split)
     assert sk.config_supported(sk.OP_FP8, 4, 1040, 640, f8split)
@@ -547,7 +547,7 @@ def test_hip_graph_replays_match_eager():
             v.fill_(-1) if v.dtype == torch.int32 else v.fill_(float("nan"))
         for w in wss.values():
             if w is not None:
-                w.fill_(0x5A)
+                w[sk.WORKSPACE_SYNC_BYTES:].fill_(0x5A)   # the counters stay zero at rest
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()

@@ -28,7 +28,7 @@ def _with_workspace(case, M):
     K, N = case["K"], case["N"]
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     n = sk.workspace_bytes(sk.OP_NVFP4, M, K, N)
-    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda") if n else None
+    ws = sk.new_workspace(n, fill=0xA5)
     sk.nvfp4_gemm(dev(case["blob"]), dev(case["x"][:M]), y, workspace=ws)
     return y
 
