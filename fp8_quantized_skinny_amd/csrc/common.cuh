@@ -95,14 +95,6 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// 16 bytes of weights whose 128-byte line another load of the same wavefront
-// also reads (the canonical FP8 order): a plain load, which keeps the line
-// cached for its second reader.  Streamed, the canonical FP8 calls ran 9-13%
-// slower.
-__device__ __forceinline__ u32x4 load16_shared_line(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
 // Zeroes halves [from, to) of rows 0..M-1 of an LDS copy of x (row stride RS
 // halves) with 16-byte stores: the part of the copy past K, which the
 // direct-to-LDS loads leave untouched.  from, to and RS are multiples of 8.

@@ -22,15 +22,18 @@
 // a K split over workgroups when K has more units (partial sums stored with
 // plain stores and added in split order by the reduction kernel).  The MFMA
 // engine copies x into LDS once per workgroup with direct-to-LDS loads.
-// Lane (grp, c) reads, per chunk, the
-// two 16-byte pieces K = 128j + 64h + 16grp .. +16 (h = 0, 1) of column c, so
-// each load instruction covers 64 contiguous bytes of 16 columns.  Pieces past
-// K or columns past N read a clamped valid address and are zeroed.
+// Both engines contract, per chunk j, lane (grp, c)'s two 16-byte pieces
+// K = 128j + 64h + 16grp .. +16 (h = 0, 1) of column c.  Canonical codes are
+// not loaded in that layout (it would read every 128-byte line as two halves
+// from two instructions): each load reads eight whole lines and a small
+// per-wavefront LDS tile rearranges them into the pieces.  Pieces past K or
+// columns past N read a clamped valid address and are zeroed.
 //
 // The packed variant reads the same pieces from a blob of fp8_pack: 8 KiB
 // units (one tile x 512 K) in span-major order, in which piece 2j + h of a
 // unit holds each lane's 16 bytes next to each other, so every load
 // instruction is one contiguous KiB, as for NVFP4 (padding is zero codes).
+// Canonical and packed codes give the same registers, hence the same bits.
 #include <hip/hip_runtime.h>
 
 #include "common.cuh"
@@ -88,6 +91,66 @@ __device__ void fp8_stage_x(const Fp8Args& a, const Fp8Plan& P, _Float16* xs) {
   }
 }
 
+// Canonical codes, whole lines per load: load i of a unit (tile t, K range
+// 512u ..) gives lane (c, p) = (lane / 8, lane % 8) the 16 bytes
+// K = 512u + 128(i % 4) + 16p .. +16 of column 16t + 8(i / 4) + c, so the
+// eight lanes of a column cover one 128-byte line and each instruction eight
+// whole lines.  (Reading the tile in the compute layout instead, sixteen half
+// lines per instruction and two instructions per line, ran at about three
+// quarters of the whole-line read rate.)  Loads go out in the order
+// 0, 4, 1, 5, ... so that chunk j (loads j and 4 + j) is complete after its
+// first 2(j + 1) loads.  Pieces past K read the row start instead (K % 16 ==
+// 0: a piece is all in or all out); their x is zero.
+__device__ __forceinline__ void fp8_load_lines(u32x4 (&v)[2 * kFp8UnitChunks], const Fp8Args& a, int tt, int u,
+                                               int lane) {
+  const int c8 = lane >> 3, p = lane & 7;
+#pragma unroll
+  for (int j = 0; j < kFp8UnitChunks; ++j) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int n = min(tt * kTileCols + 8 * g + c8, a.N - 1);
+      const int k = u * kFp8UnitK + kChunkK * j + 16 * p;
+      v[4 * g + j] = load16(a.w + static_cast<size_t>(n) * a.K + (k < a.K ? k : 0));
+    }
+  }
+}
+
+// Per-wavefront LDS slot: first the tile through which the loads above are
+// rearranged into the compute layout, half a chunk at a time (16 rows of 64
+// bytes, padded to 80 so that the column-strided reads touch every bank once
+// per eight lanes), then the wavefront's partial tile sums (MFMA engine).
+constexpr int kLineRowBytes = 80;
+constexpr int kWaveSlotBytes = kTileCols * kLineRowBytes;
+static_assert(kWaveSlotBytes >= 32 * 16, "slot holds the reduction entry");
+
+// Orders this wavefront's LDS accesses of different lanes: stores before the
+// fence are seen by loads after it, and loads before it read their data
+// before stores after it land.  The hardware runs one wavefront's LDS
+// operations in order; the fences and the wave barrier keep the compiler
+// from moving an access across (to one lane's view the accesses of the
+// others do not exist).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Piece h of chunk j in the compute (and packed) layout: lane (grp, c) gets
+// the 16 bytes K = 128j + 64h + 16grp .. +16 of column c, which load j
+// (columns 0..7) or 4 + j (columns 8..15) gave lane (c % 8, 4h + grp).  Only
+// this wavefront touches `tile`.
+__device__ __forceinline__ u32x4 fp8_line_piece(const u32x4 (&v)[2 * kFp8UnitChunks], int j, int h,
+                                                unsigned char* tile, int lane) {
+  const int c8 = lane >> 3, p = lane & 7;
+  wave_lds_sync();  // the previous piece's reads are done with the tile
+  if ((p >> 2) == h) {
+    *reinterpret_cast<u32x4*>(tile + c8 * kLineRowBytes + 16 * (p & 3)) = v[j];
+    *reinterpret_cast<u32x4*>(tile + (8 + c8) * kLineRowBytes + 16 * (p & 3)) = v[4 + j];
+  }
+  wave_lds_sync();
+  return *reinterpret_cast<const u32x4*>(tile + (lane & 15) * kLineRowBytes + 16 * (lane >> 4));
+}
+
 // A fragments of chunk j: lane (row c, grp) holds, for MFMA i = 2h + s,
 // x[min(c, M-1)][512u + 128j + 64h + 16grp + 8s .. +8].  Rows c >= M only
 // feed output rows that are never stored, so they repeat row M-1.
@@ -121,12 +184,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const Fp8Plan P(a, CT);
   _Float16* xs = reinterpret_cast<_Float16*>(lds);
-  f32x4* red = reinterpret_cast<f32x4*>(lds + ((a.M * fp8_xs_stride(P.S) * 2 + 15) & ~15));  // [nw][32]
+  unsigned char* slots = lds + ((a.M * fp8_xs_stride(P.S) * 2 + 15) & ~15);  // [nw][kWaveSlotBytes]
+  unsigned char* slot = slots + P.wave * kWaveSlotBytes;
 
   fp8_stage_x(a, P, xs);
   const int cl = P.lane & 15, grp = P.lane >> 4;
   const int tt = min(P.tile0 + P.t, a.nt - 1);
   u32x4 w[kFp8UnitChunks][2];
+  u32x4 v[2 * kFp8UnitChunks];  // canonical codes as loaded (whole lines)
   float sc[kFp8UnitChunks];
   // Every wavefront loads, an idle one (past the last K span) clamped
   // addresses it never uses: with no load under a branch the compiler waits
@@ -154,21 +219,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
         for (int h = 0; h < 2; ++h) w[j][h] = load16(up + (2 * j + h) * 1024);
       }
     } else {
-      const int n = min(tt * kTileCols + cl, a.N - 1);
-      const uint8_t* row = a.w + static_cast<size_t>(n) * a.K;
-      const int k0 = u * kFp8UnitK + grp * 16;
-#pragma unroll
-      for (int j = 0; j < kFp8UnitChunks; ++j) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int k = k0 + j * kChunkK + 64 * h;
-          w[j][h] = load16_shared_line(row + (k + 16 <= a.K ? k : 0));
-        }
-      }
+      fp8_load_lines(v, a, tt, min(u, a.ku - 1), P.lane);
     }
   }
   // x is in LDS once every wavefront's copies are done; the weights keep arriving.
   lds_copy_barrier<2 * kFp8UnitChunks>(true);
+  if (!PACKED) {
+#pragma unroll
+    for (int j = 0; j < kFp8UnitChunks; ++j) {
+      w[j][0] = fp8_line_piece(v, j, 0, slot, P.lane);
+      w[j][1] = fp8_line_piece(v, j, 1, slot, P.lane);
+    }
+  }
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (P.active) {
@@ -177,14 +239,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
     fp8_read_x(x0, xrow, 0);
     fp8_steps<0>(w, sc, x0, x1, acc, xrow);
   }
-  if (P.lane < 32) red[P.wave * 32 + P.lane] = acc;
+  if (P.lane < 32) reinterpret_cast<f32x4*>(slot)[P.lane] = acc;
   __syncthreads();
 
   const bool fin = P.wave < CT && P.tile0 + P.wave < a.nt && P.lane < 32;
   const int n = (P.tile0 + P.wave) * kTileCols + cl;
   if (fin && n < a.N) {
     f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < P.sw; ++s) tot += red[(P.wave * P.S + s) * 32 + P.lane];
+    for (int s = 0; s < P.sw; ++s)
+      tot += reinterpret_cast<const f32x4*>(slots + (P.wave * P.S + s) * kWaveSlotBytes)[P.lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = grp * 4 + i;
@@ -431,6 +494,7 @@ __device__ __forceinline__ void fp8_half_dot(float (&p)[MR], const uint32_t (&xv
 // reads row 2 again and is never stored).
 template <int CT, bool PACKED, int MR>
 __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // canonical codes: [nw][kWaveSlotBytes]
   __shared__ float red[kMaxWaves][MR][16];
   const Fp8Plan P(a, CT);
   const int q = P.lane & 15, r = P.lane >> 4;
@@ -448,6 +512,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
     }
   }
   u32x4 w[kFp8UnitChunks][2];
+  u32x4 v[2 * kFp8UnitChunks];  // canonical codes as loaded (whole lines)
   uint32_t xv[kFp8UnitChunks][MR];
   const int kx = u * kFp8UnitK + 64 * (q >> 3) + 16 * r + 2 * (q & 7);
   const _Float16* xr[MR];
@@ -467,19 +532,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
         xv[j][m] = *reinterpret_cast<const uint32_t*>(xr[m] + min(kx + j * kChunkK, a.K - 2));
     }
   } else {
-    const int cl = P.lane & 15, grp = P.lane >> 4;
-    const uint8_t* row = a.w + static_cast<size_t>(min(tt * kTileCols + cl, a.N - 1)) * a.K;
-    const int k0 = u * kFp8UnitK + grp * 16;
+    fp8_load_lines(v, a, tt, u, P.lane);
 #pragma unroll
     for (int j = 0; j < kFp8UnitChunks; ++j) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = k0 + j * kChunkK + 64 * h;
-        w[j][h] = load16_shared_line(row + (k + 16 <= a.K ? k : 0));
-      }
-#pragma unroll
       for (int m = 0; m < MR; ++m)
         xv[j][m] = *reinterpret_cast<const uint32_t*>(xr[m] + min(kx + j * kChunkK, a.K - 2));
+    }
+    unsigned char* slot = lds + P.wave * kWaveSlotBytes;
+#pragma unroll
+    for (int j = 0; j < kFp8UnitChunks; ++j) {
+      w[j][0] = fp8_line_piece(v, j, 0, slot, P.lane);
+      w[j][1] = fp8_line_piece(v, j, 1, slot, P.lane);
     }
   }
   float acc[MR];
@@ -536,7 +600,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
 
 size_t fp8_lds_bytes(int M, int S, int nw) {
   return ((static_cast<size_t>(M) * (S * kFp8UnitK + 8) * 2 + 15) & ~static_cast<size_t>(15)) +
-         static_cast<size_t>(nw) * 32 * sizeof(f32x4);
+         static_cast<size_t>(nw) * kWaveSlotBytes;
 }
 
 }  // namespace
@@ -555,12 +619,13 @@ bool fp8_cfg_supported(const LaunchCfg& c, int M, int K) {
 // The VALU engine's instance for M rows (M = 3 runs as four rows).
 template <int CT, bool PACKED>
 void launch_fp8_valu_rows(const Fp8Args& a, dim3 grid, dim3 blk, hipStream_t stream) {
+  const size_t lds = PACKED ? 0 : static_cast<size_t>(blk.x / 64) * kWaveSlotBytes;
   if (a.M == 1)
-    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 1>), grid, blk, 0, stream, a);
+    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 1>), grid, blk, lds, stream, a);
   else if (a.M == 2)
-    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 2>), grid, blk, 0, stream, a);
+    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 2>), grid, blk, lds, stream, a);
   else
-    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 4>), grid, blk, 0, stream, a);
+    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 4>), grid, blk, lds, stream, a);
 }
 
 template <int CT>
