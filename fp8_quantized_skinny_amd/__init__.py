@@ -191,8 +191,9 @@ def nvfp4_gemm(w_packed, x, y, K=None, N=None, workspace=None, stream=None, conf
     """y[M, N] fp16 = x[M, K] fp16 . dequant(W); w_packed: CUDA uint8 blob from nvfp4_pack.
 
     config: optional (engine, ct, nw, ksplit) kernel choice; default lets the library pick.
-    workspace: CUDA uint8 tensor of at least workspace_bytes(OP_NVFP4, ...) bytes when that is > 0
-    (scratch: any contents, not shared by calls that overlap in time)."""
+    workspace: CUDA uint8 tensor of at least workspace_bytes(OP_NVFP4, ...) bytes when that is > 0,
+    from new_workspace() (its first WORKSPACE_SYNC_BYTES zero before the first call; every call
+    leaves them zero; the rest scratch); not shared by calls that overlap in time."""
     import torch
     M, Kx = x.shape
     K = Kx if K is None else K
@@ -237,7 +238,8 @@ def nvfp4_gemm_swiglu(w_packed, x, h, workspace=None, stream=None, config=None):
     """h[M, F] fp16 = silu(x . Wg~) * (x . Wu~); w_packed: CUDA uint8 blob from nvfp4_pack_swiglu.
 
     config: optional (engine, ct, nw, ksplit) for the packed blob's 16 * ceil(F / 8) columns.
-    workspace: CUDA uint8 tensor of at least workspace_bytes(OP_SWIGLU, M, K, F, config) bytes."""
+    workspace: CUDA uint8 tensor of at least workspace_bytes(OP_SWIGLU, M, K, F, config) bytes,
+    from new_workspace() (as for nvfp4_gemm)."""
     import torch
     M, K = x.shape
     F = h.shape[-1]
@@ -317,7 +319,8 @@ def fp8_gemm(w, block_scales, x, y, workspace=None, stream=None, config=None):
 def lm_head_gemm_argmax(w_packed, x, idx, N, logits=None, workspace=None, stream=None, config=None):
     """idx[M] int32 = per-row argmax over the fp32 logits of x . dequant(W) (ties -> lowest n).
 
-    workspace: CUDA uint8 tensor of at least workspace_bytes(OP_LM_HEAD, ...) bytes (scratch)."""
+    workspace: CUDA uint8 tensor of at least workspace_bytes(OP_LM_HEAD, ...) bytes, from
+    new_workspace() (as for nvfp4_gemm)."""
     import torch
     M, K = x.shape
     _shape_checks(x, M, K, logits, N, "logits")
