@@ -5,7 +5,9 @@
 // When K is split over several workgroups, each one stores its fp32 partial
 // sums with plain stores, part[split][m][n], and exits.  finalize_splits then
 // adds the splits in split order (so results never depend on timing),
-// applies the per-tensor scale and rounds to fp16.  For the lm_head it also
+// applies the per-tensor scale and rounds to fp16.  (Plain NVFP4 calls on the
+// MFMA engine add their splits inside the GEMM kernel instead; these kernels
+// serve the VALU engine, FP8, SwiGLU pairs and the lm_head.)  For the lm_head it also
 // takes, per row and per block of 256 columns, the largest logit as one
 // ordered 64-bit key (logit bits above the inverted column, so a larger key is
 // a larger logit or the same logit at a lower column); argmax_reduce then
@@ -25,8 +27,9 @@ constexpr int kFinalizeThreads = 256;
 // Block (x, m): columns 256x .. 256x+255 of row m, one column per thread.
 // Each thread adds its column's partials in split order.  One column per
 // thread gives four times the wavefronts of four columns per thread (16-byte
-// loads); on MI355X that took the down projection at M = 8 (nine splits)
-// from 15.2 to 14.9 us per call.
+// loads); on MI355X that took a nine-way split of the down projection at
+// M = 8 from 15.2 to 14.9 us per call (before such splits moved into the
+// GEMM kernel).
 template <bool ARGMAX>
 __global__ __launch_bounds__(kFinalizeThreads) void finalize_splits(const float* part, int ksplit, int M, int N,
                                                                     const float* gptr, _Float16* y,

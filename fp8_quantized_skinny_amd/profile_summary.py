@@ -31,12 +31,24 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = ("common.cuh", "internal.h", "nvfp4_gemm.hip", "fp8_gemm.hip", "reduce.hip")
 
 
+def _code_only(text):
+    """C++ source without its comments and with each line's whitespace collapsed:
+    what the compiler sees, so that editing a comment keeps a measurement valid.
+    (String literals in these sources hold no comment markers.)"""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = (" ".join(line.split()) for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def sources_sha256():
-    """SHA-256 over the kernel source files, in a fixed order."""
+    """SHA-256 over the code of the kernel source files (comments and blank
+    space left out), in a fixed order."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -78,3 +78,11 @@ def test_traffic_refuses_an_ambiguous_kernel_match(tmp_path):
 def test_sources_hash_is_stable_hex():
     h = ps.sources_sha256()
     assert re.fullmatch(r"[0-9a-f]{64}", h) and h == ps.sources_sha256()
+
+
+def test_sources_hash_ignores_comments_not_code():
+    a = "int f(int x) {  // doubles\n  return 2 * x;  /* the\n result */\n}\n"
+    b = "int f(int x) {\n\n    return 2 * x;\n}\n"
+    c = "int f(int x) {\n  return 3 * x;\n}\n"
+    assert ps._code_only(a) == ps._code_only(b)
+    assert ps._code_only(a) != ps._code_only(c)
