@@ -5,6 +5,11 @@
 Every HIP source is compiled with packed-fp32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops): the kernels get no
 v_pk_*_f32 from the compiler.
+
+The build also reads the compiler's per-kernel resource report and fails if a
+kernel spills registers to scratch memory beyond KNOWN_SPILLS: a spill turns
+the kernels' exact per-chunk load waits into full waits, so it is a
+performance regression even when results stay right.
 """
 
 import os
@@ -18,6 +23,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libskinny.so")
 SOURCES = ["host.cpp", "nvfp4_gemm.hip", "fp8_gemm.hip", "reduce.hip", "probe.hip", "noalloc.hip"]
 ARCH = "gfx950"
+
+# Kernels known to spill, with their scratch bytes per lane: the streaming
+# lm_head instance for three K spans (K <= 3072), which no decode shape here
+# uses.
+KNOWN_SPILLS = {"_ZN6skinny12_GLOBAL__N_112nvfp4_streamILi3ELi1EEEvNS0_9Nvfp4ArgsE": 24}
 
 
 def hipcc():
@@ -36,13 +46,38 @@ def build(verbose=False):
         cmd = [hipcc(), *common, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".hip"):
             cmd[1:1] = ["-x", "hip", f"--offload-arch={ARCH}",
-                        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-        _run(cmd, verbose)
+                        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                        "-Rpass-analysis=kernel-resource-usage"]
+        out = _run(cmd, verbose)
+        if src.endswith(".hip"):
+            check_spills(scratch_per_kernel(out), src)
         objs.append(obj)
     tmp = LIB + ".tmp"
     _run([hipcc(), "-shared", "-fPIC", "-pthread", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
+
+
+def scratch_per_kernel(report):
+    """{kernel symbol: scratch bytes per lane} from the compiler's
+    kernel-resource-usage remarks."""
+    import re
+    sizes, name = {}, None
+    for line in report.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name:
+            sizes[name] = int(m.group(1))
+    return sizes
+
+
+def check_spills(sizes, src):
+    bad = {k: v for k, v in sizes.items() if v > KNOWN_SPILLS.get(k, 0)}
+    if bad:
+        raise RuntimeError(f"build failed: {src}: kernels spill to scratch (bytes per lane): {bad}")
 
 
 def _run(cmd, verbose):
@@ -54,7 +89,8 @@ def _run(cmd, verbose):
     if r.returncode != 0:
         raise RuntimeError(f"build failed: {' '.join(cmd)}\n{out}")
     if verbose and out.strip():
-        print(out)
+        print("\n".join(l for l in out.splitlines() if "kernel-resource-usage" not in l))
+    return out
 
 
 if __name__ == "__main__":
