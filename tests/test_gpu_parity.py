@@ -254,6 +254,30 @@ def test_fp8_parity_all_configs(shape):
         assert np.array_equal(run_fp8(case, config=cfg, packed=True), y), f"{shape} {cfg} packed"
 
 
+@pytest.mark.parametrize("groups", [1024, 1025])
+def test_in_kernel_split_reduction_group_limit(groups):
+    """A plain MFMA call with a K split adds the splits inside the GEMM kernel
+    when it has at most 1024 tile groups (one arrival counter each in the
+    workspace's first 128 KiB), and through the split-reduction kernel beyond;
+    both at the limit, against the oracle, and twice in a row on one workspace
+    (the counters must be back at zero after the first call)."""
+    M, K, N = 3, 2048, 16 * groups
+    cfg = (1, 1, 1, 2)
+    case = workload.nvfp4_case(M, K, N, seed=groups)
+    ref = ref_nvfp4(case)
+    blob, x = dev(case["blob"]), dev(case["x"])
+    ws = ws_for(sk.OP_NVFP4, M, K, N, cfg)
+    ys = []
+    for _ in range(2):
+        y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+        sk.nvfp4_gemm(blob, x, y, config=cfg, workspace=ws)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    _check(ys[0].float().cpu().numpy(), ref, f"{groups} tile groups")
+    assert not ws[:sk.WORKSPACE_SYNC_BYTES].any().item(), "arrival counters not back at zero"
+
+
 def test_deterministic_repeats(small_nvfp4):
     case = small_nvfp4[(8, 1040, 1000)]
     a = run_nvfp4(case)
