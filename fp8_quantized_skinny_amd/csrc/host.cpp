@@ -239,8 +239,8 @@ bool nvfp4_uses_xsplit(const LaunchCfg& cfg, int N, bool plain_epilogue) {
   // The reduction's buffer offsets, up to (ksplit + 16) blocks of at most
   // 8 rows x ct tiles of fp32, stay far inside an int.
   const int64_t reach = static_cast<int64_t>(cfg.ksplit + 16) * 8 * cfg.ct * kTileCols * 4;
-  return cfg.engine == 1 && cfg.ksplit > 1 && plain_epilogue && (nt + cfg.ct - 1) / cfg.ct <= kMaxSyncGroups &&
-         reach < (int64_t{1} << 30);
+  return (cfg.engine == 0 || cfg.engine == 1) && cfg.ksplit > 1 && plain_epilogue &&
+         (nt + cfg.ct - 1) / cfg.ct <= kMaxSyncGroups && reach < (int64_t{1} << 30);
 }
 
 // Partial sums of a K split: fp32, ksplit x M x (the tiles' columns) for the

@@ -126,7 +126,8 @@ struct WorkspaceLayout {
 };
 WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N, bool argmax);
 // True when an NVFP4 call with this choice adds its K split inside the GEMM
-// kernel (the MFMA engine, plain epilogue, at most kMaxSyncGroups tile groups).
+// kernel (the VALU or MFMA engine, plain epilogue, at most kMaxSyncGroups tile
+// groups).
 bool nvfp4_uses_xsplit(const LaunchCfg& cfg, int N, bool plain_epilogue);
 WorkspaceLayout fp8_workspace_layout(const LaunchCfg& cfg, int M, int K, int N);
 

@@ -273,6 +273,7 @@ template <int CT, int EPI, int MR>
 __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu(Nvfp4Args a) {
   __shared__ float red[kMaxWaves][MR][16];
   const Plan P(a, CT);
+  if (a.xsplit && P.group >= a.ntg) return;  // grid rounding to whole groups of 8 (uniform)
   float acc[MR];
 #pragma unroll
   for (int r = 0; r < MR; ++r) acc[r] = 0.0f;
@@ -342,6 +343,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu(Nvfp4Args a) {
 #pragma unroll
       for (int r = 0; r < MR; ++r) tot[r] += red[P.wave * P.S + s][r][P.lane];
     }
+  }
+  if (a.ksplit > 1 && a.xsplit) {  // this split's block of the group; the last split adds them
+    if (fin) {
+      float* blk = a.part + (static_cast<size_t>(P.group) * a.ksplit + P.split) * MR * (CT * kTileCols);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) blk[r * (CT * kTileCols) + P.wave * kTileCols + P.lane] = tot[r];
+    }
+    xsplit_finish<CT>(a, P);
+    return;
+  }
+  if (fin) {
     if (EPI == kEpiSwiglu && a.ksplit == 1) {  // lanes 0..15 of the wavefront are all here
       const int f = (P.tile0 + P.wave) * 8 + P.lane;
 #pragma unroll
