@@ -100,9 +100,12 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 //
 // NVFP4 at M = 1 (GEMV, and the lm_head with its argmax: on the 151936-column
 // vocabulary the GEMV reads at 6.95 TB/s against 6.5 TB/s for the streaming
-// engine): VALU engine, whole K per workgroup (K beyond
-// 16 spans split over workgroups, evened out), two tiles per workgroup when
-// there are few tiles (N <= 6144), else one.  NVFP4 at M = 2 without argmax
+// engine): VALU engine, whole K per workgroup, two tiles per workgroup when
+// there are few tiles (N <= 6144), else one.  With few tiles and K beyond 16
+// spans (a K split either way), four tiles of two spans per workgroup
+// instead: with the split added inside the kernel, the 17408 x 5120 down
+// projection took 10.40-10.43 us so against 10.65-10.72 us for two tiles of
+// six spans (three-way split).  NVFP4 at M = 2 without argmax
 // takes the same choice when there are few tiles (N <= 6144): on the
 // 17408 x 5120 down projection it took 12.7 us against 13.7 us for the MFMA
 // engine, and 6.0 against 6.5-6.7 us on one rank's 4-way share of up and
@@ -170,6 +173,7 @@ bool pick_stream_cfg(int M, int K, int N, bool argmax, LaunchCfg* out) {
 LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax) {
   const Geometry g = nvfp4_geometry(K, N);
   auto fits = [&](const LaunchCfg& c) { return nvfp4_cfg_supported(c, M, K, argmax); };
+  if (M == 1 && !argmax && g.nt <= 384 && g.ku > kMaxWaves) return fit_spans(0, 4, g.ku, 2, fits);
   if (M == 1 || (M == 2 && !argmax && g.nt <= 384)) return pick_whole_k_cfg(0, g.nt <= 384 ? 2 : 1, g.ku, fits);
   LaunchCfg c;
   if (pick_stream_cfg(M, K, N, argmax, &c)) return c;

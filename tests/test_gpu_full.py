@@ -60,7 +60,7 @@ def _whole(got, ref, what):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,ms", [("up", (1, 4)), ("gate_up", (8, 4)), ("down", (8, 4)),
+@pytest.mark.parametrize("name,ms", [("up", (1, 4)), ("gate_up", (8, 4)), ("down", (8, 4, 2, 1)),
                                      ("up_tp4", (1, 4, 8)), ("gate_up_tp4", (1, 4, 8)), ("down_tp4", (1, 4, 8))])
 def test_nvfp4_full_shape_whole_output(name, ms):
     """The decode shapes in the benchmark's kernel choice, with M = 4 (k = 3
