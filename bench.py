@@ -9,6 +9,7 @@ K = 5120, N = 17408 (an MLP up-projection at decode): one step is one
 nvfp4_gemm call.  The same line also carries, timed the same way:
   * the NVFP4 M = 8 shapes: fused gate+up 5120 x 34816, down 17408 x 5120,
     and gate+up with the fused SwiGLU epilogue (nvfp4_gemm_swiglu, h[8, 17408]);
+  * the other two NVFP4 MLP projections at M = 1: gate+up and down;
   * the FP8 shapes qkv 5120 x 7168 and o_proj 6144 x 5120 at M = 1, 2 and 4,
     with canonical codes (fp8_gemm) and packed codes (fp8_gemm_packed);
   * the 151936-column NVFP4 lm_head with its fused argmax at M = 1 and 8;
@@ -435,11 +436,13 @@ def measure_block(M, steps, warmup):
 
 def companions(steps, warmup):
     """The other configurations of the benchmark, timed like the headline: the NVFP4 M = 8
-    shapes, the FP8 shapes at M = 1, 2, 4 (canonical and packed codes) and the lm_head at M = 1
-    and 8, each with the read ceiling at its weight size."""
+    shapes, the other two NVFP4 MLP projections at M = 1, the FP8 shapes at M = 1, 2, 4
+    (canonical and packed codes) and the lm_head at M = 1 and 8, each with the read ceiling at
+    its weight size."""
     m8 = []
     for name in ("gate_up", "down", "gate_up_swiglu"):
         m8.append(measure(name, 8, None, steps, warmup, ceiling=name != "gate_up_swiglu"))
+    m1 = [measure(name, 1, None, steps, warmup) for name in ("gate_up", "down")]
     fp8 = []
     for name in ("qkv", "o_proj"):
         case = prepare(name)
@@ -454,7 +457,7 @@ def companions(steps, warmup):
         lm.append(measure("lm_head", M, None, max(20, steps // 10), max(2, warmup // 10), case=case,
                           ceiling=M == 1))
     del case
-    return m8, fp8, lm
+    return m8, m1, fp8, lm
 
 
 def main():
@@ -487,9 +490,9 @@ def main():
     case = prepare(args.workload, args.M)
     head = measure(args.workload, args.M, cfg, args.steps, args.warmup, case=case,
                    ceiling=not args.headline_only, large_probe=True)
-    m8, fp8, lm, block = [], [], [], None
+    m8, m1, fp8, lm, block = [], [], [], [], None
     if not args.headline_only and args.workload == "up" and cfg is None:
-        m8, fp8, lm = companions(args.steps, args.warmup)
+        m8, m1, fp8, lm = companions(args.steps, args.warmup)
         block = measure_block(8, args.steps, args.warmup)
     value = head["GB/s"]
     out = {
@@ -507,7 +510,8 @@ def main():
         "data": "synthetic",
         "config": {**head, "timed": "one HIP-graph replay of K steps, weights rotated over R copies; "
                                     "spread: that replay and 6 more",
-                   "m8_shapes": m8, "fp8_shapes": fp8, "lm_head_shapes": lm, "decoder_block_m8": block},
+                   "m8_shapes": m8, "m1_shapes": m1, "fp8_shapes": fp8, "lm_head_shapes": lm,
+                   "decoder_block_m8": block},
         "roofline": {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4),
                      "traffic": None if cfg else recorded_traffic(args.workload, head["M"]),
