@@ -16,14 +16,13 @@
 // workgroup is CT tiles x S consecutive K spans (nw = CT * S wavefronts);
 // the S partial sums of a tile are added in LDS in span order.  When K has
 // more spans than a workgroup covers, ksplit workgroups share a tile group:
-// each stores its fp32 partial sums with plain stores and exits, and a second
-// small kernel (reduce.hip) adds the splits in split order, so results never
-// depend on timing.  (Handing partials over inside one kernel needs
-// system-scope stores, a wait for them and an arrival counter; on MI355X that
-// kept finished workgroups resident for microseconds and cost more than the
-// second launch.)  Few registers per wavefront (one unit) let the chip keep
-// tens of megabytes of weight loads in flight, which is what saturates HBM at
-// these sizes.
+// each stores its fp32 partial sums with plain stores.  With the plain
+// epilogue the splits of a group run on one XCD and the last of them to
+// arrive adds all of them in split order (xsplit_finish below); otherwise a
+// second small kernel (reduce.hip) adds them in split order.  Either way the
+// result does not depend on timing.  Few registers per wavefront (one unit)
+// let the chip keep tens of megabytes of weight loads in flight, which is
+// what saturates HBM at these sizes.
 //
 // Two engines (lane l = 16*grp + c handles column c of the tile and the
 // 32-K run 128j + 32grp .. +32 of every chunk j):
