@@ -170,9 +170,20 @@ bool pick_stream_cfg(int M, int K, int N, bool argmax, LaunchCfg* out) {
   return true;
 }
 
-LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax) {
+LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax, bool swiglu = false) {
   const Geometry g = nvfp4_geometry(K, N);
   auto fits = [&](const LaunchCfg& c) { return nvfp4_cfg_supported(c, M, K, argmax); };
+  // One tile of whole K per workgroup, balanced over the CUs when the tiles
+  // do not divide evenly (BalancedLayout), with three or four whole tiles per
+  // CU.  On MI355X at K = 5120: 1088 tiles took 10.11 against 10.28 us at
+  // M = 1 and 11.04 against 11.23 us (streaming engine) at M = 2, 832 tiles
+  // 8.17 against 8.30 and 9.21 against 10.34 us; with one or two whole tiles
+  // per CU (400 and 576 tiles) it was up to 0.24 us slower.
+  BalancedLayout bal;
+  const int cus = device_cu_count();
+  if (M <= 2 && !argmax && !swiglu && g.nt > 384 && g.ku <= kMaxWaves && g.nt / cus >= 3 &&
+      nvfp4_balanced_layout(g.nt, g.ku, cus, &bal))
+    return LaunchCfg{3, 1, g.ku, 1};
   if (M == 1 && !argmax && g.nt <= 384 && g.ku > kMaxWaves) return fit_spans(0, 4, g.ku, 2, fits);
   if (M == 1 || (M == 2 && !argmax && g.nt <= 384)) return pick_whole_k_cfg(0, g.nt <= 384 ? 2 : 1, g.ku, fits);
   LaunchCfg c;
@@ -238,6 +249,20 @@ Geometry nvfp4_geometry(int K, int N) {
   return g;
 }
 
+bool nvfp4_balanced_layout(int nt, int ku, int cus, BalancedLayout* out) {
+  if (cus < 1 || nt % cus == 0 || nt / cus > 4) return false;
+  const int rest = nt % cus;
+  const int cap = std::min(cus, kMaxSyncGroups);
+  for (int spans = 1; spans <= ku; ++spans) {
+    const int splits = (ku + spans - 1) / spans;
+    if (static_cast<long>(rest) * splits <= cap) {
+      *out = BalancedLayout{nt - rest, spans, splits};
+      return true;
+    }
+  }
+  return false;
+}
+
 bool nvfp4_uses_xsplit(const LaunchCfg& cfg, int N, bool plain_epilogue) {
   const int nt = (N + kTileCols - 1) / kTileCols;
   // The reduction's buffer offsets, up to (ksplit + 16) blocks of at most
@@ -256,6 +281,13 @@ bool nvfp4_uses_xsplit(const LaunchCfg& cfg, int N, bool plain_epilogue) {
 WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N, bool argmax) {
   const Geometry g = nvfp4_geometry(K, N);
   WorkspaceLayout w{};
+  if (cfg.engine == 3) {  // the balanced GEMV's split tiles: at most kMaxSyncGroups blocks of M x 16
+    w.sync_bytes = kSyncBytes;
+    w.part_off = kSyncBytes;
+    w.part_bytes = static_cast<size_t>(kMaxSyncGroups) * M * kTileCols * 4;
+    w.total = align256(w.part_off + w.part_bytes);
+    return w;
+  }
   if (!argmax && cfg.ksplit == 1) return w;
   size_t off = kSyncBytes;
   w.sync_bytes = kSyncBytes;
@@ -315,7 +347,7 @@ size_t skinny_workspace_bytes_config(int op, int M, int K, int N, int engine, in
     case 1: return fp8_cfg_supported(c, M, K) ? fp8_workspace_layout(c, M, K, N).total : 0;
     case 2: return nvfp4_cfg_supported(c, M, K, true) ? nvfp4_workspace_layout(c, M, K, N, true).total : 0;
     case 3:
-      return swiglu_shape(M, K, N) == SKINNY_OK && nvfp4_cfg_supported(c, M, K, false)
+      return swiglu_shape(M, K, N) == SKINNY_OK && c.engine != 3 && nvfp4_cfg_supported(c, M, K, false)
                  ? nvfp4_workspace_layout(c, M, K, swiglu_packed_cols(N), false).total
                  : 0;
     default: return 0;
@@ -329,7 +361,7 @@ int skinny_config_supported(int op, int M, int K, int N, int engine, int ct, int
     case 0: return nvfp4_cfg_supported(c, M, K, false) ? 1 : 0;
     case 1: return fp8_cfg_supported(c, M, K) ? 1 : 0;
     case 2: return nvfp4_cfg_supported(c, M, K, true) ? 1 : 0;
-    case 3: return swiglu_shape(M, K, N) == SKINNY_OK && nvfp4_cfg_supported(c, M, K, false) ? 1 : 0;
+    case 3: return swiglu_shape(M, K, N) == SKINNY_OK && c.engine != 3 && nvfp4_cfg_supported(c, M, K, false) ? 1 : 0;
     default: return 0;
   }
 }
@@ -378,7 +410,7 @@ int skinny_default_config(int op, int M, int K, int N, int* engine, int* ct, int
   if (op < 0 || op > 3) return SKINNY_EINVAL;
   if (op == 3 ? swiglu_shape(M, K, N) : check_shape(M, K, N)) return SKINNY_ESHAPE;
   const LaunchCfg c = op == 1   ? default_fp8_cfg(M, K, N)
-                      : op == 3 ? default_nvfp4_cfg(M, K, swiglu_packed_cols(N), false)
+                      : op == 3 ? default_nvfp4_cfg(M, K, swiglu_packed_cols(N), false, true)
                                 : default_nvfp4_cfg(M, K, N, op == 2);
   *engine = c.engine;
   *ct = c.ct;
@@ -396,7 +428,7 @@ size_t skinny_workspace_bytes(int op, int M, int K, int N) {
     case 3: {
       if (swiglu_shape(M, K, N)) return 0;
       const int Np = swiglu_packed_cols(N);
-      return nvfp4_workspace_layout(default_nvfp4_cfg(M, K, Np, false), M, K, Np, false).total;
+      return nvfp4_workspace_layout(default_nvfp4_cfg(M, K, Np, false, true), M, K, Np, false).total;
     }
     default: return 0;
   }
@@ -752,7 +784,7 @@ int nvfp4_gemm_swiglu_config(const void* w_packed, const uint16_t* x, uint16_t* 
   if (!aligned(h, 16)) return SKINNY_EALIGN;
   const int N = swiglu_packed_cols(F);
   const LaunchCfg cfg{engine, ct, nw, ksplit};
-  if (!nvfp4_cfg_supported(cfg, M, K, false)) return SKINNY_EINVAL;
+  if (cfg.engine == 3 || !nvfp4_cfg_supported(cfg, M, K, false)) return SKINNY_EINVAL;  // 3: plain epilogue only
   s = check_workspace(workspace, workspace_bytes, nvfp4_workspace_layout(cfg, M, K, N, false).total);
   if (s) return s;
   return launch_status(launch_nvfp4(static_cast<const uint8_t*>(w_packed), x, h, M, K, N, cfg, nullptr,
@@ -763,7 +795,7 @@ int nvfp4_gemm_swiglu(const void* w_packed, const uint16_t* x, uint16_t* h, int 
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int s = swiglu_shape(M, K, F);
   if (s) return s;
-  const LaunchCfg c = default_nvfp4_cfg(M, K, swiglu_packed_cols(F), false);
+  const LaunchCfg c = default_nvfp4_cfg(M, K, swiglu_packed_cols(F), false, true);
   return nvfp4_gemm_swiglu_config(w_packed, x, h, M, K, F, workspace, workspace_bytes, stream, c.engine, c.ct,
                                   c.nw, c.ksplit);
 }
@@ -838,7 +870,7 @@ static int layer_check(const skinny_layer& l, const uint16_t* x, const uint16_t*
       if (s) return s;
       if (!aligned(y, 16)) return SKINNY_EALIGN;
       const int Np = swiglu_packed_cols(l.N);
-      *need = nvfp4_workspace_layout(default_nvfp4_cfg(M, l.K, Np, false), M, l.K, Np, false).total;
+      *need = nvfp4_workspace_layout(default_nvfp4_cfg(M, l.K, Np, false, true), M, l.K, Np, false).total;
       return SKINNY_OK;
     }
     default:

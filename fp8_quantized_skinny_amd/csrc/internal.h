@@ -102,7 +102,8 @@ static_assert(sizeof(Fp8Header) <= kHeaderBytes, "header too large");
 
 // Launch parameters picked by the host for one call.
 struct LaunchCfg {
-  int engine;  // 0 = VALU dot2 (NVFP4 M <= 2, FP8 M <= 4), 1 = MFMA 16x16x32 f16, 2 = streaming MFMA
+  int engine;  // 0 = VALU dot2 (NVFP4 M <= 2, FP8 M <= 4), 1 = MFMA 16x16x32 f16, 2 = streaming MFMA,
+               // 3 = the NVFP4 VALU GEMV with whole K per tile, balanced over the CUs (see BalancedLayout)
   int ct;      // engines 0, 1: column tiles (of 16) per workgroup; engine 2: workgroups per CU
   int nw;      // wavefronts per workgroup (1..16); engines 0, 1: ct * K spans per workgroup
   int ksplit;  // workgroups that split K (1 = no split; engine 2 never splits)
@@ -125,6 +126,22 @@ struct WorkspaceLayout {
   size_t sync_off, sync_bytes, keys_off, keys_bytes, part_off, part_bytes, total;
 };
 WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N, bool argmax);
+// The balanced VALU GEMV (engine 3).  The one-tile-whole-K GEMV puts nt
+// workgroups of ku wavefronts on the CUs; when nt is not a multiple of the
+// CU count, some CUs get one whole tile more than the others (ku units of
+// 9 KiB), and the call lasts as long as those CUs take.  The balanced layout
+// keeps `whole` = the largest multiple of the CU count of tiles as whole-K
+// workgroups and cuts each of the other nt - whole tiles into `splits`
+// workgroups of `spans` K spans, at most one per CU, added inside the kernel
+// (as an in-kernel K split).  False when nothing is to gain or the layout does
+// not fit: nt a multiple of the CU count, more than four whole tiles per CU
+// (the grid would no longer be resident at once), or more split workgroups
+// than CUs (or than kMaxSyncGroups).
+struct BalancedLayout {
+  int whole, spans, splits;
+};
+bool nvfp4_balanced_layout(int nt, int ku, int cus, BalancedLayout* out);
+
 // True when an NVFP4 call with this choice adds its K split inside the GEMM
 // kernel (the VALU or MFMA engine, plain epilogue, at most kMaxSyncGroups tile
 // groups).

@@ -67,6 +67,11 @@ struct Nvfp4Args {
   int xsplit;                // 1: the K split is added inside the kernel on each tile group's XCD
   int ntg;                   // tile groups (xsplit)
   unsigned* sync;            // xsplit: one arrival counter per tile group, 128 bytes apart (zero at rest)
+  // Balanced VALU GEMV (engine 3; bal_small == 0 otherwise): workgroups b <
+  // bal_small each take bal_s K spans of one of the last bal_r tiles (bal_ks
+  // workgroups per tile, added as an xsplit); the others take one whole tile
+  // of the first bal_whole tiles each.
+  int bal_small, bal_r, bal_whole, bal_s, bal_ks;
 };
 
 // What a kernel does with its finished fp32 tile sums.
@@ -97,12 +102,40 @@ struct Plan {
   int lane, wave, nw, S, tile0, s0, sw;  // sw: spans in this split
   int t, s;                              // local tile and span of this wavefront's unit
   int group, split;                      // tile group and K split of this workgroup
+  int ks;                                // workgroups that share the tile group along K
   bool active;
+  bool small;                            // a K-split workgroup of the balanced GEMV
   __device__ Plan(const Nvfp4Args& a, int ct) {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     nw = blockDim.x >> 6;
     S = a.S;
+    ks = a.ksplit;
+    small = false;
+    if (a.bal_small > 0) {  // balanced GEMV (ct = 1, nw = ku)
+      const int b = blockIdx.x;
+      small = b < a.bal_small;
+      if (small) {
+        ks = a.bal_ks;
+        xsplit_place(b, a.bal_ks, group, split);
+        tile0 = a.bal_whole + group;
+        S = a.bal_s;
+        s0 = split * S;
+        sw = min(S, a.ku - s0);
+      } else {
+        ks = 1;
+        group = b - a.bal_small;
+        split = 0;
+        tile0 = group;
+        s0 = 0;
+        sw = a.ku;
+      }
+      t = wave / S;
+      s = wave % S;
+      // A small workgroup has nw = ku wavefronts for its S spans: the rest idle.
+      active = t == 0 && s < sw && (!small || group < a.bal_r);
+      return;
+    }
     if (a.xsplit) {
       xsplit_place(blockIdx.x, a.ksplit, group, split);
     } else {
@@ -128,13 +161,13 @@ struct Plan {
 // already stored to the group's block for split P.split, are published with
 // an arrival count on the group's counter; the workgroup that arrives last
 // (all splits of the group run on one XCD, so plain stores, an atomic in that
-// XCD's L2 and loads that skip the CU's L1 see each other) adds the ksplit
+// XCD's L2 and loads that skip the CU's L1 see each other) adds the ks
 // blocks in split order, scales by g and writes y.  It then sets the counter
 // back to zero for the next call.  Nothing waits on another workgroup, and the
 // order of the sums does not depend on which split arrives last.
 // Every thread of the workgroup must call this.
 template <int CT>
-__device__ void xsplit_finish(const Nvfp4Args& a, const Plan& P) {
+__device__ void xsplit_finish(const Nvfp4Args& a, const Plan& P, int ks) {
   constexpr int kCols = CT * kTileCols;
   __shared__ int last;
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have reached L2
@@ -142,15 +175,15 @@ __device__ void xsplit_finish(const Nvfp4Args& a, const Plan& P) {
   if (threadIdx.x == 0) {
     unsigned* cnt = a.sync + static_cast<size_t>(P.group) * 32;
     const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    last = old == static_cast<unsigned>(a.ksplit - 1);
+    last = old == static_cast<unsigned>(ks - 1);
     if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();
   if (!last) return;
   const size_t block = static_cast<size_t>(a.M) * kCols;
-  const float* base = a.part + static_cast<size_t>(P.group) * a.ksplit * block;
+  const float* base = a.part + static_cast<size_t>(P.group) * ks * block;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(base), 0, static_cast<int>(a.ksplit * block * sizeof(float)), 0x00020000);
+      const_cast<float*>(base), 0, static_cast<int>(ks * block * sizeof(float)), 0x00020000);
   const float g = *a.gptr;
   for (int o = threadIdx.x; o < static_cast<int>(block); o += blockDim.x) {
     const int m = o / kCols, n = P.tile0 * kTileCols + o % kCols;
@@ -158,7 +191,7 @@ __device__ void xsplit_finish(const Nvfp4Args& a, const Plan& P) {
     // split past the last reads 0 (outside the buffer's range) and adds 0.
     constexpr int kBatch = 16;
     float sum = 0.0f;
-    for (int k0 = 0; k0 < a.ksplit; k0 += kBatch) {
+    for (int k0 = 0; k0 < ks; k0 += kBatch) {
       float v[kBatch];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)  // sc0: past this CU's L1, from the XCD's L2
@@ -273,6 +306,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu(Nvfp4Args a) {
   __shared__ float red[kMaxWaves][MR][16];
   const Plan P(a, CT);
   if (a.xsplit && P.group >= a.ntg) return;  // grid rounding to whole groups of 8 (uniform)
+  if (P.small && P.group >= a.bal_r) return;  // the same for the balanced GEMV's split tiles
   float acc[MR];
 #pragma unroll
   for (int r = 0; r < MR; ++r) acc[r] = 0.0f;
@@ -343,13 +377,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu(Nvfp4Args a) {
       for (int r = 0; r < MR; ++r) tot[r] += red[P.wave * P.S + s][r][P.lane];
     }
   }
-  if (a.ksplit > 1 && a.xsplit) {  // this split's block of the group; the last split adds them
+  if (P.ks > 1 && (a.xsplit || P.small)) {  // this split's block of the group; the last split adds them
     if (fin) {
-      float* blk = a.part + (static_cast<size_t>(P.group) * a.ksplit + P.split) * MR * (CT * kTileCols);
+      float* blk = a.part + (static_cast<size_t>(P.group) * P.ks + P.split) * MR * (CT * kTileCols);
 #pragma unroll
       for (int r = 0; r < MR; ++r) blk[r * (CT * kTileCols) + P.wave * kTileCols + P.lane] = tot[r];
     }
-    xsplit_finish<CT>(a, P);
+    xsplit_finish<CT>(a, P, P.ks);
     return;
   }
   if (fin) {
@@ -504,7 +538,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
         if (m < a.M) blk[m * (CT * kTileCols) + P.wave * kTileCols + cl] = tot[i];
       }
     }
-    xsplit_finish<CT>(a, P);
+    xsplit_finish<CT>(a, P, a.ksplit);
     return;
   }
   if (a.ksplit > 1) {  // this split's partial sums; the split reduction finishes
@@ -785,6 +819,7 @@ bool nvfp4_cfg_supported(const LaunchCfg& c, int M, int K, bool argmax) {
   const int S = c.nw / c.ct;
   if (static_cast<long>(c.ksplit) * S < ku || static_cast<long>(c.ksplit - 1) * S >= ku) return false;
   if (c.engine == 0) return M <= 2;
+  if (c.engine == 3) return M <= 2 && !argmax && c.ct == 1 && c.ksplit == 1;  // whole K: nw = ku
   if (c.engine != 1) return false;
   return nvfp4_mfma_lds_bytes(M, S, c.nw) <= kMaxLdsBytes;
 }
@@ -868,6 +903,21 @@ hipError_t launch_nvfp4(const uint8_t* blob, const uint16_t* x, uint16_t* y, int
   a.xsplit = nvfp4_uses_xsplit(cfg, N, !argmax && !swiglu) ? 1 : 0;
   a.ntg = (geo.nt + cfg.ct - 1) / cfg.ct;
   a.sync = reinterpret_cast<unsigned*>(ws + wl.sync_off);
+  a.bal_small = a.bal_r = a.bal_whole = a.bal_s = a.bal_ks = 0;
+  if (cfg.engine == 3) {  // plain epilogue only (checked by the callers)
+    BalancedLayout b;
+    LaunchCfg c0 = cfg;
+    c0.engine = 0;
+    if (!nvfp4_balanced_layout(geo.nt, geo.ku, device_cu_count(), &b))
+      return launch_gemm(a, c0, kEpiPlain, stream);  // whole tiles spread evenly already
+    a.bal_whole = b.whole;
+    a.bal_r = geo.nt - b.whole;
+    a.bal_s = b.spans;
+    a.bal_ks = b.splits;
+    a.bal_small = 8 * ((a.bal_r + 7) / 8) * b.splits;
+    a.part = reinterpret_cast<float*>(ws + wl.part_off);
+    return launch_valu<1, kEpiPlain>(dim3(a.bal_small + b.whole), cfg.nw, a, stream);
+  }
   hipError_t e = launch_gemm(a, cfg, argmax ? kEpiArgmax : swiglu ? kEpiSwiglu : kEpiPlain, stream);
   if (e != hipSuccess || a.xsplit) return e;
   int groups = cfg.engine == 2 ? nvfp4_stream_groups(cfg, N) : (geo.nt + cfg.ct - 1) / cfg.ct;

@@ -341,6 +341,16 @@ int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales);
  *                K <= 9216): each workgroup keeps all of x in LDS and each
  *                wavefront walks whole column tiles along K, so K is never
  *                split
+ *            3 = the VALU engine with one tile of whole K per workgroup,
+ *                balanced over the CUs (nvfp4_gemm only, M <= 2; ct = 1,
+ *                nw >= the K spans, ksplit = 1).  When the tiles do not
+ *                divide evenly over the CUs of the current device and there
+ *                are at most four per CU, the tiles past the largest
+ *                multiple of the CU count are cut along K into workgroups
+ *                of a few spans, at most one per CU, whose partial sums are
+ *                added inside the kernel like a K split; every CU then reads
+ *                about the same number of weight bytes.  Otherwise it runs
+ *                as engine 0.  Needs a workspace (skinny_workspace_bytes_config)
  *   ct     : engines 0, 1: 16-column tiles per workgroup: 1, 2, 4 or 8;
  *            engine 2: workgroups per CU, 1 or 2 (the grid is that many per
  *            CU of the current device, at most 1024)

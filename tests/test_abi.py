@@ -94,6 +94,17 @@ def test_explicit_config_rejections():
     assert sk.config_supported(sk.OP_LM_HEAD, 2, 5120, 151936, (0, 1, 5, 1))
     assert sk.config_supported(sk.OP_SWIGLU, 2, 5120, 17408, (0, 1, 5, 1))
     assert not sk.config_supported(sk.OP_NVFP4, 3, 5120, 17408, (0, 1, 5, 1))
+    # engine 3 (VALU GEMV balanced over the CUs): plain nvfp4_gemm, M <= 2, one tile of whole K per workgroup
+    for M in (1, 2):
+        assert sk.config_supported(sk.OP_NVFP4, M, 5120, 17408, (3, 1, 5, 1))
+        assert sk.workspace_bytes(sk.OP_NVFP4, M, 5120, 17408, (3, 1, 5, 1)) == \
+            sk.WORKSPACE_SYNC_BYTES + 1024 * M * 16 * 4
+    assert not sk.config_supported(sk.OP_NVFP4, 3, 5120, 17408, (3, 1, 5, 1))
+    for c in ((3, 2, 10, 1), (3, 1, 3, 2), (3, 1, 4, 1)):
+        assert not sk.config_supported(sk.OP_NVFP4, 1, 5120, 17408, c), c
+    assert not sk.config_supported(sk.OP_LM_HEAD, 1, 5120, 17408, (3, 1, 5, 1))
+    assert not sk.config_supported(sk.OP_SWIGLU, 1, 5120, 8704, (3, 1, 5, 1))
+    assert L.nvfp4_gemm_swiglu_config(A, A, A, 1, 5120, 8704, A, 1 << 20, None, 3, 1, 5, 1) == sk.EINVAL
     # a K split needs its workspace
     big = lambda ws, wsb: L.nvfp4_gemm_config(A, A, A, 8, 17408, 5120, ws, wsb, None, 1, 1, 4, 5)
     need = sk.workspace_bytes(sk.OP_NVFP4, 8, 17408, 5120, (1, 1, 4, 5))
@@ -526,6 +537,12 @@ def test_default_config_query():
                 cfg = sk.default_config(op, M, K, N)
                 assert sk.config_supported(op, M, K, N, cfg), (op, M, K, N, cfg)
                 assert sk.workspace_bytes(op, M, K, N, cfg) == sk.workspace_bytes(op, M, K, N)
+    # 1088 tiles on 256 CUs (the count assumed without a GPU, and MI355X's): the balanced GEMV
+    # at M <= 2; 1024 tiles divide evenly and keep the plain whole-K choice at M = 1.
+    for M in (1, 2):
+        assert sk.default_config(sk.OP_NVFP4, M, 5120, 17408) == (3, 1, 5, 1)
+    assert sk.default_config(sk.OP_NVFP4, 1, 5120, 16384) == (0, 1, 5, 1)
+    assert sk.default_config(sk.OP_SWIGLU, 1, 5120, 8704)[0] != 3
     L = lib()
     v = [ctypes.c_int() for _ in range(4)]
     refs = [ctypes.byref(c) for c in v]

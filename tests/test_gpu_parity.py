@@ -278,6 +278,57 @@ def test_in_kernel_split_reduction_group_limit(groups):
     assert not ws[:sk.WORKSPACE_SYNC_BYTES].any().item(), "arrival counters not back at zero"
 
 
+def balanced_layout(nt, ku, cus):
+    """The library's split of a one-tile-whole-K GEMV over `cus` CUs (engine 3): the largest
+    multiple of cus of tiles stay whole; each other tile becomes `splits` workgroups of `spans`
+    K spans, at most one per CU.  None when the tiles divide evenly or there are more than four
+    whole tiles per CU."""
+    if nt % cus == 0 or nt // cus > 4:
+        return None
+    rest = nt % cus
+    for spans in range(1, ku + 1):
+        splits = -(-ku // spans)
+        if rest * splits <= min(cus, 1024):
+            return nt - rest, spans, splits
+    return None
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 5120, 4688), (2, 3088, 8272), (2, 9008, 1008), (1, 1024, 4112),
+                                   (1, 2048, 4096)])
+def test_balanced_gemv(M, K, N):
+    """Engine 3 (one tile of whole K per workgroup, balanced over the CUs): the tiles past the
+    largest multiple of the CU count are cut into K-split workgroups, added inside the kernel.
+    Whole tiles give the bits of (0, 1, ku, 1) and split tiles those of (0, 1, spans, splits),
+    which add the same sums in the same order; against the oracle too, twice in a row on one
+    workspace (the arrival counters must be back at zero)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ku, nt = -(-K // 1024), -(-N // 16)
+    cfg = (3, 1, ku, 1)
+    assert sk.config_supported(sk.OP_NVFP4, M, K, N, cfg)
+    case = workload.nvfp4_case(M, K, N, seed=N)
+    blob, x = dev(case["blob"]), dev(case["x"])
+    ws = ws_for(sk.OP_NVFP4, M, K, N, cfg)
+    ys = []
+    for _ in range(2):
+        y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+        sk.nvfp4_gemm(blob, x, y, config=cfg, workspace=ws)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    assert not ws[:sk.WORKSPACE_SYNC_BYTES].any().item(), "arrival counters not back at zero"
+    got = ys[0].float().cpu().numpy()
+    _check(got, ref_nvfp4(case), f"balanced {M}x{K}x{N}")
+    whole = run_nvfp4(case, config=(0, 1, ku, 1))
+    lay = balanced_layout(nt, ku, cus)
+    if lay is None:
+        assert np.array_equal(got, whole)
+        return
+    w, spans, splits = lay
+    assert np.array_equal(got[:, :16 * w], whole[:, :16 * w])
+    split = run_nvfp4(case, config=(0, 1, spans, splits))
+    assert np.array_equal(got[:, 16 * w:], split[:, 16 * w:])
+
+
 def test_deterministic_repeats(small_nvfp4):
     case = small_nvfp4[(8, 1040, 1000)]
     a = run_nvfp4(case)
