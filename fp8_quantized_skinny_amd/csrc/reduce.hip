@@ -6,8 +6,8 @@
 // sums with plain stores, part[split][m][n], and exits.  finalize_splits then
 // adds the splits in split order (so results never depend on timing),
 // applies the per-tensor scale and rounds to fp16.  (Plain NVFP4 calls on the
-// MFMA engine add their splits inside the GEMM kernel instead; these kernels
-// serve the VALU engine, FP8, SwiGLU pairs and the lm_head.)  For the lm_head it also
+// VALU and MFMA engines add their splits inside the GEMM kernel instead; these
+// kernels serve FP8, SwiGLU pairs and the lm_head.)  For the lm_head it also
 // takes, per row and per block of 256 columns, the largest logit as one
 // ordered 64-bit key (logit bits above the inverted column, so a larger key is
 // a larger logit or the same logit at a lower column); argmax_reduce then
