@@ -161,10 +161,18 @@ LaunchCfg pick_oneshot_cfg(int M, int K, int ku, int nt, Fits fits) {
   return pick_short_cfg(ku, nt, fits);
 }
 
+// Streaming choice: one workgroup per CU of about nt / 200 wavefronts, 4 to
+// 6 up to 4096 tiles and 4 to 12 beyond.  On the 2176 tiles of gate+up, six
+// wavefronts (all 256 CUs, one or two tiles each) against eleven (198 CUs,
+// one tile each) took 18.87-18.92 us against 19.40-19.99 us at M = 8,
+// 18.21-18.87 against 18.40-19.68 us at M = 5..7 and the same within noise at
+// M = 2 and 4 (and the SwiGLU pair at M = 8 18.84-18.87 against 19.48 us);
+// the 2374 tiles of one rank's lm_head took the same with 6 or 12, and the
+// whole vocabulary (9496 tiles) 73.3-73.4 us with 12 against 77.1 with 6.
 bool pick_stream_cfg(int M, int K, int N, bool argmax, LaunchCfg* out) {
   const int nt = (N + kTileCols - 1) / kTileCols;
   if (nt < 512) return false;
-  const LaunchCfg c{2, 1, std::min(12, std::max(4, (nt + 199) / 200)), 1};
+  const LaunchCfg c{2, 1, std::min(nt <= 4096 ? 6 : 12, std::max(4, (nt + 199) / 200)), 1};
   if (!nvfp4_cfg_supported(c, M, K, argmax)) return false;
   *out = c;
   return true;
