@@ -30,7 +30,11 @@
 //     row_newbcast (lane 16r + i holds the x pair that every lane of row r
 //     needs at step i), each 16-K block's sum scaled by its E4M3 scale in fp32,
 //     the four rows that split a column's K added with lane shuffles.  At
-//     M = 2 each widened code pair feeds one v_dot2c per x row.
+//     M = 2 each widened code pair feeds one v_dot2c per x row.  Its balanced
+//     layout (engine 3, the Plan's bal_* fields) keeps whole-K tiles for the
+//     largest multiple of the CU count and cuts the rest along K, so that
+//     every CU reads about the same number of weight bytes: a GEMV with one
+//     tile per workgroup lasts as long as its most loaded CUs.
 //   * MFMA (M = 1..8): v_mfma_f32_16x16x32_f16 with the widened weights
 //     (E2M1 * E4M3 in fp16, exact) as operand B and the x rows, zero-padded to
 //     16, as operand A.  The workgroup's x slice is copied into LDS with
