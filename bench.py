@@ -363,6 +363,10 @@ def read_sweep(name, steps):
                 ("persistent, 256 workgroups x 4 wavefronts, 2 blocks in flight", 4, 256, 4),
                 ("persistent, 256 workgroups x 8 wavefronts, 2 blocks in flight", 4, 256, 8),
                 ("persistent, 1024 workgroups x 4 wavefronts, 2 blocks in flight", 4, 1024, 4)]
+    for flight, pat in ((3, 5), (4, 6)):  # wavefronts per SIMD 1, 2, 4, 8 and 1, 2, 4 workgroups per CU
+        for groups, waves in ((256, 4), (256, 8), (256, 16), (512, 8), (1024, 4), (1024, 8)):
+            patterns.append((f"persistent, {groups} workgroups x {waves} wavefronts, {flight} blocks in flight",
+                             pat, groups, waves))
     out = []
     for label, pattern, a, b in patterns:
         if pattern == 3 and not 1 <= a <= 16:

@@ -399,7 +399,7 @@ int skinny_read_probe_pattern(const void* buf, size_t bytes, int pattern, int a,
       read = bytes / block * block;
       groups = bytes / block;
       break;
-    case 4:
+    case 4: case 5: case 6:
       if (a < 1 || a > 65535 || b < 1 || b > kMaxWaves) return SKINNY_EINVAL;
       block = kUnitBytes;
       read = bytes / block * block;

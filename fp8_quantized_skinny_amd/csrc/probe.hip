@@ -15,8 +15,8 @@
 //   * tiles: the NVFP4 GEMV's shape: 9 KiB units in span-major order, one
 //     workgroup per 16-column tile with one wavefront per K span.
 //   * persistent: G workgroups of W wavefronts walk the blocks (wavefront w
-//     reads blocks w, w + all wavefronts, ...) with two 9 KiB blocks in
-//     flight each.
+//     reads blocks w, w + all wavefronts, ...) with two, three or four 9 KiB
+//     blocks in flight each.
 #include <hip/hip_runtime.h>
 
 #include "common.cuh"
@@ -58,27 +58,32 @@ __global__ __launch_bounds__(1024) void read_tiles(const uint8_t* buf, int nt, u
   fold_and_sink(h, sink);
 }
 
-// Two blocks in flight per wavefront; past the end a wavefront re-reads its
-// current block (never used), so every address stays inside the blocks.
+// IN blocks in flight per wavefront: wavefront w of W reads blocks w, w + W,
+// ...; each block's loads go out IN blocks ahead of its use.  Past the end a
+// wavefront re-reads its first block (never used), so every address stays
+// inside the blocks.
+template <int IN>
 __global__ __launch_bounds__(1024) void read_persistent(const uint8_t* buf, size_t blocks, uint32_t* sink) {
   const size_t W = (static_cast<size_t>(gridDim.x) * blockDim.x) >> 6;
   const size_t w = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   if (w >= blocks) return;
   const uint8_t* base = buf + (threadIdx.x & 63) * 16;
-  u32x4 a[9], c[9], h = {0u, 0u, 0u, 0u};
+  u32x4 v[IN][9], h = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int j = 0; j < 9; ++j) a[j] = load16(base + w * kUnitBytes + j * 1024);
-  for (size_t b = w; b < blocks; b += 2 * W) {
-    const size_t b1 = b + W < blocks ? b + W : b;
+  for (int i = 0; i < IN; ++i) {
+    const size_t b = w + i * W < blocks ? w + i * W : w;
 #pragma unroll
-    for (int j = 0; j < 9; ++j) c[j] = load16(base + b1 * kUnitBytes + j * 1024);
+    for (int j = 0; j < 9; ++j) v[i][j] = load16(base + b * kUnitBytes + j * 1024);
+  }
+  for (size_t b0 = w; b0 < blocks; b0 += IN * W) {
 #pragma unroll
-    for (int j = 0; j < 9; ++j) h ^= a[j];
-    const size_t b2 = b + 2 * W < blocks ? b + 2 * W : b;
+    for (int i = 0; i < IN; ++i) {
 #pragma unroll
-    for (int j = 0; j < 9; ++j) a[j] = load16(base + b2 * kUnitBytes + j * 1024);
+      for (int j = 0; j < 9; ++j) h ^= v[i][j];
+      const size_t nb = b0 + (i + IN) * W < blocks ? b0 + (i + IN) * W : w;
 #pragma unroll
-    for (int j = 0; j < 9; ++j) h ^= c[j];
+      for (int j = 0; j < 9; ++j) v[i][j] = load16(base + nb * kUnitBytes + j * 1024);
+    }
   }
   fold_and_sink(h, sink);
 }
@@ -111,7 +116,13 @@ hipError_t launch_read_probe_pattern(const void* buf, size_t bytes, int pattern,
       break;
     }
     case 4:
-      hipLaunchKernelGGL(read_persistent, dim3(a), dim3(64 * b), 0, stream, p, bytes / kUnitBytes, sink);
+      hipLaunchKernelGGL(read_persistent<2>, dim3(a), dim3(64 * b), 0, stream, p, bytes / kUnitBytes, sink);
+      break;
+    case 5:
+      hipLaunchKernelGGL(read_persistent<3>, dim3(a), dim3(64 * b), 0, stream, p, bytes / kUnitBytes, sink);
+      break;
+    case 6:
+      hipLaunchKernelGGL(read_persistent<4>, dim3(a), dim3(64 * b), 0, stream, p, bytes / kUnitBytes, sink);
       break;
     default: return hipErrorInvalidValue;
   }

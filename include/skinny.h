@@ -450,8 +450,9 @@ int skinny_read_probe(const void* buf, size_t bytes, uint32_t* sink,
  *                    (1..16); b unused
  *   pattern 3: the NVFP4 GEMV's shape: 9 KiB units in span-major order of
  *              a K spans (1..16), one workgroup of a wavefronts per tile
- *   pattern 4: a workgroups (1..65535) of b wavefronts (1..16) walk the
- *              9 KiB blocks, two blocks in flight per wavefront
+ *   pattern 4, 5, 6: a workgroups (1..65535) of b wavefronts (1..16) walk
+ *              the 9 KiB blocks with two, three or four blocks in flight per
+ *              wavefront
  * SKINNY_EINVAL for a bad pattern, a or b; SKINNY_ESIZE if not one block
  * fits. */
 int skinny_read_probe_pattern(const void* buf, size_t bytes, int pattern,

@@ -196,13 +196,14 @@ def test_read_probe_pattern_argument_errors():
     assert call(P, 9216, 0, 1, 0, None) == sk.EINVAL
     assert call(P + 8, 9216, 0, 1, 0, P) == sk.EALIGN
     for pattern, a, b in ((0, 0, 0), (0, 17, 0), (1, 0, 0), (2, 17, 0), (3, 0, 0), (3, 17, 0), (4, 0, 1),
-                          (4, 65536, 1), (4, 1, 0), (4, 1, 17), (5, 1, 1), (-1, 1, 1)):
+                          (4, 65536, 1), (4, 1, 0), (4, 1, 17), (5, 0, 1), (6, 1, 17), (7, 1, 1), (-1, 1, 1)):
         assert call(P, 1 << 20, pattern, a, b, P) == sk.EINVAL, (pattern, a, b)
     assert call(P, 9215, 0, 1, 0, P) == sk.ESIZE
     assert call(P, 4095, 1, 1, 0, P) == sk.ESIZE
     assert call(P, 18431, 2, 4, 0, P) == sk.ESIZE
     assert call(P, 5 * 9216 - 1, 3, 5, 0, P) == sk.ESIZE
-    assert call(P, 9215, 4, 1, 1, P) == sk.ESIZE
+    for pattern in (4, 5, 6):
+        assert call(P, 9215, pattern, 1, 1, P) == sk.ESIZE
 
 
 def test_lm_head_argument_errors():
