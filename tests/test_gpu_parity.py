@@ -549,7 +549,7 @@ def test_layer_table_mixed_allocation():
 # ------------------------------------------------------------- graph replay
 def test_hip_graph_replays_match_eager():
     """Every entry point captured in one HIP graph (K-split choices with their
-    workspaces included, packed FP8 and a two-layer table too) and replayed three times, with the outputs cleared by
+    workspaces included, the balanced GEMV, packed FP8 and a two-layer table too) and replayed three times, with the outputs cleared by
     eager fills between replays: each replay equals the eager results bit for
     bit.  The benchmark times graph replays, and the library records no memset
     into a stream (workspaces are written before they are read)."""
@@ -557,11 +557,13 @@ def test_hip_graph_replays_match_eager():
     f8 = workload.fp8_case(4, 1040, 640, seed=52)
     sw = workload.swiglu_case(8, 2064, 72, seed=53)
     lm = workload.nvfp4_case(8, 1024, 3000, seed=54)
+    bal = workload.nvfp4_case(2, 2064, 4800, seed=55)      # 300 tiles: engine 3 cuts the last 44 along K
     want_idx = oracle.argmax_rows(ref_nvfp4(lm))[0]
     drafts = dev(np.asarray(want_idx[:7], np.int32))
     bufs = {"nv": dev(nv["blob"]), "nvx": dev(nv["x"]), "f8c": dev(f8["codes"]), "f8s": dev(f8["scales"]),
             "f8x": dev(f8["x"]), "sw": dev(sw["blob"]), "swx": dev(sw["x"]), "lm": dev(lm["blob"]), "lmx": dev(lm["x"]),
-            "f8p": dev(sk.fp8_pack(f8["codes"], 1040, 640)), "nvx4": dev(nv["x"][:4])}
+            "f8p": dev(sk.fp8_pack(f8["codes"], 1040, 640)), "nvx4": dev(nv["x"][:4]),
+            "bal": dev(bal["blob"]), "balx": dev(bal["x"])}
     # a two-layer table at M = 4: NVFP4 then packed FP8 (independent inputs)
     layers = [(sk.LAYER_NVFP4, bufs["nv"], None, 2064, 1000), (sk.LAYER_FP8_PACKED, bufs["f8p"], bufs["f8s"], 1040, 640)]
     outs = {"y_nv": torch.empty((8, 1000), dtype=torch.float16, device="cuda"),
@@ -574,14 +576,16 @@ def test_hip_graph_replays_match_eager():
             "res": torch.empty((9,), dtype=torch.int32, device="cuda"),
             "y_f8p": torch.empty((4, 640), dtype=torch.float16, device="cuda"),
             "ly_nv": torch.empty((4, 1000), dtype=torch.float16, device="cuda"),
-            "ly_f8p": torch.empty((4, 640), dtype=torch.float16, device="cuda")}
+            "ly_f8p": torch.empty((4, 640), dtype=torch.float16, device="cuda"),
+            "y_bal": torch.empty((2, 4800), dtype=torch.float16, device="cuda")}
     split = (1, 2, 4, 2)                                   # three K spans over two workgroups
     f8split = (1, 1, 1, 3)
     wss = {k: ws_for(op, M, K, N, cfg) for k, (op, M, K, N, cfg) in {
         "nv": (sk.OP_NVFP4, 8, 2064, 1000, None), "nv_split": (sk.OP_NVFP4, 8, 2064, 1000, split),
         "f8": (sk.OP_FP8, 4, 1040, 640, f8split), "sw": (sk.OP_SWIGLU, 8, 2064, 72, None),
         "sw_split": (sk.OP_SWIGLU, 8, 2064, 72, split), "lm": (sk.OP_LM_HEAD, 8, 1024, 3000, None),
-        "lmv": (sk.OP_LM_HEAD, 8, 1024, 3000, None), "f8p": (sk.OP_FP8, 4, 1040, 640, f8split)}.items()}
+        "lmv": (sk.OP_LM_HEAD, 8, 1024, 3000, None), "f8p": (sk.OP_FP8, 4, 1040, 640, f8split),
+        "bal": (sk.OP_NVFP4, 2, 2064, 4800, (3, 1, 3, 1))}.items()}
     n_layers = sk.layers_workspace_bytes(layers, 4)
     wss["layers"] = sk.new_workspace(n_layers)
     assert wss["nv_split"] is not None and wss["f8"] is not None and wss["sw_split"] is not None
@@ -601,6 +605,7 @@ def test_hip_graph_replays_match_eager():
                            stream=stream)
         sk.layers_run(layers, [bufs["nvx4"], bufs["f8x"]], [outs["ly_nv"], outs["ly_f8p"]], workspace=wss["layers"],
                       stream=stream)
+        sk.nvfp4_gemm(bufs["bal"], bufs["balx"], outs["y_bal"], config=(3, 1, 3, 1), workspace=wss["bal"], stream=stream)
 
     calls(torch.cuda.current_stream())
     torch.cuda.synchronize()
@@ -612,6 +617,7 @@ def test_hip_graph_replays_match_eager():
     assert torch.equal(eager["y_f8p"], eager["y_f8"]), "packed FP8 differs from canonical FP8"
     _check(eager["ly_nv"].float().cpu().numpy(), ref_nvfp4(nv, 4), "graph test eager layer table, NVFP4 layer")
     _check(eager["ly_f8p"].float().cpu().numpy(), ref_fp8(f8), "graph test eager layer table, packed FP8 layer")
+    _check(eager["y_bal"].float().cpu().numpy(), ref_nvfp4(bal), "graph test eager balanced GEMV")
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     with torch.cuda.stream(cap):

@@ -66,3 +66,23 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
     from fp8_quantized_skinny_amd._lib import lib
     st = lib().nvfp4_gemm_noalloc(blob.data_ptr(), x.data_ptr(), y.data_ptr(), 8, 1 << 20, 4096, None)
     assert st == sk.ESIZE
+
+
+def test_noalloc_balanced_gemv():
+    """A GEMV whose library choice is the balanced layout (engine 3: 800 tiles on 256 CUs, the last
+    32 cut into two K-split workgroups each, added through counters in the library's array): the
+    allocation-free call equals the workspace call bit for bit, twice in a row."""
+    case = workload.nvfp4_case(1, 2048, 12800, seed=93)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert sk.default_config(sk.OP_NVFP4, 1, 2048, 12800)[0] == 3
+    ys = []
+    for _ in range(2):
+        y = torch.full((1, 12800), float("nan"), dtype=torch.float16, device="cuda")
+        sk.nvfp4_gemm_noalloc(dev(case["blob"]), dev(case["x"]), y)
+        ys.append(y)
+    want = _with_workspace(case, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], want) and torch.equal(ys[1], want)
+    ref = oracle.nvfp4_gemm(case["x"], case["codes"], case["scales"], case["g"])
+    m = oracle.compare(want.float().cpu().numpy(), ref)
+    assert m["rel_frob"] <= 2e-3 and m["row_max"] <= 1e-2, m
