@@ -116,7 +116,7 @@ struct Plan {
     S = a.S;
     ks = a.ksplit;
     small = false;
-    if (a.bal_small > 0) {  // balanced GEMV (ct = 1, nw = ku)
+    if (a.bal_small > 0) {  // balanced GEMV (ct = 1, nw >= ku, S = nw)
       const int b = blockIdx.x;
       small = b < a.bal_small;
       if (small) {
@@ -136,7 +136,8 @@ struct Plan {
       }
       t = wave / S;
       s = wave % S;
-      // A small workgroup has nw = ku wavefronts for its S spans: the rest idle.
+      // Every workgroup of the grid has nw >= ku wavefronts: those past a
+      // workgroup's spans (all but S of a small one) idle.
       active = t == 0 && s < sw && (!small || group < a.bal_r);
       return;
     }
