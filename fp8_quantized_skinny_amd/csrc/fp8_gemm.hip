@@ -23,11 +23,12 @@
 // plain stores and added in split order by the reduction kernel).  The MFMA
 // engine copies x into LDS once per workgroup with direct-to-LDS loads.
 // Both engines contract, per chunk j, lane (grp, c)'s two 16-byte pieces
-// K = 128j + 64h + 16grp .. +16 (h = 0, 1) of column c.  Canonical codes are
-// not loaded in that layout (it would read every 128-byte line as two halves
-// from two instructions): each load reads eight whole lines and a small
-// per-wavefront LDS tile rearranges them into the pieces.  Pieces past K or
-// columns past N read a clamped valid address and are zeroed.
+// K = 128j + 32grp + 16h .. +16 (h = 0, 1) of column 8(c % 2) + c / 2 of the
+// tile.  Canonical codes are not loaded in that layout (it would read every
+// 128-byte line as two halves from two instructions): each load reads eight
+// whole lines, and selects with one-lane DPP shifts merge a chunk's two loads
+// into the pieces.  Pieces past K or columns past N read a clamped valid address and
+// are zeroed.
 //
 // The packed variant reads the same pieces from a blob of fp8_pack: 8 KiB
 // units (one tile x 512 K) in span-major order, in which piece 2j + h of a
@@ -91,19 +92,24 @@ __device__ void fp8_stage_x(const Fp8Args& a, const Fp8Plan& P, _Float16* xs) {
   }
 }
 
+// Column of the tile held by lane c of a 16-lane row in the compute layout:
+// even lanes hold columns 0..7, odd lanes 8..15, so that both canonical
+// loads of a chunk merge into it with one-lane shifts (below).
+__device__ __forceinline__ int fp8_lane_col(int c) { return 8 * (c & 1) + (c >> 1); }
+
 // Canonical codes, whole lines per load: load i of a unit (tile t, K range
-// 512u ..) gives lane (c, p) = (lane / 8, lane % 8) the 16 bytes
-// K = 512u + 128(i % 4) + 16p .. +16 of column 16t + 8(i / 4) + c, so the
-// eight lanes of a column cover one 128-byte line and each instruction eight
-// whole lines.  (Reading the tile in the compute layout instead, sixteen half
-// lines per instruction and two instructions per line, ran at about three
-// quarters of the whole-line read rate.)  Loads go out in the order
-// 0, 4, 1, 5, ... so that chunk j (loads j and 4 + j) is complete after its
-// first 2(j + 1) loads.  Pieces past K read the row start instead (K % 16 ==
-// 0: a piece is all in or all out); their x is zero.
+// 512u ..) gives lane 16q + i' the 16 bytes K = 512u + 128(i % 4) + 16p .. +16
+// with p = 2q + i' % 2 of column 16t + 8(i / 4) + i' / 2: each lane pair reads
+// 32 consecutive bytes and each instruction eight whole 128-byte lines.
+// (Reading the tile in the compute layout instead, sixteen half lines per
+// instruction and two instructions per line, ran at about three quarters of
+// the whole-line read rate.)  Loads go out in the order 0, 4, 1, 5, ... so
+// that chunk j (loads j and 4 + j) is complete after its first 2(j + 1)
+// loads.  Pieces past K read the row start instead (K % 16 == 0: a piece is
+// all in or all out); their x is zero.
 __device__ __forceinline__ void fp8_load_lines(u32x4 (&v)[2 * kFp8UnitChunks], const Fp8Args& a, int tt, int u,
                                                int lane) {
-  const int c8 = lane >> 3, p = lane & 7;
+  const int c8 = (lane & 15) >> 1, p = 2 * (lane >> 4) + (lane & 1);
 #pragma unroll
   for (int j = 0; j < kFp8UnitChunks; ++j) {
 #pragma unroll
@@ -115,71 +121,63 @@ __device__ __forceinline__ void fp8_load_lines(u32x4 (&v)[2 * kFp8UnitChunks], c
   }
 }
 
-// Per-wavefront LDS slot: first the tile through which the loads above are
-// rearranged into the compute layout, one chunk at a time (16 rows of 128
-// bytes, one per column, padded to 144 to stagger the rows over the LDS
-// banks), then the wavefront's partial tile sums (MFMA engine).  A tile of
-// half a chunk (rows of 64 bytes, every lane writing half the time) took
-// 0.1-0.2 us more on the 5120 x 7168 and 6144 x 5120 weights at M = 4.
-constexpr int kLineRowBytes = 144;
-constexpr int kWaveSlotBytes = kTileCols * kLineRowBytes;
-static_assert(kWaveSlotBytes >= 32 * 16, "slot holds the reduction entry");
-
-// Orders this wavefront's LDS accesses of different lanes: stores before the
-// fence are seen by loads after it, and loads before it read their data
-// before stores after it land.  The hardware runs one wavefront's LDS
-// operations in order; the fences and the wave barrier keep the compiler
-// from moving an access across (to one lane's view the accesses of the
-// others do not exist).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Both pieces of a chunk in the compute (and packed) layout from its two
+// whole-line loads lo (columns 0..7) and hi (columns 8..15).  In row grp,
+// lanes 2c and 2c + 1 of lo hold pieces 2grp and 2grp + 1 of column c, and
+// the same lanes of hi those of column 8 + c.  w0 (piece 2grp) keeps lo's
+// even lanes and takes hi's even lanes one lane up; w1 (piece 2grp + 1) keeps
+// hi's odd lanes and takes lo's odd lanes one lane down.  The shifts (DPP
+// row_shr:1 / row_shl:1) run in every lane, since a DPP read of a lane that
+// a branch switched off gives 0; only the selects depend on the lane.  (The
+// same merge as v_cndmask_b32 with a DPP operand in inline asm, half the
+// instructions, measured no faster at M = 4 and 0.1 us slower at M = 1.)
+constexpr int kRowShl1 = 0x101, kRowShr1 = 0x111;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_shift(uint32_t from) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(from), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ void fp8_line_merge(const u32x4& lo, const u32x4& hi, u32x4& w0, u32x4& w1) {
+  const bool odd = (threadIdx.x & 1) != 0;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t up = dpp_shift<kRowShr1>(hi[d]), down = dpp_shift<kRowShl1>(lo[d]);
+    w0[d] = odd ? up : lo[d];
+    w1[d] = odd ? hi[d] : down;
+  }
 }
 
-// Both pieces of chunk j in the compute (and packed) layout: lane (grp, c)
-// gets in w0 (h = 0) and w1 (h = 1) the 16 bytes K = 128j + 64h + 16grp ..
-// +16 of column c.  Load j (columns 0..7) or 4 + j (columns 8..15) gave
-// lane (c8, p) the 16 bytes K = 128j + 16p of column c8 or 8 + c8, which go
-// to row c8 or 8 + c8 of the tile at byte 16p.  Only this wavefront touches
-// `tile`.
-__device__ __forceinline__ void fp8_line_chunk(const u32x4 (&v)[2 * kFp8UnitChunks], int j, unsigned char* tile,
-                                               int lane, u32x4& w0, u32x4& w1) {
-  const int c8 = lane >> 3, p = lane & 7;
-  wave_lds_sync();  // the previous chunk's reads are done with the tile
-  *reinterpret_cast<u32x4*>(tile + c8 * kLineRowBytes + 16 * p) = v[j];
-  *reinterpret_cast<u32x4*>(tile + (8 + c8) * kLineRowBytes + 16 * p) = v[4 + j];
-  wave_lds_sync();
-  const unsigned char* row = tile + (lane & 15) * kLineRowBytes + 16 * (lane >> 4);
-  w0 = *reinterpret_cast<const u32x4*>(row);
-  w1 = *reinterpret_cast<const u32x4*>(row + 64);
-}
+// Per-wavefront LDS slot of the MFMA engine: the wavefront's partial tile
+// sums (32 lanes x 16 bytes).
+constexpr int kWaveSlotBytes = 32 * 16;
 
 // A fragments of chunk j: lane (row c, grp) holds, for MFMA i = 2h + s,
-// x[min(c, M-1)][512u + 128j + 64h + 16grp + 8s .. +8].  Rows c >= M only
-// feed output rows that are never stored, so they repeat row M-1.
+// x[min(c, M-1)][512u + 128j + 32grp + 16h + 8s .. +8], i.e. the 32 halves
+// from 128j + 32grp in order.  Rows c >= M only feed output rows that are
+// never stored, so they repeat row M-1.
 __device__ __forceinline__ void fp8_read_x(f16x8 (&xa)[4], const _Float16* xrow, int j) {
   const _Float16* p = xrow + j * kChunkK;
-  xa[0] = *reinterpret_cast<const f16x8*>(p);
-  xa[1] = *reinterpret_cast<const f16x8*>(p + 8);
-  xa[2] = *reinterpret_cast<const f16x8*>(p + 64);
-  xa[3] = *reinterpret_cast<const f16x8*>(p + 72);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const f16x8*>(p + 8 * i);
 }
 
-template <int J>
-__device__ __forceinline__ void fp8_steps(const u32x4 (&w)[kFp8UnitChunks][2], const float (&sc)[kFp8UnitChunks],
-                                          f16x8 (&x0)[4], f16x8 (&x1)[4], f32x4& acc, const _Float16* xrow) {
+// Chunk J and on; canonical codes are merged into the compute layout just
+// before their chunk, so a chunk waits for its own two loads only.
+template <int J, bool PACKED>
+__device__ __forceinline__ void fp8_steps(u32x4 (&w)[kFp8UnitChunks][2], const u32x4 (&v)[2 * kFp8UnitChunks],
+                                          const float (&sc)[kFp8UnitChunks], f16x8 (&x0)[4], f16x8 (&x1)[4],
+                                          f32x4& acc, const _Float16* xrow) {
   if constexpr (J < kFp8UnitChunks) {
     f16x8 (&cur)[4] = (J & 1) ? x1 : x0;
     f16x8 (&nxt)[4] = (J & 1) ? x0 : x1;
     if constexpr (J + 1 < kFp8UnitChunks) fp8_read_x(nxt, xrow, J + 1);
+    if constexpr (!PACKED) fp8_line_merge(v[J], v[4 + J], w[J][0], w[J][1]);
     f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[0], e4m3x8(w[J][0].x, w[J][0].y), p, 0, 0, 0);
     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[1], e4m3x8(w[J][0].z, w[J][0].w), p, 0, 0, 0);
     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[2], e4m3x8(w[J][1].x, w[J][1].y), p, 0, 0, 0);
     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[3], e4m3x8(w[J][1].z, w[J][1].w), p, 0, 0, 0);
     acc += sc[J] * p;
-    fp8_steps<J + 1>(w, sc, x0, x1, acc, xrow);
+    fp8_steps<J + 1, PACKED>(w, v, sc, x0, x1, acc, xrow);
   }
 }
 
@@ -209,6 +207,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
     const float* srow = a.scales + static_cast<size_t>(min(tt * kTileCols, a.N - 1) / 128) * a.kb;
 #pragma unroll
     for (int j = 0; j < kFp8UnitChunks; ++j) sc[j] = srow[min(u * kFp8UnitChunks + j, a.kb - 1)];
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the codes'
     // Codes: pieces past K load from the row start instead (x is zero there,
     // so they add exact zeros); no select on loaded data, which would make
     // every load wait for the previous one.
@@ -228,25 +227,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
   }
   // x is in LDS once every wavefront's copies are done; the weights keep arriving.
   lds_copy_barrier<2 * kFp8UnitChunks>(true);
-  if (!PACKED) {
-#pragma unroll
-    for (int j = 0; j < kFp8UnitChunks; ++j) {
-      fp8_line_chunk(v, j, slot, P.lane, w[j][0], w[j][1]);
-    }
-  }
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (P.active) {
-    const _Float16* xrow = xs + min(cl, a.M - 1) * fp8_xs_stride(P.S) + P.s * kFp8UnitK + grp * 16;
+    const _Float16* xrow = xs + min(cl, a.M - 1) * fp8_xs_stride(P.S) + P.s * kFp8UnitK + grp * 32;
     f16x8 x0[4], x1[4];
     fp8_read_x(x0, xrow, 0);
-    fp8_steps<0>(w, sc, x0, x1, acc, xrow);
+    fp8_steps<0, PACKED>(w, v, sc, x0, x1, acc, xrow);
   }
   if (P.lane < 32) reinterpret_cast<f32x4*>(slot)[P.lane] = acc;
   __syncthreads();
 
   const bool fin = P.wave < CT && P.tile0 + P.wave < a.nt && P.lane < 32;
-  const int n = (P.tile0 + P.wave) * kTileCols + cl;
+  const int n = (P.tile0 + P.wave) * kTileCols + fp8_lane_col(cl);
   if (fin && n < a.N) {
     f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < P.sw; ++s)
@@ -491,13 +484,13 @@ __device__ __forceinline__ void fp8_half_dot(float (&p)[MR], const uint32_t (&xv
 
 // One unit per wavefront, as in the MFMA engine; lane 16r + q holds, for each
 // chunk j and row m, the x pair the lanes of its row r need at step q % 8 of
-// half q / 8: x[m][512u + 128j + 64(q/8) + 16r + 2(q%8) ..+2].  Each chunk's
+// half q / 8: x[m][512u + 128j + 32r + 16(q/8) + 2(q%8) ..+2], which is
+// x[m][512u + 128j + 32r + 2q ..+2].  Each chunk's
 // sum over its 128 K is multiplied by its block scale in fp32.  x needs no
 // LDS copy.  MR rows per instance (M = 3 runs as MR = 4: its fourth row
 // reads row 2 again and is never stored).
 template <int CT, bool PACKED, int MR>
 __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // canonical codes: [nw][kWaveSlotBytes]
   __shared__ float red[kMaxWaves][MR][16];
   const Fp8Plan P(a, CT);
   const int q = P.lane & 15, r = P.lane >> 4;
@@ -517,7 +510,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
   u32x4 w[kFp8UnitChunks][2];
   u32x4 v[2 * kFp8UnitChunks];  // canonical codes as loaded (whole lines)
   uint32_t xv[kFp8UnitChunks][MR];
-  const int kx = u * kFp8UnitK + 64 * (q >> 3) + 16 * r + 2 * (q & 7);
+  const int kx = u * kFp8UnitK + 32 * r + 2 * q;
   const _Float16* xr[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) xr[m] = a.x + static_cast<size_t>(min(m, a.M - 1)) * a.K;
@@ -542,11 +535,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
       for (int m = 0; m < MR; ++m)
         xv[j][m] = *reinterpret_cast<const uint32_t*>(xr[m] + min(kx + j * kChunkK, a.K - 2));
     }
-    unsigned char* slot = lds + P.wave * kWaveSlotBytes;
-#pragma unroll
-    for (int j = 0; j < kFp8UnitChunks; ++j) {
-      fp8_line_chunk(v, j, slot, P.lane, w[j][0], w[j][1]);
-    }
   }
   float acc[MR];
 #pragma unroll
@@ -561,6 +549,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
       // would still give 0 * x = NaN: a unit that straddles K (wave-uniform)
       // selects too, which no full unit does.
       const bool in = (!PACKED || straddles) ? kx + j * kChunkK < a.K : true;
+      if (!PACKED) fp8_line_merge(v[j], v[4 + j], w[j][0], w[j][1]);
       uint32_t x[MR];
       float p[MR];
 #pragma unroll
@@ -577,7 +566,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     const float v = sum_over_rows(acc[m]);
-    if (P.lane < 16) red[P.wave][m][P.lane] = v;
+    if (P.lane < 16) red[P.wave][m][fp8_lane_col(P.lane)] = v;
   }
   __syncthreads();
 
@@ -621,13 +610,12 @@ bool fp8_cfg_supported(const LaunchCfg& c, int M, int K) {
 // The VALU engine's instance for M rows (M = 3 runs as four rows).
 template <int CT, bool PACKED>
 void launch_fp8_valu_rows(const Fp8Args& a, dim3 grid, dim3 blk, hipStream_t stream) {
-  const size_t lds = PACKED ? 0 : static_cast<size_t>(blk.x / 64) * kWaveSlotBytes;
   if (a.M == 1)
-    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 1>), grid, blk, lds, stream, a);
+    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 1>), grid, blk, 0, stream, a);
   else if (a.M == 2)
-    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 2>), grid, blk, lds, stream, a);
+    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 2>), grid, blk, 0, stream, a);
   else
-    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 4>), grid, blk, lds, stream, a);
+    hipLaunchKernelGGL((fp8_valu<CT, PACKED, 4>), grid, blk, 0, stream, a);
 }
 
 template <int CT>

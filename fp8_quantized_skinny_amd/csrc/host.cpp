@@ -584,16 +584,16 @@ int fp8_pack(const uint8_t* codes, int K, int N, void* out, size_t* out_bytes) {
   h.units_bytes = total - kHeaderBytes;
   std::memcpy(blob, &h, sizeof(h));
   // Piece q = 2j + h of unit (t, u), lane l = 16grp + c: 16 codes of column
-  // 16t + c from K = 512u + 128j + 64h + 16grp on (K % 16 == 0: a run is all
-  // in or all out of range).
+  // 16t + 8(c % 2) + c / 2 from K = 512u + 128j + 32grp + 16h on (K % 16 ==
+  // 0: a run is all in or all out of range).
   parallel_for(nt, [&](int, int t0, int t1) {
     for (int t = t0; t < t1; ++t)
       for (int u = 0; u < ku; ++u) {
         uint8_t* unit = blob + kHeaderBytes + (static_cast<size_t>(u) * nt + t) * kFp8UnitBytes;
         for (int q = 0; q < 8; ++q)
           for (int lane = 0; lane < 64; ++lane) {
-            const int n = t * kTileCols + (lane & 15);
-            const int k = u * kFp8PackK + (q >> 1) * 128 + (q & 1) * 64 + (lane >> 4) * 16;
+            const int n = t * kTileCols + 8 * (lane & 1) + ((lane & 15) >> 1);
+            const int k = u * kFp8PackK + (q >> 1) * 128 + (lane >> 4) * 32 + (q & 1) * 16;
             if (n < N && k < K)
               std::memcpy(unit + q * 1024 + lane * 16, codes + static_cast<size_t>(n) * K + k, 16);
           }

@@ -86,12 +86,12 @@ Geometry nvfp4_geometry(int K, int N);
 //
 // Unit (t, u) covers columns 16t .. 16t+15 and K 512u .. 512u+511: eight
 // 1 KiB pieces q = 2j + h; in piece q, lane l = 16*grp + c owns bytes
-// [16l, 16l+16): the E4M3 codes of column 16t+c at K = 512u + 128j + 64h +
-// 16grp + i (i = 0..15).  K is padded to a multiple of 512 and N to a
+// [16l, 16l+16): the E4M3 codes of column 16t + 8(c%2) + c/2 at K = 512u +
+// 128j + 32grp + 16h + i (i = 0..15).  K is padded to a multiple of 512 and N to a
 // multiple of 16 with zero codes.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kFp8BlobMagic = 0x38464B53u;  // "SKF8" little-endian
-constexpr uint32_t kFp8BlobVersion = 1;
+constexpr uint32_t kFp8BlobVersion = 2;
 constexpr int kFp8PackK = 512;
 constexpr size_t kFp8UnitBytes = 8192;
 struct Fp8Header {

@@ -409,17 +409,18 @@ def test_fp8_pack_places_every_byte_once(K, N):
     ku, nt = -(-K // 512), -(-N // 16)
     assert blob.size == 256 + ku * nt * 8192 == sk.fp8_packed_bytes(K, N)
     h = blob[:64]
-    assert bytes(h[:4]) == b"SKF8" and list(h[4:32].view(np.uint32)) == [1, K, N, ku, nt, 8192, 0]
+    assert bytes(h[:4]) == b"SKF8" and list(h[4:32].view(np.uint32)) == [2, K, N, ku, nt, 8192, 0]
     units = blob[256:].reshape(ku, nt, 8, 4, 16, 16)                   # [span][tile][piece][grp][c][byte]
     seen = np.zeros(codes.shape, np.int64)
     mask = np.zeros(units.shape, bool)
     for n in range(N):
-        t, c = divmod(n, 16)
+        t, col = divmod(n, 16)
+        c = 2 * (col % 8) + col // 8                                     # lane c holds column 8(c%2) + c//2
         for k in range(K):
             u, r = divmod(k, 512)
             j, r = divmod(r, 128)
-            hh, r = divmod(r, 64)
-            grp, i = divmod(r, 16)
+            grp, r = divmod(r, 32)
+            hh, i = divmod(r, 16)
             assert units[u, t, 2 * j + hh, grp, c, i] == codes[n, k]
             seen[n, k] += 1
             mask[u, t, 2 * j + hh, grp, c, i] = True
