@@ -46,12 +46,19 @@ __device__ __forceinline__ float e4m3f(uint32_t w) {
 }
 
 // Sum of v over lanes {l, l^16, l^32, l^48}: the four 16-lane rows of a
-// wavefront, exchanged with ds_bpermute lane shuffles.  Every lane ends with
-// the same value, (v0 + v2) + (v1 + v3) for rows 0..3.
+// wavefront.  Every lane ends with the same value, (v0 + v2) + (v1 + v3) for
+// rows 0..3.  The rows move with gfx950's permlane swaps, which run in the
+// VALU: v_permlane32_swap of two copies of v leaves rows (0, 1, 0, 1) in one
+// and (2, 3, 2, 3) in the other, v_permlane16_swap then rows (0, 0, 2, 2) and
+// (1, 1, 3, 3).  Lane shuffles (ds_bpermute) gave the same sums but waited for
+// an LDS round trip each.  Every lane of the wavefront must be active.
 __device__ __forceinline__ float sum_over_rows(float v) {
-  v += __shfl_xor(v, 32);
-  v += __shfl_xor(v, 16);
-  return v;
+  const uint32_t u = __float_as_uint(v);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const uint32_t w = __float_as_uint(v);
+  const auto q = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most `vm` vector
