@@ -129,32 +129,61 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
   return (static_cast<unsigned long long>(ord) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(n));
 }
 
-// Largest key over the WIDTH lanes of each lane group (every lane gets it).
-template <int WIDTH = 64>
-__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
-#pragma unroll
-  for (int off = WIDTH / 2; off >= 1; off >>= 1) {
-    const unsigned long long o = __shfl_xor(k, off, WIDTH);
-    k = o > k ? o : k;
+// The larger of lane l's key and its partner's in one step of a max
+// reduction over lane groups: the partner is lane l ^ 32 (OFF = 32) or
+// l ^ 16 (OFF = 16), exchanged with gfx950's permlane swaps, or lane
+// (l - OFF) mod 16 of the same 16-lane row (OFF = 8, 4, 2, 1), read through
+// DPP row_ror.  Rotating by 8, 4, 2 and 1 covers a row as xor partners do, so
+// steps OFF = WIDTH/2 .. 1 leave every lane with the largest key of its WIDTH
+// lanes.  Both halves of the 64-bit key move the same way.  All VALU, no LDS
+// round trip; every lane of the wavefront must be active.
+template <int OFF>
+__device__ __forceinline__ unsigned long long max_with_partner(unsigned long long k) {
+  static_assert(OFF == 32 || OFF == 16 || OFF == 8 || OFF == 4 || OFF == 2 || OFF == 1, "partner offset");
+  const uint32_t lo = static_cast<uint32_t>(k), hi = static_cast<uint32_t>(k >> 32);
+  unsigned long long a, b;
+  if constexpr (OFF >= 16) {
+    // Each swap of two copies leaves the lane's own value in one result and
+    // its partner's in the other.
+    const auto l = OFF == 32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                             : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = OFF == 32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                             : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    a = (static_cast<unsigned long long>(h[0]) << 32) | l[0];
+    b = (static_cast<unsigned long long>(h[1]) << 32) | l[1];
+  } else {
+    constexpr int kRowRor = 0x120 + OFF;  // DPP row_ror:OFF
+    const uint32_t plo = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(lo), kRowRor, 0xf, 0xf, false));
+    const uint32_t phi = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(hi), kRowRor, 0xf, 0xf, false));
+    a = (static_cast<unsigned long long>(phi) << 32) | plo;
+    b = k;
   }
-  return k;
+  return a > b ? a : b;
 }
 
-// Largest key of each of R independent values over the WIDTH lanes of each
-// lane group (every lane gets them).  Each shuffle step exchanges all R
-// values before comparing any, so the R reductions share one LDS round trip
-// per step; reducing them one after another waits for a round trip at every
-// step of every value (6 x R waits over 64 lanes).
+// Largest key of each of R independent values over the WIDTH lanes (16 or 64)
+// of each lane group; every lane gets them.  Every lane must be active.
 template <int R, int WIDTH = 64>
 __device__ __forceinline__ void wave_max_keys(unsigned long long (&k)[R]) {
+  static_assert(WIDTH == 16 || WIDTH == 64, "lane group");
+  if constexpr (WIDTH == 64) {
 #pragma unroll
-  for (int off = WIDTH / 2; off >= 1; off >>= 1) {
-    unsigned long long o[R];
+    for (int r = 0; r < R; ++r) k[r] = max_with_partner<1>(max_with_partner<2>(max_with_partner<4>(
+                                        max_with_partner<8>(max_with_partner<16>(max_with_partner<32>(k[r]))))));
+  } else {
 #pragma unroll
-    for (int r = 0; r < R; ++r) o[r] = __shfl_xor(k[r], off, WIDTH);
-#pragma unroll
-    for (int r = 0; r < R; ++r) k[r] = o[r] > k[r] ? o[r] : k[r];
+    for (int r = 0; r < R; ++r)
+      k[r] = max_with_partner<1>(max_with_partner<2>(max_with_partner<4>(max_with_partner<8>(k[r]))));
   }
+}
+
+template <int WIDTH = 64>
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+  unsigned long long one[1] = {k};
+  wave_max_keys<1, WIDTH>(one);
+  return one[0];
 }
 
 }  // namespace skinny

@@ -29,7 +29,7 @@
 //   * VALU (M = 1, 2): v_dot2c_f32_f16 whose x operand is read through DPP
 //     row_newbcast (lane 16r + i holds the x pair that every lane of row r
 //     needs at step i), each 16-K block's sum scaled by its E4M3 scale in fp32,
-//     the four rows that split a column's K added with lane shuffles.  At
+//     the four rows that split a column's K added with permlane swaps.  At
 //     M = 2 each widened code pair feeds one v_dot2c per x row.  Its balanced
 //     layout (engine 3, the Plan's bal_* fields) keeps whole-K tiles for the
 //     largest multiple of the CU count and cuts the rest along K, so that
