@@ -82,11 +82,14 @@ struct Nvfp4Args {
 enum : int { kEpiPlain = 0, kEpiArgmax = 1, kEpiSwiglu = 2 };
 
 // SwiGLU of a pair-interleaved tile: the lane of gate column c < 8 takes its
-// up sum from lane c + 8 (same row group) and returns silu(g * gate) * (g2 *
-// up); lanes c >= 8 get a value that is never stored.  Every lane of the
-// 16-lane row must execute this.
+// up sum from lane c + 8 (same row group, DPP row_ror:8: a rotation by half a
+// row pairs lanes c and c ^ 8 without an LDS round trip) and returns
+// silu(g * gate) * (g2 * up); lanes c >= 8 get a value that is never stored.
+// Every lane of the 16-lane row must execute this.
 __device__ __forceinline__ float swiglu_pair(float sum, float g, float g2) {
-  const float up = __shfl_xor(sum, 8);
+  constexpr int kRowRor8 = 0x128;
+  const float up = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), kRowRor8, 0xf, 0xf, false));
   return silu(g * sum) * (g2 * up);
 }
 
