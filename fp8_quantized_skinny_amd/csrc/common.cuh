@@ -179,6 +179,7 @@ __device__ __forceinline__ void wave_max_keys(unsigned long long (&k)[R]) {
   }
 }
 
+// The same for one value.
 template <int WIDTH = 64>
 __device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
   unsigned long long one[1] = {k};
