@@ -163,6 +163,34 @@ def test_fp8_one_hot_reproduces_codes_exactly():
                 assert np.array_equal(got, deq[r0:r0 + 3]), f"VALU config {cfg} packed={packed} rows {r0}..+3"
 
 
+def test_fp8_one_hot_exact_over_several_units():
+    """The same over three 512-K units with a ragged last unit (K = 1040) and a
+    ragged last tile (N = 40): every K row of every unit, chunk and piece lands
+    on its own column, canonical and packed, in the MFMA engine (every row) and
+    the VALU engine (a sample of rows)."""
+    K, N = 1040, 40
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C
+    scales = np.ldexp(1.0, rng.integers(-6, 2, size=(1, 9))).astype(np.float32)
+    case = {"codes": codes, "scales": scales, "K": K, "N": N}
+    deq = oracle.fp8_dequant(codes, scales)
+    assert np.array_equal(deq.astype(np.float16).astype(np.float64), deq)
+    eye = np.eye(K, dtype=np.float16)
+    for packed in (False, True):
+        for cfg in cfgs(1, K, unit_k=512, cts=(1, 4)):
+            out = np.empty((K, N))
+            for r0 in range(0, K, 8):
+                case["x"] = eye[r0:r0 + 8]
+                out[r0:r0 + 8] = run_fp8(case, M=8, config=cfg, packed=packed)
+            assert np.array_equal(out, deq), f"config {cfg} packed={packed}: {np.argwhere(out != deq)[:5]}"
+        for cfg in cfgs(0, K, unit_k=512, cts=(1, 2)):
+            for r0 in list(range(0, K, 5)) + [K - 1]:
+                case["x"] = eye[r0:r0 + 1]
+                got = run_fp8(case, M=1, config=cfg, packed=packed)
+                assert np.array_equal(got[0], deq[r0]), f"VALU config {cfg} packed={packed} row {r0}"
+
+
 # -------------------------------------------------------- tolerance parity
 @pytest.mark.parametrize("shape", SMALL_NVFP4)
 def test_nvfp4_parity_all_configs(small_nvfp4, shape):
