@@ -132,6 +132,29 @@ def test_nvfp4_one_hot_reproduces_dequantized_weights_exactly(K, N):
             assert np.array_equal(out, deq), f"config {cfg} rows {rows}: {np.argwhere(out != deq)[:5]}"
 
 
+def test_nvfp4_one_hot_exact_in_the_balanced_gemv():
+    """The balanced GEMV (engine 3) over several spans with a ragged last span (K = 3088)
+    and 257 tiles, so 256 whole-K tiles and one tile cut into K-split workgroups added
+    inside the kernel: with g = 1 and one-hot rows, every weight comes out exactly, at
+    M = 1 and 2."""
+    K, N = 3088, 4112
+    case = workload.nvfp4_case(1, K, N, seed=9)
+    blob = dev(sk.nvfp4_pack(case["codes"], case["scales"], 1.0, K, N))
+    deq = oracle.nvfp4_dequant_unscaled(case["codes"], case["scales"], K)       # [K, N]
+    assert np.array_equal(deq.astype(np.float16).astype(np.float64), deq)
+    cfg = (3, 1, -(-K // 1024), 1)
+    eye = torch.eye(K, dtype=torch.float16, device="cuda")
+    for rows in (1, 2):
+        assert sk.config_supported(sk.OP_NVFP4, rows, K, N, cfg)
+        ws = ws_for(sk.OP_NVFP4, rows, K, N, cfg)
+        out = torch.empty((K, N), dtype=torch.float16, device="cuda")
+        for r0 in range(0, K, rows):
+            sk.nvfp4_gemm(blob, eye[r0:r0 + rows].contiguous(), out[r0:r0 + rows], config=cfg, workspace=ws)
+        got = out.float().cpu().numpy()
+        assert np.array_equal(got, deq), f"rows {rows}: {np.argwhere(got != deq)[:5]}"
+        assert not ws[:sk.WORKSPACE_SYNC_BYTES].any().item(), "arrival counters not back at zero"
+
+
 def test_fp8_one_hot_reproduces_codes_exactly():
     """Random finite E4M3 codes, power-of-two block scales: y = e4m3(c) * S exactly."""
     K, N = 272, 200
