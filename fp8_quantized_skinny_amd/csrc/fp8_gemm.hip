@@ -39,6 +39,7 @@
 
 #include "common.cuh"
 #include "internal.h"
+#include "xsplit.cuh"
 
 namespace skinny {
 namespace {
@@ -55,19 +56,33 @@ struct Fp8Args {
   int M, K, N;
   int nt, kb, ku;  // column tiles, scale blocks along K, units along K
   int ksplit, S;
-  float* part;  // [ksplit][M][N] fp32 partial sums (ksplit > 1)
+  float* part;  // fp32 partial sums (ksplit > 1): [ksplit][M][N], or xsplit one block [M][ct * 16] per (tile group, split)
+  int xsplit;      // 1: the K split is added inside the kernel on each tile group's XCD (MFMA engine)
+  int ntg;         // tile groups (xsplit)
+  unsigned* sync;  // xsplit: one arrival counter per tile group, 128 bytes apart (zero at rest)
 };
 
+// This wavefront's unit and its workgroup's geometry (wave-uniform values).
+// An xsplit grid is one-dimensional: tile group and split from xsplit_place
+// (xsplit.cuh), so that the splits of a group run on one XCD; otherwise
+// blockIdx.x is the tile group and blockIdx.y the split.
 struct Fp8Plan {
   int lane, wave, nw, S, tile0, s0, sw, t, s;
+  int group, split;
   bool active;
   __device__ Fp8Plan(const Fp8Args& a, int ct) {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     nw = blockDim.x >> 6;
     S = a.S;
-    tile0 = blockIdx.x * ct;
-    s0 = blockIdx.y * S;
+    if (a.xsplit) {
+      xsplit_place(blockIdx.x, a.ksplit, group, split);
+    } else {
+      group = blockIdx.x;
+      split = blockIdx.y;
+    }
+    tile0 = group * ct;
+    s0 = split * S;
     sw = min(S, a.ku - s0);
     t = wave / S;
     s = wave % S;
@@ -185,6 +200,7 @@ template <int CT, bool PACKED>
 __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(8))) void fp8_mfma(Fp8Args a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const Fp8Plan P(a, CT);
+  if (a.xsplit && P.group >= a.ntg) return;  // grid rounding to whole groups of 8 (uniform)
   _Float16* xs = reinterpret_cast<_Float16*>(lds);
   unsigned char* slots = lds + ((a.M * fp8_xs_stride(P.S) * 2 + 15) & ~15);  // [nw][kWaveSlotBytes]
   unsigned char* slot = slots + P.wave * kWaveSlotBytes;
@@ -239,7 +255,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
   __syncthreads();
 
   const bool fin = P.wave < CT && P.tile0 + P.wave < a.nt && P.lane < 32;
-  const int n = (P.tile0 + P.wave) * kTileCols + fp8_lane_col(cl);
+  const int col = P.wave * kTileCols + fp8_lane_col(cl);  // column within the tile group
+  const int n = P.tile0 * kTileCols + col;
   if (fin && n < a.N) {
     f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < P.sw; ++s)
@@ -248,12 +265,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
     for (int i = 0; i < 4; ++i) {
       const int m = grp * 4 + i;
       if (m >= a.M) continue;
-      if (a.ksplit > 1)
-        a.part[(static_cast<size_t>(blockIdx.y) * a.M + m) * a.N + n] = tot[i];
+      if (a.xsplit)  // this split's block of the group; the last split adds them
+        a.part[((static_cast<size_t>(P.group) * a.ksplit + P.split) * a.M + m) * (CT * kTileCols) + col] = tot[i];
+      else if (a.ksplit > 1)
+        a.part[(static_cast<size_t>(P.split) * a.M + m) * a.N + n] = tot[i];
       else
         a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(tot[i]);
     }
   }
+  if (a.xsplit) xsplit_add<CT * kTileCols, false>(a.sync, a.part, a.y, nullptr, a.M, a.N, P.tile0, P.group, a.ksplit);
 }
 
 // ---------------------------------------------------------------------------
@@ -581,7 +601,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fp8_valu(Fp8Args a) {
         float tot = 0.0f;
         for (int s = 0; s < P.sw; ++s) tot += red[P.wave * P.S + s][m][P.lane];
         if (a.ksplit > 1)
-          a.part[(static_cast<size_t>(blockIdx.y) * a.M + m) * a.N + n] = tot;
+          a.part[(static_cast<size_t>(P.split) * a.M + m) * a.N + n] = tot;
         else
           a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(tot);
       }
@@ -656,14 +676,17 @@ hipError_t launch_fp8(const uint8_t* w, const float* scales, const uint16_t* x, 
   a.ksplit = cfg.ksplit;
   a.S = cfg.nw / cfg.ct;
   a.part = wl.part_bytes ? reinterpret_cast<float*>(ws + wl.part_off) : nullptr;
-  const dim3 grid((a.nt + cfg.ct - 1) / cfg.ct, cfg.ksplit);
+  a.ntg = (a.nt + cfg.ct - 1) / cfg.ct;
+  a.xsplit = fp8_uses_xsplit(cfg, N) ? 1 : 0;
+  a.sync = wl.sync_bytes ? reinterpret_cast<unsigned*>(ws) : nullptr;
+  const dim3 grid = a.xsplit ? dim3(8 * ((a.ntg + 7) / 8) * cfg.ksplit) : dim3(a.ntg, cfg.ksplit);
   const size_t lds = fp8_lds_bytes(M, a.S, cfg.nw);
   hipError_t e = hipErrorInvalidValue;
   SKINNY_FP8_DISPATCH(1)
   SKINNY_FP8_DISPATCH(2)
   SKINNY_FP8_DISPATCH(4)
   SKINNY_FP8_DISPATCH(8)
-  if (e != hipSuccess || cfg.ksplit == 1) return e;
+  if (e != hipSuccess || cfg.ksplit == 1 || a.xsplit) return e;
   return launch_finalize(a.part, cfg.ksplit, M, N, nullptr, y, nullptr, stream);
 }
 

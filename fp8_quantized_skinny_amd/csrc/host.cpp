@@ -202,6 +202,22 @@ LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax, bool swiglu = fals
 LaunchCfg default_fp8_cfg(int M, int K, int N) {
   const int ku = (K + 511) / 512, nt = (N + 15) / 16;
   auto fits = [&](const LaunchCfg& c) { return fp8_cfg_supported(c, M, K); };
+  // Whole-K workgroups of one tile load the CUs unevenly when there are
+  // between one and two tiles per CU.  There the MFMA engine with two tiles
+  // of two units per workgroup and a K split added inside the kernel reads
+  // x once per two tiles and spreads the work evenly.  On MI355X with K = 6144
+  // (12 units), packed codes: 320 tiles (o_proj, 5120 columns) M = 2 / 3 / 4
+  // 7.89 / 8.10 / 8.34 us against 8.28 / 9.09 / 9.51 us whole-K (canonical
+  // M = 4 8.43-8.60 against 10.24 us); 352 to 416 tiles gained 0.1-0.55 us
+  // from M = 3 on but lost at M = 2; 256 and 448 tiles, and K = 1536, lost at
+  // every M.  So: from one to 1.75 tiles per CU at M = 3 and 4, to 1.25 at
+  // M = 2, with K of at least 8 units.
+  const int cus = device_cu_count();
+  const bool uneven = nt > cus && ku >= 8 && (M >= 3 ? 4 * nt < 7 * cus : M == 2 && 4 * nt <= 5 * cus);
+  if (uneven && M <= 4) {
+    const LaunchCfg c{1, 2, 4, (ku + 1) / 2};
+    if (fits(c)) return c;
+  }
   // M <= 2: the VALU engine, whole K per workgroup (two tiles per workgroup
   // only when both fit whole: 2 * ku <= 16 and few tiles).
   if (M <= 2) return pick_whole_k_cfg(0, 2 * ku <= kMaxWaves && nt <= 384 ? 2 : 1, ku, fits);
@@ -317,14 +333,29 @@ WorkspaceLayout nvfp4_workspace_layout(const LaunchCfg& cfg, int M, int K, int N
   return w;
 }
 
+// The MFMA engine adds its K splits inside the kernel (as nvfp4_uses_xsplit)
+// when the tile groups fit the arrival counters; the VALU engine's splits go
+// to the split reduction kernel.
+bool fp8_uses_xsplit(const LaunchCfg& cfg, int N) {
+  const int nt = (N + kTileCols - 1) / kTileCols;
+  const int64_t reach = static_cast<int64_t>(cfg.ksplit + 16) * 8 * cfg.ct * kTileCols * 4;
+  return cfg.engine == 1 && cfg.ksplit > 1 && (nt + cfg.ct - 1) / cfg.ct <= kMaxSyncGroups &&
+         reach < (int64_t{1} << 30);
+}
+
+// Partial sums of a K split: fp32, ksplit x M x (the tiles' columns), laid
+// out [split][m][n] for the split reduction kernel or in one [m][column] block
+// per (tile group, split) for the in-kernel reduction; the size covers both.
 WorkspaceLayout fp8_workspace_layout(const LaunchCfg& cfg, int M, int K, int N) {
   (void)K;
   WorkspaceLayout w{};
   if (cfg.ksplit == 1) return w;
+  const int nt = (N + kTileCols - 1) / kTileCols;
+  const size_t cols = std::max(static_cast<size_t>(N), static_cast<size_t>((nt + cfg.ct - 1) / cfg.ct) * cfg.ct * kTileCols);
   size_t off = kSyncBytes;
   w.sync_bytes = kSyncBytes;
   w.part_off = off;
-  w.part_bytes = static_cast<size_t>(cfg.ksplit) * M * N * 4;
+  w.part_bytes = static_cast<size_t>(cfg.ksplit) * M * cols * 4;
   off = align256(off + w.part_bytes);
   w.total = off;
   return w;

@@ -146,6 +146,8 @@ bool nvfp4_balanced_layout(int nt, int ku, int cus, BalancedLayout* out);
 // kernel (the VALU or MFMA engine, plain epilogue, at most kMaxSyncGroups tile
 // groups).
 bool nvfp4_uses_xsplit(const LaunchCfg& cfg, int N, bool plain_epilogue);
+// The same for the FP8 GEMM (MFMA engine only).
+bool fp8_uses_xsplit(const LaunchCfg& cfg, int N);
 WorkspaceLayout fp8_workspace_layout(const LaunchCfg& cfg, int M, int K, int N);
 
 // Kernel launchers (defined in the .hip files).  Arguments are validated.

@@ -18,7 +18,7 @@
 // more spans than a workgroup covers, ksplit workgroups share a tile group:
 // each stores its fp32 partial sums with plain stores.  With the plain
 // epilogue the splits of a group run on one XCD and the last of them to
-// arrive adds all of them in split order (xsplit_finish below); otherwise a
+// arrive adds all of them in split order (xsplit_add, xsplit.cuh); otherwise a
 // second small kernel (reduce.hip) adds them in split order.  Either way the
 // result does not depend on timing.  Few registers per wavefront (one unit)
 // let the chip keep tens of megabytes of weight loads in flight, which is
@@ -52,6 +52,7 @@
 
 #include "common.cuh"
 #include "internal.h"
+#include "xsplit.cuh"
 
 namespace skinny {
 namespace {
@@ -95,16 +96,8 @@ __device__ __forceinline__ float swiglu_pair(float sum, float g, float g2) {
 
 // This wavefront's unit and its workgroup's geometry (wave-uniform values).
 // Workgroup b of an xsplit grid (1-D, 8 * ceil(ntg / 8) * ksplit workgroups)
-// takes tile group 8 * (b / (8 * ksplit)) + b % 8 and split (b % (8 * ksplit))
-// / 8: the splits of a tile group are workgroups congruent mod 8, which the
-// hardware dispatches to one XCD (it deals the workgroups of a kernel to the
-// 8 XCDs in turn), so they share that XCD's L2.
-__device__ __forceinline__ void xsplit_place(int b, int ksplit, int& group, int& split) {
-  const int per = 8 * ksplit;
-  group = (b / per) * 8 + (b & 7);
-  split = (b % per) >> 3;
-}
-
+// takes tile group and split from xsplit_place (xsplit.cuh): the splits of a
+// tile group run on one XCD.
 struct Plan {
   int lane, wave, nw, S, tile0, s0, sw;  // sw: spans in this split
   int t, s;                              // local tile and span of this wavefront's unit
@@ -164,53 +157,6 @@ struct Plan {
     return a.units + (static_cast<size_t>(s0 + s) * a.nt + tt) * kUnitBytes + lane * 16;
   }
 };
-
-// The end of an xsplit workgroup: its partial sums of tile group P.group,
-// already stored to the group's block for split P.split, are published with
-// an arrival count on the group's counter; the workgroup that arrives last
-// (all splits of the group run on one XCD, so plain stores, an atomic in that
-// XCD's L2 and loads that skip the CU's L1 see each other) adds the ks
-// blocks in split order, scales by g and writes y.  It then sets the counter
-// back to zero for the next call.  Nothing waits on another workgroup, and the
-// order of the sums does not depend on which split arrives last.
-// Every thread of the workgroup must call this.
-template <int CT>
-__device__ void xsplit_finish(const Nvfp4Args& a, const Plan& P, int ks) {
-  constexpr int kCols = CT * kTileCols;
-  __shared__ int last;
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have reached L2
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned* cnt = a.sync + static_cast<size_t>(P.group) * 32;
-    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    last = old == static_cast<unsigned>(ks - 1);
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-  __syncthreads();
-  if (!last) return;
-  const size_t block = static_cast<size_t>(a.M) * kCols;
-  const float* base = a.part + static_cast<size_t>(P.group) * ks * block;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(base), 0, static_cast<int>(ks * block * sizeof(float)), 0x00020000);
-  const float g = *a.gptr;
-  for (int o = threadIdx.x; o < static_cast<int>(block); o += blockDim.x) {
-    const int m = o / kCols, n = P.tile0 * kTileCols + o % kCols;
-    // Sixteen splits per batch, all loads issued before the first add; a
-    // split past the last reads 0 (outside the buffer's range) and adds 0.
-    constexpr int kBatch = 16;
-    float sum = 0.0f;
-    for (int k0 = 0; k0 < ks; k0 += kBatch) {
-      float v[kBatch];
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i)  // sc0: past this CU's L1, from the XCD's L2
-        v[i] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, static_cast<int>(((k0 + i) * block + o) * 4), 0, 1));
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) sum += v[i];
-    }
-    if (n < a.N) a.y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(g * sum);
-  }
-}
 
 // Read in place of activation pairs past K by the VALU engine (a global,
 // not a constant, so that both choices of address are global loads).
@@ -391,7 +337,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_valu(Nvfp4Args a) {
 #pragma unroll
       for (int r = 0; r < MR; ++r) blk[r * (CT * kTileCols) + P.wave * kTileCols + P.lane] = tot[r];
     }
-    xsplit_finish<CT>(a, P, P.ks);
+    xsplit_add<CT * kTileCols, true>(a.sync, a.part, a.y, a.gptr, a.M, a.N, P.tile0, P.group, P.ks);
     return;
   }
   if (fin) {
@@ -546,7 +492,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void nvfp4_mfma(Nvfp4Args a) {
         if (m < a.M) blk[m * (CT * kTileCols) + P.wave * kTileCols + cl] = tot[i];
       }
     }
-    xsplit_finish<CT>(a, P, a.ksplit);
+    xsplit_add<CT * kTileCols, true>(a.sync, a.part, a.y, a.gptr, a.M, a.N, P.tile0, P.group, a.ksplit);
     return;
   }
   if (a.ksplit > 1) {  // this split's partial sums; the split reduction finishes

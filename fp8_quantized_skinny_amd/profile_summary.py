@@ -28,7 +28,7 @@ import sys
 import numpy as np
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-KERNEL_SOURCES = ("common.cuh", "internal.h", "nvfp4_gemm.hip", "fp8_gemm.hip", "reduce.hip")
+KERNEL_SOURCES = ("common.cuh", "internal.h", "xsplit.cuh", "nvfp4_gemm.hip", "fp8_gemm.hip", "reduce.hip")
 
 
 def _code_only(text):

@@ -365,8 +365,8 @@ int fp8_quantize(const float* w, int K, int N, uint8_t* codes, float* scales);
  *            the workspace (size from skinny_workspace_bytes_config for the
  *            same choice) and they are added in split order: by the last
  *            split to arrive, on the tile group's XCD, for plain NVFP4 calls
- *            on engines 0 and 1; by a second kernel otherwise (FP8, SwiGLU
- *            pairs, the lm_head).
+ *            on engines 0 and 1 and FP8 calls on engine 1; by a second kernel
+ *            otherwise (FP8 on engine 0, SwiGLU pairs, the lm_head).
  * A combination that is not built (or whose LDS need exceeds the CU)
  * returns SKINNY_EINVAL.
  * ------------------------------------------------------------------------- */
