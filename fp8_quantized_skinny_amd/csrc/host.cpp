@@ -203,17 +203,22 @@ LaunchCfg default_fp8_cfg(int M, int K, int N) {
   const int ku = (K + 511) / 512, nt = (N + 15) / 16;
   auto fits = [&](const LaunchCfg& c) { return fp8_cfg_supported(c, M, K); };
   // Whole-K workgroups of one tile load the CUs unevenly when there are
-  // between one and two tiles per CU.  There the MFMA engine with two tiles
-  // of two units per workgroup and a K split added inside the kernel reads
-  // x once per two tiles and spreads the work evenly.  On MI355X with K = 6144
-  // (12 units), packed codes: 320 tiles (o_proj, 5120 columns) M = 2 / 3 / 4
-  // 7.89 / 8.10 / 8.34 us against 8.28 / 9.09 / 9.51 us whole-K (canonical
-  // M = 4 8.43-8.60 against 10.24 us); 352 to 416 tiles gained 0.1-0.55 us
-  // from M = 3 on but lost at M = 2; 256 and 448 tiles, and K = 1536, lost at
-  // every M.  So: from one to 1.75 tiles per CU at M = 3 and 4, to 1.25 at
-  // M = 2, with K of at least 8 units.
+  // between one and two tiles per CU, and leave CUs idle below one per CU,
+  // where each busy CU's time grows with its K.  There the MFMA engine with
+  // two tiles of two units per workgroup and a K split added inside the
+  // kernel reads x once per two tiles and spreads the work evenly.  On MI355X,
+  // packed codes, K = 6144 (12 units): 320 tiles (o_proj, 5120 columns)
+  // M = 2 / 3 / 4 7.89 / 8.10 / 8.34 us against 8.28 / 9.09 / 9.51 us whole-K
+  // (canonical M = 4 8.43-8.60 against 10.24 us); 352 to 416 tiles gained
+  // 0.1-0.55 us from M = 3 on but lost at M = 2; 256 and 448 tiles, and
+  // K = 1536, lost at every M.  K = 5120 (10 units): 32 / 64 / 112 tiles
+  // gained 0.6-0.9 / 0.6-0.8 / 0.2 us at M = 3 and 4, 32 and 64 tiles 0.2-0.3
+  // us at M = 2; 160 tiles tied and 224 lost.  K = 4096 (8 units) lost from
+  // 64 tiles on.
   const int cus = device_cu_count();
-  const bool uneven = nt > cus && ku >= 8 && (M >= 3 ? 4 * nt < 7 * cus : M == 2 && 4 * nt <= 5 * cus);
+  const bool uneven =
+      nt > cus ? ku >= 8 && (M >= 3 ? 4 * nt < 7 * cus : M == 2 && 4 * nt <= 5 * cus)
+               : ku >= 10 && (M >= 3 ? 2 * nt <= cus : M == 2 && 4 * nt <= cus);
   if (uneven && M <= 4) {
     const LaunchCfg c{1, 2, 4, (ku + 1) / 2};
     if (fits(c)) return c;
