@@ -124,7 +124,8 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 // parallelism, so the one-unit-per-wavefront MFMA engine is used instead,
 // like FP8:
 //   - up to four rows and K <= 8192: whole K per workgroup (two tiles per
-//     workgroup when K and N are short);
+//     workgroup when K and N are short), except NVFP4 with few tiles and
+//     K of at least 5 spans, which takes the short choice below;
 //   - otherwise four tiles per workgroup and the fewest K spans per workgroup
 //     that keep the K split at most nine ways (the x slice a workgroup stages
 //     in LDS grows with M and with its spans; short workgroups keep it small).
@@ -193,6 +194,23 @@ LaunchCfg default_nvfp4_cfg(int M, int K, int N, bool argmax, bool swiglu = fals
       nvfp4_balanced_layout(g.nt, g.ku, cus, &bal))
     return LaunchCfg{3, 1, g.ku, 1};
   if (M == 1 && !argmax && g.nt <= 384 && g.ku > kMaxWaves) return fit_spans(0, 4, g.ku, 2, fits);
+  // With at most 384 tiles and K of at least 5 spans, MFMA workgroups of four
+  // tiles of one span each (pick_short_cfg), added inside the kernel, spread
+  // the bytes over every CU, where whole-K workgroups leave CUs idle or
+  // unevenly loaded and each busy CU's time grows with K.  On MI355X (one
+  // box, same runs), M = 3 / 4: 128 tiles at K = 5120 5.12 / 5.24 us against
+  // 6.53 / 6.81 us whole-K; 272 tiles (one rank's up share) 6.39 / 6.53
+  // against 6.89 / 7.15; 384 tiles 6.72 / 6.91 against 7.33 / 7.58; 320 tiles
+  // at K = 4352 (one rank's down share) 6.85 / 6.97 against 7.22 / 7.48; 256
+  // tiles at K = 8192 6.82 / 6.97 against 8.48 / 8.85.  At 480 tiles it tied,
+  // and at K = 2048 (2 spans) it lost by 0.5-0.7 us.  At M = 2 it won with at
+  // most half a tile per CU (128 tiles: 5.07 against 6.12 us for the VALU
+  // engine) or K of at least 8 spans (256 tiles at K = 8192: 6.71 against
+  // 7.41), and tied or lost by up to 0.13 us at 272 to 384 tiles and K = 5120
+  // or 4352.
+  if (!argmax && !swiglu && g.ku >= 5 && g.nt <= 384 &&
+      (M == 3 || M == 4 || (M == 2 && (2 * g.nt <= cus || (g.ku >= 8 && g.nt <= cus)))))
+    return pick_short_cfg(g.ku, g.nt, fits);
   if (M == 1 || (M == 2 && !argmax && g.nt <= 384)) return pick_whole_k_cfg(0, g.nt <= 384 ? 2 : 1, g.ku, fits);
   LaunchCfg c;
   if (pick_stream_cfg(M, K, N, argmax, &c)) return c;
